@@ -1,0 +1,183 @@
+/*
+ * kvq.h -- C ABI of libkvq.so: quantizing KV-cache writes and paged decode
+ * attention over INT8 / FP8 / FP16 block pools, for AMD MI355X (gfx950).
+ *
+ * What the calls compute (web pages, cited by title and section):
+ *   "KV Cache优化实战：大模型推理显存占用与加速方案详解" (0539edu.com)
+ *     s1.1  each decode step computes only the new token's K/V, appends it to
+ *           the end of the cache, and attends with the current query over all
+ *           cached K/V.
+ *     s2.1  GQA: the query heads are split into groups; each group shares one
+ *           KV head (query head g reads KV head g / (Hq / Hkv)).
+ *     s2.2  paged cache: fixed-size physical blocks, a per-sequence block table
+ *           mapping logical blocks to physical ones anywhere in the pool.
+ *     s2.3  INT8 absmax symmetric quantization storing a scale, dequantized at
+ *           run time; per-group scales (e.g. 128 elements per group); FP8.
+ *     s3.3  per_group granularity, group size 128 or 64.
+ *     s4.3  dequantization fused into the attention kernel instead of separate
+ *           small kernels.
+ *   xpshop.cn article 312, s3: 16- or 32-token blocks; FP8 KV cache.
+ *
+ * Conventions shared by every call
+ *  - All buffers are device memory owned by the caller; the library never
+ *    allocates, frees or keeps pointers.  Calls are asynchronous on `stream`
+ *    (a hipStream_t; NULL = the legacy default stream) and never synchronize.
+ *  - The library never prints, aborts or falls back to another format or a
+ *    slower path: unsupported combinations return KVQ_ERR_UNSUPPORTED.
+ *  - The synchronous return value covers host-side argument checks and launch
+ *    errors.  Device contents (block ids, slots, lengths) are trusted, except
+ *    that cache writes skip slots outside the pool.
+ *  - Supported: head_dim 64 or 128; block_size 16 or 32; INT8 group_size 64 or
+ *    128 dividing head_dim; Hq / Hkv between 1 and 16; gfx950 only.
+ *  - Pointers to q, out, pools, scales and workspace must be 16-byte aligned.
+ *
+ * Pool layout (one layer; the caller keeps one set of pools per layer):
+ *   k_pool  [num_blocks][Hkv][block_size][head_dim]   token-major
+ *   v_pool  [num_blocks][Hkv][head_dim][block_size]   dim-major
+ *   element type: INT8 = int8 codes, FP8 = E4M3 bytes, FP16 = IEEE half.
+ *   INT8 scales: k_scale, v_scale [num_blocks][Hkv][block_size][head_dim/G]
+ *   fp32, one per (token slot, group of G consecutive head_dim elements).
+ *   FP8 scales:  k_scale, v_scale [Hkv] fp32, static, read only.
+ *   FP16: no scales (pass NULL).
+ *   A slot is block * block_size + offset.
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KVQ_API __attribute__((visibility("default")))
+
+/* KV element formats (per layer). */
+enum {
+    KVQ_FP16 = 0,
+    KVQ_INT8 = 1,     /* per-group absmax, one fp32 scale per group   */
+    KVQ_FP8_E4M3 = 2  /* OCP E4M3FN, one static fp32 scale per KV head */
+};
+
+typedef int32_t kvq_status;
+enum {
+    KVQ_OK = 0,
+    KVQ_ERR_INVALID_ARG = -1,
+    KVQ_ERR_UNSUPPORTED = -2,
+    KVQ_ERR_WORKSPACE = -3,
+    KVQ_ERR_HIP = -4
+};
+
+/* Human-readable name of a status code (static string, never NULL). */
+KVQ_API const char *kvq_status_string(kvq_status status);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+KVQ_API int32_t kvq_version(void);
+
+/*
+ * kvq_cache_write -- quantize the K/V of new tokens and store them in their
+ * slots ("KV Cache优化实战" s1.1 append, s2.2 block placement, s2.3 / s3.3
+ * per-group absmax quantization; xpshop.cn article 312 s3 FP8).
+ *
+ *   k, v          fp16 [num_tokens][num_kv_heads][head_dim], contiguous.
+ *   slot_mapping  int64 [num_tokens]: slot of each token; a negative slot, or
+ *                 one >= num_blocks * block_size, skips the token.
+ *   dtype         KVQ_INT8: for each (token, head, group of group_size
+ *                   elements): a = max |x|; s = fl32(a / 127);
+ *                   code = clamp(round_half_even(fl32(x / s)), -127, 127);
+ *                   a == 0 stores s = 0 and zero codes.  Codes go to the
+ *                   pools, s to k_scale / v_scale (written).
+ *                 KVQ_FP8_E4M3: code = E4M3(fl32(x / S[h])) rounding to
+ *                   nearest-even and saturating to +-448; S = k_scale /
+ *                   v_scale [num_kv_heads] (read only).
+ *                 KVQ_FP16: the values are copied.
+ *   group_size    INT8 only (64 or 128, divides head_dim); ignored otherwise.
+ * Tokens are independent; two tokens mapped to the same slot race.
+ */
+KVQ_API kvq_status kvq_cache_write(const void *k, const void *v,
+                           const int64_t *slot_mapping, int32_t num_tokens,
+                           int32_t num_kv_heads, int32_t head_dim,
+                           int32_t block_size, int32_t num_blocks,
+                           int32_t dtype, int32_t group_size,
+                           void *k_pool, void *v_pool,
+                           float *k_scale, float *v_scale, void *stream);
+
+/*
+ * kvq_paged_decode -- one decode step of attention for a batch of sequences
+ * over the paged pool ("KV Cache优化实战" s1.1, s2.1, s2.2, s4.3).
+ *
+ * For sequence b with ctx = context_lens[b] and query head g (KV head
+ * h = g / (Hq / Hkv)):
+ *   z_t = softmax_scale * q[b][g] . Khat[b][t][h]          for t < ctx
+ *   out[b][g] = sum_t softmax(z)_t * Vhat[b][t][h]
+ * where logical token t lives in slot block_tables[b][t / block_size] *
+ * block_size + t % block_size and Khat / Vhat are the dequantized values
+ * (code * scale; dequantization is fused into the kernel).
+ *
+ *   q             fp16 [num_seqs][num_q_heads][head_dim].
+ *   block_tables  int32 [num_seqs][max_blocks_per_seq]; entries past
+ *                 ceil(ctx / block_size) are never read.
+ *   context_lens  int32 [num_seqs] on the device, each in
+ *                 [1, max_context_len]; max_context_len is the host-side bound
+ *                 (used to plan the split) and must not exceed
+ *                 max_blocks_per_seq * block_size.
+ *   softmax_scale 0 selects 1 / sqrt(head_dim).
+ *   split_tokens  0 = automatic; otherwise a multiple of 16: every sequence
+ *                 is cut into spans of split_tokens logical tokens, each
+ *                 attended separately and merged exactly (log-sum-exp).
+ *                 The split depends only on logical positions, so results do
+ *                 not depend on which physical blocks hold the data.
+ *   out           fp16 [num_seqs][num_q_heads][head_dim] (written).
+ *   workspace     device scratch of at least kvq_decode_workspace_size(...)
+ *                 bytes (may be NULL when that size is 0).  It must be
+ *                 zero-filled before its first use; every call leaves it
+ *                 ready for the next one.  Calls sharing a workspace must be
+ *                 ordered (same stream).
+ */
+KVQ_API kvq_status kvq_paged_decode(const void *q, const void *k_pool,
+                            const void *v_pool, const float *k_scale,
+                            const float *v_scale, const int32_t *block_tables,
+                            int32_t max_blocks_per_seq,
+                            const int32_t *context_lens,
+                            int32_t max_context_len, int32_t num_seqs,
+                            int32_t num_q_heads, int32_t num_kv_heads,
+                            int32_t head_dim, int32_t block_size,
+                            int32_t num_blocks, int32_t dtype,
+                            int32_t group_size, float softmax_scale,
+                            int32_t split_tokens, void *out, void *workspace,
+                            size_t workspace_bytes, void *stream);
+
+/* Logical tokens per split chosen by kvq_paged_decode for these arguments
+ * (split_tokens as passed to it); returns -1 for invalid arguments. */
+KVQ_API int32_t kvq_decode_split_tokens(int32_t num_seqs, int32_t num_kv_heads,
+                                int32_t block_size, int32_t max_context_len,
+                                int32_t split_tokens);
+
+/* Workspace bytes kvq_paged_decode needs for these arguments (0 when no
+ * sequence is split).  Returns SIZE_MAX for invalid arguments. */
+KVQ_API size_t kvq_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads,
+                                 int32_t num_kv_heads, int32_t head_dim,
+                                 int32_t block_size, int32_t max_context_len,
+                                 int32_t split_tokens);
+
+/*
+ * kvq_copy_blocks -- copy whole blocks (codes of every slot, and INT8 scales)
+ * of one layer's pools: block pairs[2i] -> pairs[2i+1].  Used for
+ * copy-on-write of a shared, partially filled block before a sequence writes
+ * into it ("KV Cache优化实战" s4.4).  block_pairs: int32 [num_pairs][2] on the
+ * device; destinations must be distinct and not be sources.  FP8 / FP16 pools
+ * pass NULL scales.
+ */
+KVQ_API kvq_status kvq_copy_blocks(const int32_t *block_pairs, int32_t num_pairs,
+                           int32_t num_kv_heads, int32_t head_dim,
+                           int32_t block_size, int32_t num_blocks,
+                           int32_t dtype, int32_t group_size, void *k_pool,
+                           void *v_pool, float *k_scale, float *v_scale,
+                           void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVQ_H */

@@ -1,0 +1,374 @@
+// kvq_decode.hpp -- paged decode attention with fused dequantization (gfx950).
+//
+// Computes, for one decode step ("KV Cache优化实战" s1.1: the current query
+// attends over every cached K/V; s2.1: the query heads of a group share one
+// KV head; s2.2: tokens live in blocks found through a block table; s4.3:
+// dequantization fused into attention):
+//     out[b][g] = sum_t softmax_t(sm * q[b][g] . Khat[t]) Vhat[t]
+//
+// Work decomposition.  One wavefront owns one (sequence b, KV head h, split)
+// item: a span of `span` logical tokens (all of them when the sequence is not
+// split).  It walks the span in tiles of 16 tokens (a 16-token block, or half
+// of a 32-token block), gathering each tile through the block table.
+//
+// Both contractions run on 16x16x16 fp16 MFMA with the head_dim / token axes
+// laid out so that no data moves between lanes except for softmax maxima:
+//   S^T[token][head] = K_tile (16 x D) * Q^T (D x 16)
+//       A operand: lane (col, grp) holds token `col`, 4 head_dim values per
+//       k-step; B operand: q of query head `col` (zero for col >= r).
+//       Output: lane (col, grp) holds the scores of query head `col` for the
+//       tile's tokens 4*grp .. 4*grp+3.
+//   O^T[d][head] += V_tile^T (16 d x 16 tokens) * P^T (16 tokens x 16 heads)
+//       B operand = P^T, which is exactly the softmaxed S^T output already in
+//       the lane; A operand: lane holds d-row `col` of a 16-dim tile for the
+//       tokens 4*grp .. 4*grp+3 -- 4 consecutive bytes of the dim-major V
+//       block.
+// Codes are converted to exact fp16 (INT8 c, or E4M3 value * 2^-8) right
+// before the MFMA; K group scales multiply the per-group partial dot products
+// (one accumulator per group); V group scales are folded into P (rounded to
+// fp16 once) so the token sum stays a single MFMA chain.
+//
+// Online softmax in base 2 (the log2(e) factor rides on the score scale), with
+// a rescale of the running output only when some head's maximum grows.
+// Splits of one (b, h) write (m, l, acc) partials; the last wavefront of the
+// (b, h) to finish (atomic counter) merges them with a log-sum-exp and resets
+// the counter, so a single kernel launch produces the output.
+#pragma once
+
+#include "kvq_device.hpp"
+
+namespace kvq {
+
+struct DecodeParams {
+    const f16 *q;
+    const uint8_t *k_pool;
+    const uint8_t *v_pool;
+    const float *k_scale;
+    const float *v_scale;
+    const int32_t *block_tables;
+    const int32_t *context_lens;
+    f16 *out;
+    float *ws_acc;    // [B][Hq][max_splits][D]
+    float *ws_ml;     // [B][Hq][max_splits][2]
+    int32_t *ws_cnt;  // [B][Hkv]
+    int32_t max_blocks;
+    int32_t max_ctx;     // host bound on context_lens (<= max_blocks * BS)
+    int32_t num_blocks;
+    int32_t Hq;
+    int32_t Hkv;
+    int32_t r;
+    int32_t span;
+    int32_t max_splits;
+    float score_scale;  // softmax_scale * log2(e)
+};
+
+template <int FMT, int D>
+struct TileData {
+    static constexpr int EB = FMT == FMT_FP16 ? 2 : 1;
+    static constexpr int KV4 = D * EB / 64;   // 16-byte K loads per lane
+    static constexpr int DT = D / 16;         // 16-dim tiles
+    uint32_t k[4 * KV4];                      // head_dim slice of token `col`
+    uint32_t v[DT * EB];                      // 4 tokens of one d-row
+    f32x4 sk[2];
+    f32x4 sv[2];
+};
+
+template <int FMT, int D, int BS, int NG>
+__device__ __forceinline__ void load_tile(const DecodeParams &p, TileData<FMT, D> &t,
+                                          int phys, int h, int toff, int col, int grp)
+{
+    constexpr int EB = TileData<FMT, D>::EB;
+    constexpr int DT = D / 16;
+    const int64_t tile = (int64_t)phys * p.Hkv + h;
+    // K: token-major rows; lane reads row `col`, dims [64c + 16 grp, +16)
+    const uint8_t *krow = p.k_pool + ((tile * BS + toff + col) * D) * EB;
+#pragma unroll
+    for (int c = 0; c < D / 64; ++c) {
+        const uint8_t *src = krow + (64 * c + 16 * grp) * EB;
+#pragma unroll
+        for (int e = 0; e < EB; ++e) {
+            const uint4 w = *reinterpret_cast<const uint4 *>(src + 16 * e);
+            const int i = 4 * (c * EB + e);
+            t.k[i + 0] = w.x;
+            t.k[i + 1] = w.y;
+            t.k[i + 2] = w.z;
+            t.k[i + 3] = w.w;
+        }
+    }
+    // V: dim-major; lane reads d-row 16*tau + col, tokens toff + 4 grp .. +3
+    const uint8_t *vblk = p.v_pool + (tile * D * BS) * EB;
+#pragma unroll
+    for (int tau = 0; tau < DT; ++tau) {
+        const uint8_t *src = vblk + ((int64_t)(16 * tau + col) * BS + toff + 4 * grp) * EB;
+        if constexpr (EB == 1) {
+            t.v[tau] = *reinterpret_cast<const uint32_t *>(src);
+        } else {
+            const uint2 w = *reinterpret_cast<const uint2 *>(src);
+            t.v[2 * tau] = w.x;
+            t.v[2 * tau + 1] = w.y;
+        }
+    }
+    if constexpr (FMT == FMT_INT8) {
+        const int64_t s0 = (tile * BS + toff + 4 * grp) * NG;
+#pragma unroll
+        for (int i = 0; i < NG; ++i) {
+            t.sk[i] = *reinterpret_cast<const f32x4 *>(p.k_scale + s0 + 4 * i);
+            t.sv[i] = *reinterpret_cast<const f32x4 *>(p.v_scale + s0 + 4 * i);
+        }
+    }
+}
+
+template <int FMT, int D, int BS, int NG>
+__global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
+{
+    constexpr int KS = D / 16;   // MFMA k-steps over head_dim
+    constexpr int DT = D / 16;   // 16-dim output tiles
+    constexpr int EB = TileData<FMT, D>::EB;
+    constexpr int G = D / NG;    // INT8 group size
+    static_assert(FMT != FMT_INT8 || G >= 64, "groups must cover a 64-dim chunk");
+
+    const int split = blockIdx.x;
+    const int h = blockIdx.y;
+    const int b = blockIdx.z;
+    const int lane = threadIdx.x;
+    const int col = lane & 15;
+    const int grp = lane >> 4;
+
+    // Device lengths beyond the host bound are clamped so that no table entry
+    // or workspace slot outside the caller's buffers is ever addressed.
+    const int ctx = min(p.context_lens[b], p.max_ctx);
+    const int t_begin = split * p.span;
+    if (t_begin >= ctx)
+        return;
+    const int t_end = min(ctx, t_begin + p.span);
+    const int nsplit = (ctx + p.span - 1) / p.span;
+    const int ntiles = (t_end - t_begin + 15) >> 4;
+    const bool head_ok = col < p.r;
+    const int qhead = h * p.r + col;
+
+    // ---- query operand: q[qhead][64c + 16 grp + 4j + v] for k-step 4c + j
+    f16x4 qop[KS];
+    {
+        const f16 *qrow = p.q + ((int64_t)b * p.Hq + (head_ok ? qhead : h * p.r)) * D;
+#pragma unroll
+        for (int c = 0; c < D / 64; ++c) {
+            const uint4 w0 = *reinterpret_cast<const uint4 *>(qrow + 64 * c + 16 * grp);
+            const uint4 w1 = *reinterpret_cast<const uint4 *>(qrow + 64 * c + 16 * grp + 8);
+            qop[4 * c + 0] = f16x4_from_u2(w0.x, w0.y);
+            qop[4 * c + 1] = f16x4_from_u2(w0.z, w0.w);
+            qop[4 * c + 2] = f16x4_from_u2(w1.x, w1.y);
+            qop[4 * c + 3] = f16x4_from_u2(w1.z, w1.w);
+        }
+        if (!head_ok) {
+#pragma unroll
+            for (int s = 0; s < KS; ++s)
+                qop[s] = f16x4{0, 0, 0, 0};
+        }
+    }
+
+    float score_scale = p.score_scale;
+    float out_scale = 1.0f;
+    if constexpr (FMT == FMT_FP8) {
+        score_scale *= 256.0f * p.k_scale[h];
+        out_scale = 256.0f * p.v_scale[h];
+    }
+
+    // ---- block table: a window of 64 consecutive logical blocks in a VGPR
+    const int32_t *bt = p.block_tables + (int64_t)b * p.max_blocks;
+    const int blk_last = (t_end - 1) / BS;
+    int win_base = t_begin / BS;
+    int win = (win_base + lane <= blk_last) ? bt[win_base + lane] : 0;
+
+    auto phys_of = [&](int lblk) -> int {
+        if (lblk - win_base >= 64) {  // wave-uniform
+            win_base = lblk;
+            win = (win_base + lane <= blk_last) ? bt[win_base + lane] : 0;
+        }
+        const int id = __builtin_amdgcn_readlane(win, lblk - win_base);
+        return min(max(id, 0), p.num_blocks - 1);  // never leave the pool
+    };
+
+    f32x4 o[DT];
+#pragma unroll
+    for (int i = 0; i < DT; ++i)
+        o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m = -INFINITY;
+    float l = 0.0f;
+
+    // One tile of 16 tokens starting at logical token ts, data in `cur`.
+    auto process = [&](const TileData<FMT, D> &cur, const int ts) {
+        // ---- S^T = K Q^T, one accumulator per INT8 group
+        f32x4 sacc[NG];
+#pragma unroll
+        for (int i = 0; i < NG; ++i)
+            sacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            const int c = s >> 2, j = s & 3;
+            f16x4 a;
+            if constexpr (FMT == FMT_INT8) {
+                a = int8x4_to_f16x4(cur.k[4 * c + j]);
+            } else if constexpr (FMT == FMT_FP8) {
+                a = fp8x4_to_f16x4_scaled(cur.k[4 * c + j]);
+            } else {
+                a = f16x4_from_u2(cur.k[8 * c + 2 * j], cur.k[8 * c + 2 * j + 1]);
+            }
+            const int gi = (FMT == FMT_INT8 && NG == 2) ? c : 0;
+            sacc[gi] = __builtin_amdgcn_mfma_f32_16x16x16f16(a, qop[s], sacc[gi], 0, 0, 0);
+        }
+
+        // ---- scores of tokens ts + 4 grp + v for query head col (base 2)
+        const int tok0 = ts + 4 * grp;
+        float z[4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            float acc;
+            if constexpr (FMT == FMT_INT8) {
+                acc = sacc[0][v] * cur.sk[(NG * v) >> 2][(NG * v) & 3];
+                if constexpr (NG == 2)
+                    acc += sacc[1][v] * cur.sk[(2 * v + 1) >> 2][(2 * v + 1) & 3];
+            } else {
+                acc = sacc[0][v];
+            }
+            z[v] = (tok0 + v < t_end) ? acc * score_scale : -INFINITY;
+        }
+
+        // ---- online softmax
+        float mt = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
+        mt = fmaxf(mt, __shfl_xor(mt, 16));
+        mt = fmaxf(mt, __shfl_xor(mt, 32));
+        if (__builtin_amdgcn_ballot_w64(mt > m)) {
+            const float mn = fmaxf(m, mt);
+            const float alpha = __builtin_amdgcn_exp2f(m - mn);
+            l *= alpha;
+#pragma unroll
+            for (int i = 0; i < DT; ++i)
+                o[i] *= alpha;
+            m = mn;
+        }
+        float pr[4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            pr[v] = __builtin_amdgcn_exp2f(z[v] - m);
+            l += pr[v];
+        }
+
+        // ---- P^T operands (V group scales folded in for INT8)
+        f16x4 pop[NG];
+        if constexpr (FMT == FMT_INT8) {
+#pragma unroll
+            for (int j = 0; j < NG; ++j) {
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const float sv = cur.sv[(NG * v + j) >> 2][(NG * v + j) & 3];
+                    pop[j][v] = (f16)((tok0 + v < t_end) ? pr[v] * sv : 0.0f);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+                pop[0][v] = (f16)pr[v];
+        }
+
+        // ---- O^T += V^T P^T
+        const bool partial = ts + 16 > t_end;
+#pragma unroll
+        for (int tau = 0; tau < DT; ++tau) {
+            f16x4 a;
+            if constexpr (FMT == FMT_INT8) {
+                a = int8x4_to_f16x4(cur.v[tau]);
+            } else if constexpr (FMT == FMT_FP8) {
+                a = fp8x4_to_f16x4_scaled(cur.v[tau]);
+            } else {
+                a = f16x4_from_u2(cur.v[2 * tau], cur.v[2 * tau + 1]);
+                if (partial) {  // stale fp16 slots may hold non-finite values
+#pragma unroll
+                    for (int v = 0; v < 4; ++v)
+                        if (tok0 + v >= t_end)
+                            a[v] = (f16)0.0f;
+                }
+            }
+            const int gi = (FMT == FMT_INT8 && NG == 2) ? (16 * tau) / G : 0;
+            o[tau] = __builtin_amdgcn_mfma_f32_16x16x16f16(a, pop[gi], o[tau], 0, 0, 0);
+        }
+
+    };
+
+    // Ping-pong over two tile buffers: the loads of tile i+1 are in flight
+    // while tile i is computed.
+    TileData<FMT, D> buf0, buf1;
+    load_tile<FMT, D, BS, NG>(p, buf0, phys_of(t_begin / BS), h, t_begin % BS, col, grp);
+    for (int it = 0; it < ntiles; it += 2) {
+        const int ts = t_begin + 16 * it;
+        if (it + 1 < ntiles)
+            load_tile<FMT, D, BS, NG>(p, buf1, phys_of((ts + 16) / BS), h, (ts + 16) % BS, col, grp);
+        process(buf0, ts);
+        if (it + 1 >= ntiles)
+            break;
+        if (it + 2 < ntiles)
+            load_tile<FMT, D, BS, NG>(p, buf0, phys_of((ts + 32) / BS), h, (ts + 32) % BS, col, grp);
+        process(buf1, ts + 16);
+    }
+
+    // ---- epilogue
+    float lt = l + __shfl_xor(l, 16);
+    lt += __shfl_xor(lt, 32);
+
+    if (nsplit == 1) {
+        if (head_ok) {
+            const float inv = out_scale / lt;
+            f16 *orow = p.out + ((int64_t)b * p.Hq + qhead) * D + 4 * grp;
+#pragma unroll
+            for (int tau = 0; tau < DT; ++tau) {
+                const f16x4 hv = {(f16)(o[tau][0] * inv), (f16)(o[tau][1] * inv),
+                                  (f16)(o[tau][2] * inv), (f16)(o[tau][3] * inv)};
+                *reinterpret_cast<f16x4 *>(orow + 16 * tau) = hv;
+            }
+        }
+        return;
+    }
+
+    if (head_ok) {
+        const int64_t idx = ((int64_t)b * p.Hq + qhead) * p.max_splits + split;
+        float *wacc = p.ws_acc + idx * D + 4 * grp;
+#pragma unroll
+        for (int tau = 0; tau < DT; ++tau)
+            *reinterpret_cast<f32x4 *>(wacc + 16 * tau) = o[tau] * out_scale;
+        if (grp == 0)
+            *reinterpret_cast<float2 *>(p.ws_ml + 2 * idx) = make_float2(m, lt);
+    }
+    __threadfence();  // publish the partial before counting it
+    int prev = 0;
+    if (lane == 0)
+        prev = atomicAdd(p.ws_cnt + (int64_t)b * p.Hkv + h, 1);
+    prev = __builtin_amdgcn_readfirstlane(prev);
+    if (prev != nsplit - 1)
+        return;
+    __threadfence();  // see every other split's partial
+
+    // ---- last split of (b, h): log-sum-exp merge of its r query heads
+    for (int hh = 0; hh < p.r; ++hh) {
+        const int g = h * p.r + hh;
+        const int64_t base = ((int64_t)b * p.Hq + g) * p.max_splits;
+        float mx = -INFINITY;
+        for (int i = lane; i < nsplit; i += 64)
+            mx = fmaxf(mx, p.ws_ml[2 * (base + i)]);
+        mx = wave_max(mx);
+        float ls = 0.0f;
+        for (int i = lane; i < nsplit; i += 64)
+            ls += p.ws_ml[2 * (base + i) + 1] * __builtin_amdgcn_exp2f(p.ws_ml[2 * (base + i)] - mx);
+        ls = wave_sum(ls);
+        const float inv = 1.0f / ls;
+        for (int d = lane; d < D; d += 64) {
+            float acc = 0.0f;
+            for (int i = 0; i < nsplit; ++i)
+                acc += p.ws_acc[(base + i) * D + d] *
+                       __builtin_amdgcn_exp2f(p.ws_ml[2 * (base + i)] - mx);
+            p.out[((int64_t)b * p.Hq + g) * D + d] = (f16)(acc * inv);
+        }
+    }
+    if (lane == 0)
+        p.ws_cnt[(int64_t)b * p.Hkv + h] = 0;  // ready for the next call
+}
+
+}  // namespace kvq

@@ -1,0 +1,108 @@
+// kvq_device.hpp -- device-side helpers shared by the libkvq kernels (gfx950).
+//
+// Element conversions used inside the attention loops.  They turn stored
+// codes into exact fp16 values for the MFMA operands:
+//   INT8 code c (|c| <= 127) -> fp16 c exactly, via the 1024 + byte trick
+//     (an fp16 with exponent field 25 has a unit step, so the bit pattern
+//     0x6400 | u is the number 1024 + u for a byte u).
+//   E4M3 code -> fp16 equal to value * 2^-8 exactly: moving the 4 exponent
+//     and 3 mantissa bits into the fp16 fields keeps the mantissa and
+//     re-biases the exponent from 7 to 15 (subnormals land on fp16
+//     subnormals with the same factor); the 2^8 goes into the scale.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvq {
+
+enum { FMT_FP16 = 0, FMT_INT8 = 1, FMT_FP8 = 2 };
+
+typedef _Float16 f16;
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+template <typename To, typename From>
+__device__ __forceinline__ To bit_cast(const From &x)
+{
+    static_assert(sizeof(To) == sizeof(From), "size mismatch");
+    return __builtin_bit_cast(To, x);
+}
+
+// v_perm_b32: bytes 0..3 select from `lo`, 4..7 from `hi`, 0x0c -> 0x00.
+__device__ __forceinline__ uint32_t byte_perm(uint32_t hi, uint32_t lo,
+                                              uint32_t sel)
+{
+    return __builtin_amdgcn_perm(hi, lo, sel);
+}
+
+// Four INT8 codes (two's complement bytes of one dword) -> 4 exact fp16.
+__device__ __forceinline__ f16x4 int8x4_to_f16x4(uint32_t w)
+{
+    const uint32_t u = w ^ 0x80808080u;  // offset-binary: c + 128
+    const uint32_t lo = byte_perm(0x64646464u, u, 0x04010400u);
+    const uint32_t hi = byte_perm(0x64646464u, u, 0x04030402u);
+    const f16x2 bias = {(f16)1152.0f, (f16)1152.0f};
+    const f16x2 a = bit_cast<f16x2>(lo) - bias;  // (1024 + c + 128) - 1152
+    const f16x2 b = bit_cast<f16x2>(hi) - bias;
+    return f16x4{a.x, a.y, b.x, b.y};
+}
+
+// Four E4M3 bytes -> 4 fp16 holding value * 2^-8 exactly.
+__device__ __forceinline__ f16x4 fp8x4_to_f16x4_scaled(uint32_t w)
+{
+    const uint32_t t0 = byte_perm(0u, w, 0x0c010c00u);  // b0 in half 0, b1 in half 1
+    const uint32_t t1 = byte_perm(0u, w, 0x0c030c02u);
+    // (b + (b & 0x80)) << 7 puts the sign at bit 15, exponent/mantissa at 7..13
+    const uint32_t h0 = (t0 + (t0 & 0x00800080u)) << 7;
+    const uint32_t h1 = (t1 + (t1 & 0x00800080u)) << 7;
+    const f16x2 a = bit_cast<f16x2>(h0);
+    const f16x2 b = bit_cast<f16x2>(h1);
+    return f16x4{a.x, a.y, b.x, b.y};
+}
+
+__device__ __forceinline__ f16x4 f16x4_from_u2(uint32_t lo, uint32_t hi)
+{
+    const f16x2 a = bit_cast<f16x2>(lo);
+    const f16x2 b = bit_cast<f16x2>(hi);
+    return f16x4{a.x, a.y, b.x, b.y};
+}
+
+// Round to the nearest E4M3 value (ties to even), saturating to +-448; the
+// sign of a zero result is kept.  Bit-level, from the format definition.
+__device__ __forceinline__ uint32_t e4m3_rne_sat(float y)
+{
+    const uint32_t bits = __float_as_uint(y);
+    const uint32_t sign = (bits >> 24) & 0x80u;
+    const float a = __builtin_fabsf(y);
+    if (a != a)
+        return sign | 0x7fu;
+    if (!(a < 448.0f))
+        return sign | 0x7eu;
+    if (a < 0.015625f) {  // below 2^-6: fixed spacing 2^-9
+        const float q = __builtin_rintf(a * 512.0f);
+        return sign | (uint32_t)q;  // 0..8, 8 is the smallest normal
+    }
+    const uint32_t ab = __float_as_uint(a);
+    const uint32_t r = (ab + 0x7ffffu + ((ab >> 20) & 1u)) >> 20;  // 3 fraction bits, RNE
+    return sign | (r - (120u << 3));  // exponent bias 127 -> 7
+}
+
+__device__ __forceinline__ float wave_max(float x)
+{
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1)
+        x = fmaxf(x, __shfl_xor(x, o));
+    return x;
+}
+
+__device__ __forceinline__ float wave_sum(float x)
+{
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1)
+        x += __shfl_xor(x, o);
+    return x;
+}
+
+}  // namespace kvq

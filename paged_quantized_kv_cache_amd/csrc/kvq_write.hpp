@@ -1,0 +1,174 @@
+// kvq_write.hpp -- quantizing cache-write kernel and block-copy kernel.
+//
+// Cache write ("KV Cache优化实战" s1.1: the new token's K/V is appended to the
+// cache; s2.3 / s3.3: INT8 absmax symmetric per group of 64 or 128 elements,
+// with a stored scale; xpshop.cn article 312 s3: FP8 KV).
+//
+// One wavefront per (token, KV head): lanes 0..31 take K, lanes 32..63 take V,
+// each lane D/32 consecutive elements of the head.  A group of G elements is
+// spread over G/(D/32) neighbouring lanes; its absmax is reduced across them
+// with xor shuffles, so the scale and the codes come out in one pass.  K codes
+// are stored token-major (one dword per lane), V codes dim-major (the layout
+// the decode kernel's PV operand reads), scales next to the K/V codes of
+// their slot.
+#pragma once
+
+#include "kvq_device.hpp"
+
+namespace kvq {
+
+struct WriteParams {
+    const f16 *k;
+    const f16 *v;
+    const int64_t *slots;
+    uint8_t *k_pool;
+    uint8_t *v_pool;
+    float *k_scale;
+    float *v_scale;
+    int32_t num_tokens;
+    int32_t Hkv;
+    int32_t block_size;
+    int64_t num_slots;  // num_blocks * block_size
+};
+
+constexpr int kWriteWaves = 4;
+
+template <int FMT, int D, int G>
+__global__ __launch_bounds__(64 * kWriteWaves) void cache_write_kernel(WriteParams p)
+{
+#pragma clang fp contract(off)
+    constexpr int EPL = D / 32;               // elements per lane
+    const int wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int64_t pair = (int64_t)blockIdx.x * kWriteWaves + wave;
+    if (pair >= (int64_t)p.num_tokens * p.Hkv)
+        return;
+    const int t = (int)(pair / p.Hkv);
+    const int h = (int)(pair % p.Hkv);
+    const int64_t slot = p.slots[t];
+    if (slot < 0 || slot >= p.num_slots)
+        return;
+    const int BS = p.block_size;
+    const int64_t blk = slot / BS;
+    const int off = (int)(slot % BS);
+    const bool is_v = lane >= 32;
+    const int e0 = (lane & 31) * EPL;
+
+    const f16 *src = (is_v ? p.v : p.k) + ((int64_t)t * p.Hkv + h) * D + e0;
+    float x[EPL];
+    if constexpr (EPL == 4) {
+        const uint2 raw = *reinterpret_cast<const uint2 *>(src);
+        const f16x4 hv = f16x4_from_u2(raw.x, raw.y);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            x[i] = (float)hv[i];
+    } else {
+        const uint32_t raw = *reinterpret_cast<const uint32_t *>(src);
+        const f16x2 hv = bit_cast<f16x2>(raw);
+        x[0] = (float)hv.x;
+        x[1] = (float)hv.y;
+    }
+
+    const int64_t head_base = blk * p.Hkv + h;  // (block, head) tile index
+    uint32_t code[EPL];
+
+    if constexpr (FMT == FMT_INT8) {
+        constexpr int LPG = G / EPL;            // lanes per group
+        constexpr int NG = D / G;
+        float a = 0.0f;
+#pragma unroll
+        for (int i = 0; i < EPL; ++i)
+            a = fmaxf(a, __builtin_fabsf(x[i]));
+#pragma unroll
+        for (int o = 1; o < LPG; o <<= 1)
+            a = fmaxf(a, __shfl_xor(a, o));
+        const float s = a / 127.0f;             // IEEE division (correctly rounded)
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) {
+            float q = 0.0f;
+            if (s != 0.0f) {
+                q = __builtin_rintf(x[i] / s);  // round half to even
+                q = fminf(fmaxf(q, -127.0f), 127.0f);
+            }
+            code[i] = (uint32_t)(int32_t)q & 0xffu;
+        }
+        if ((lane & (LPG - 1)) == 0) {
+            float *sc = is_v ? p.v_scale : p.k_scale;
+            sc[(head_base * BS + off) * NG + (e0 / G)] = s;
+        }
+    } else if constexpr (FMT == FMT_FP8) {
+        const float S = (is_v ? p.v_scale : p.k_scale)[h];
+#pragma unroll
+        for (int i = 0; i < EPL; ++i)
+            code[i] = e4m3_rne_sat(x[i] / S);
+    }
+
+    if constexpr (FMT == FMT_FP16) {
+        // K: [blk][h][off][d]; V: [blk][h][d][off] (2-byte elements)
+        f16 *kp = reinterpret_cast<f16 *>(p.k_pool);
+        f16 *vp = reinterpret_cast<f16 *>(p.v_pool);
+        if (!is_v) {
+            f16 *dst = kp + (head_base * BS + off) * D + e0;
+#pragma unroll
+            for (int i = 0; i < EPL; ++i)
+                dst[i] = src[i];
+        } else {
+            f16 *dst = vp + (head_base * D + e0) * BS + off;
+#pragma unroll
+            for (int i = 0; i < EPL; ++i)
+                dst[(int64_t)i * BS] = src[i];
+        }
+    } else {
+        if (!is_v) {
+            uint8_t *dst = p.k_pool + (head_base * BS + off) * D + e0;
+            if constexpr (EPL == 4) {
+                *reinterpret_cast<uint32_t *>(dst) =
+                    code[0] | (code[1] << 8) | (code[2] << 16) | (code[3] << 24);
+            } else {
+                *reinterpret_cast<uint16_t *>(dst) = (uint16_t)(code[0] | (code[1] << 8));
+            }
+        } else {
+            uint8_t *dst = p.v_pool + (head_base * D + e0) * BS + off;
+#pragma unroll
+            for (int i = 0; i < EPL; ++i)
+                dst[(int64_t)i * BS] = (uint8_t)code[i];
+        }
+    }
+}
+
+// Whole-block copy for copy-on-write: codes of every slot (K and V) and, for
+// INT8, the scales of every slot.  blockIdx.x = pair, grid-stride over bytes.
+struct CopyParams {
+    const int32_t *pairs;
+    uint8_t *k_pool;
+    uint8_t *v_pool;
+    float *k_scale;
+    float *v_scale;
+    int64_t block_bytes;        // bytes of one block in one pool
+    int64_t scale_block_floats; // floats of one block in one scale array (0: none)
+    int32_t num_blocks;
+};
+
+__global__ __launch_bounds__(256) void copy_blocks_kernel(CopyParams p)
+{
+    const int32_t src = p.pairs[2 * blockIdx.x];
+    const int32_t dst = p.pairs[2 * blockIdx.x + 1];
+    if (src < 0 || dst < 0 || src >= p.num_blocks || dst >= p.num_blocks || src == dst)
+        return;
+    const int64_t n16 = p.block_bytes / 16;
+    const int64_t stride = (int64_t)blockDim.x * gridDim.y;
+    for (int64_t i = (int64_t)blockIdx.y * blockDim.x + threadIdx.x; i < n16; i += stride) {
+        const uint4 *ks = reinterpret_cast<const uint4 *>(p.k_pool + src * p.block_bytes);
+        uint4 *kd = reinterpret_cast<uint4 *>(p.k_pool + dst * p.block_bytes);
+        const uint4 *vs = reinterpret_cast<const uint4 *>(p.v_pool + src * p.block_bytes);
+        uint4 *vd = reinterpret_cast<uint4 *>(p.v_pool + dst * p.block_bytes);
+        kd[i] = ks[i];
+        vd[i] = vs[i];
+    }
+    for (int64_t i = (int64_t)blockIdx.y * blockDim.x + threadIdx.x; i < p.scale_block_floats; i += stride) {
+        p.k_scale[dst * p.scale_block_floats + i] = p.k_scale[src * p.scale_block_floats + i];
+        p.v_scale[dst * p.scale_block_floats + i] = p.v_scale[src * p.scale_block_floats + i];
+    }
+}
+
+}  // namespace kvq

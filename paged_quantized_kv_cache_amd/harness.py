@@ -1,0 +1,174 @@
+"""Drive the decode hot path on the GPU for a seeded workload.
+
+Builds the block layout on the host (``workloads.build_layout``), allocates one
+layer's pools with torch, and runs the library calls in the order a decode
+step uses them: prefill writes (all cached tokens), copy-on-write of shared
+partial blocks, the one-token append, then paged decode.  Only the library's
+kernels touch the pools.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import List, Optional
+
+import numpy as np
+import torch
+
+from . import kvq
+from . import workloads as W
+
+
+@dataclass
+class LayerPools:
+    fmt: str
+    k_pool: torch.Tensor
+    v_pool: torch.Tensor
+    k_scale: Optional[torch.Tensor]
+    v_scale: Optional[torch.Tensor]
+
+
+def poison_(pools: LayerPools, seed: int = 1234) -> None:
+    """Fill pools with values that would corrupt any result that read them:
+    NaN fp16 / NaN scales; INT8 codes at the extremes; E4M3 NaN bytes."""
+    g = torch.Generator(device=pools.k_pool.device)
+    g.manual_seed(seed)
+    if pools.fmt == "fp16":
+        pools.k_pool.fill_(float("nan"))
+        pools.v_pool.fill_(float("nan"))
+    elif pools.fmt == "int8":
+        pools.k_pool.fill_(-128)
+        pools.v_pool.fill_(127)
+        pools.k_scale.fill_(float("nan"))
+        pools.v_scale.fill_(float("inf"))
+    else:
+        pools.k_pool.fill_(0x7F)
+        pools.v_pool.fill_(0xFF)
+
+
+class DecodeCase:
+    """One workload on one device: layout, per-layer data and pools."""
+
+    def __init__(self, spec: W.Spec, device="cuda", gen_device=None,
+                 poison: bool = True, lens: Optional[np.ndarray] = None,
+                 layout_seed: Optional[int] = None):
+        self.spec = spec
+        self.device = torch.device(device)
+        self.gen_device = torch.device(gen_device) if gen_device else self.device
+        rng = np.random.default_rng(spec.seed)
+        self.lens = W.draw_lengths(spec, rng) if lens is None else np.asarray(lens, np.int64)
+        if layout_seed is not None:
+            rng = np.random.default_rng([spec.seed, layout_seed])
+        self.layout = W.build_layout(spec, self.lens, rng)
+        L = self.layout
+        # Table entries past a sequence's end point at a poisoned block that
+        # holds no data, never at an address outside the pool.
+        unused = sorted(set(range(L.num_blocks)) - set(int(x) for x in L.used_blocks))
+        self.pad_block = unused[0] if unused else 0
+        bt = L.block_tables.copy()
+        bt[bt < 0] = self.pad_block
+        dev = self.device
+        self.block_tables = torch.from_numpy(bt).to(dev)
+        self.context_lens = torch.from_numpy(self.lens.astype(np.int32)).to(dev)
+        self.max_context_len = int(self.lens.max())
+        self.prefill_slots = torch.from_numpy(L.prefill_slots).to(dev)
+        self.append_slots = torch.from_numpy(L.append_slots).to(dev)
+        self.prefill_ids = torch.from_numpy(L.prefill_ids).to(self.gen_device)
+        self.append_ids = torch.from_numpy(L.append_ids).to(self.gen_device)
+        self.cow_pairs = torch.from_numpy(L.cow_pairs.astype(np.int32)).to(dev)
+        self.poison = poison
+        self.pools: List[Optional[LayerPools]] = [None] * spec.layers
+        self.data: List[Optional[W.LayerData]] = [None] * spec.layers
+
+    # ------------------------------------------------------------ setup
+    def fmt(self, layer: int) -> str:
+        return self.spec.fmt_of_layer(layer)
+
+    def gen(self, layer: int) -> W.LayerData:
+        d = W.gen_layer(self.spec, self.layout.n_unique, layer, device=self.gen_device)
+        self.data[layer] = d
+        return d
+
+    def alloc(self, layer: int) -> LayerPools:
+        s, fmt = self.spec, self.fmt(layer)
+        kp, vp, ks, vs = kvq.alloc_pools(self.layout.num_blocks, s.Hkv, s.BS, s.D, fmt,
+                                         s.G, device=self.device)
+        pools = LayerPools(fmt, kp, vp, ks, vs)
+        if self.poison:
+            poison_(pools)
+        if fmt == "fp8":
+            d = self.data[layer]
+            pools.k_scale.copy_(W.fp8_static_scales(d.k))
+            pools.v_scale.copy_(W.fp8_static_scales(d.v))
+        self.pools[layer] = pools
+        return pools
+
+    def prefill(self, layer: int) -> None:
+        d, p, s = self.data[layer], self.pools[layer], self.spec
+        k = d.k.index_select(0, self.prefill_ids).to(self.device)
+        v = d.v.index_select(0, self.prefill_ids).to(self.device)
+        kvq.kvq_cache_write(k, v, self.prefill_slots, p.k_pool, p.v_pool, p.k_scale,
+                            p.v_scale, p.fmt, s.G)
+
+    def cow(self, layer: int) -> None:
+        p = self.pools[layer]
+        if self.cow_pairs.numel():
+            kvq.kvq_copy_blocks(self.cow_pairs, p.k_pool, p.v_pool, p.k_scale, p.v_scale,
+                                p.fmt, self.spec.G)
+
+    def append_inputs(self, layer: int):
+        d = self.data[layer]
+        return (d.k.index_select(0, self.append_ids).to(self.device).contiguous(),
+                d.v.index_select(0, self.append_ids).to(self.device).contiguous())
+
+    def append(self, layer: int, kv=None) -> None:
+        p, s = self.pools[layer], self.spec
+        k, v = kv if kv is not None else self.append_inputs(layer)
+        kvq.kvq_cache_write(k, v, self.append_slots, p.k_pool, p.v_pool, p.k_scale,
+                            p.v_scale, p.fmt, s.G)
+
+    def setup_layer(self, layer: int, keep_data: bool = True) -> None:
+        self.gen(layer)
+        self.alloc(layer)
+        self.prefill(layer)
+        self.cow(layer)
+        self.append(layer)
+        if not keep_data:
+            self.data[layer] = None
+
+    def workspace(self, split_tokens: int = 0) -> Optional[torch.Tensor]:
+        s = self.spec
+        n = kvq.kvq_decode_workspace_size(s.B, s.Hq, s.Hkv, s.D, s.BS,
+                                          self.max_context_len, split_tokens)
+        return kvq.alloc_workspace(n, self.device)
+
+    def decode(self, layer: int, q: Optional[torch.Tensor] = None, split_tokens: int = 0,
+               out=None, workspace=None, softmax_scale: float = 0.0) -> torch.Tensor:
+        p, s = self.pools[layer], self.spec
+        if q is None:
+            q = self.data[layer].q.to(self.device)
+        return kvq.kvq_paged_decode(q, p.k_pool, p.v_pool, p.k_scale, p.v_scale,
+                                    self.block_tables, self.context_lens,
+                                    self.max_context_len, p.fmt, s.G,
+                                    softmax_scale=softmax_scale, split_tokens=split_tokens,
+                                    out=out, workspace=workspace)
+
+    # ------------------------------------------------------------ readback
+    def gather_codes(self, layer: int, seqs=None):
+        """Read the pools back through the block tables: per sequence,
+        contiguous ``[ctx][Hkv][D]`` codes and ``[ctx][Hkv][D/G]`` scales
+        (host numpy), in logical token order."""
+        p, s = self.pools[layer], self.spec
+        bt = self.layout.block_tables
+        out = []
+        for b in (range(s.B) if seqs is None else seqs):
+            n = int(self.lens[b])
+            t = np.arange(n)
+            blk = torch.from_numpy(bt[b, t // s.BS].astype(np.int64)).to(self.device)
+            off = torch.from_numpy((t % s.BS).astype(np.int64)).to(self.device)
+            item = {"k": p.k_pool[blk, :, off, :].cpu().numpy(),      # [n][Hkv][D]
+                    "v": p.v_pool[blk, :, :, off].cpu().numpy()}      # [n][Hkv][D]
+            if p.fmt == "int8":
+                item["k_scale"] = p.k_scale[blk, :, off, :].cpu().numpy()
+                item["v_scale"] = p.v_scale[blk, :, off, :].cpu().numpy()
+            out.append(item)
+        return out

@@ -1,0 +1,234 @@
+"""Thin ctypes binding of libkvq.so (C ABI in include/kvq.h).
+
+Argument marshalling only: shapes are read off torch tensors, pointers and the
+current HIP stream are passed through, status codes become exceptions.  Every
+step of the computation runs in the library's HIP kernels; there is no CPU or
+PyTorch fallback -- if ``libkvq.so`` is missing, every call raises.
+
+Pool layout (per layer):
+  k_pool [num_blocks][Hkv][block_size][head_dim], v_pool [num_blocks][Hkv]
+  [head_dim][block_size]; element int8 (INT8), uint8 (FP8 E4M3 bytes) or
+  float16 (FP16).  INT8 scales [num_blocks][Hkv][block_size][head_dim/G]
+  fp32; FP8 scales [Hkv] fp32.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkvq.so")
+
+KVQ_FP16, KVQ_INT8, KVQ_FP8_E4M3 = 0, 1, 2
+FORMATS = {"fp16": KVQ_FP16, "int8": KVQ_INT8, "fp8": KVQ_FP8_E4M3}
+POOL_DTYPES = {"fp16": torch.float16, "int8": torch.int8, "fp8": torch.uint8}
+STATUS = {0: "KVQ_OK", -1: "KVQ_ERR_INVALID_ARG", -2: "KVQ_ERR_UNSUPPORTED",
+          -3: "KVQ_ERR_WORKSPACE", -4: "KVQ_ERR_HIP"}
+EXPORTS = ("kvq_status_string", "kvq_version", "kvq_cache_write",
+           "kvq_paged_decode", "kvq_decode_split_tokens",
+           "kvq_decode_workspace_size", "kvq_copy_blocks")
+
+
+class KvqError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__("%s: %s (%s)" % (what, STATUS.get(status, status),
+                                          _status_string(status)))
+
+
+_lock = threading.Lock()
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libkvq.so; raises if it has not been built."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise RuntimeError(
+                    "libkvq.so is missing (%s); build it with "
+                    "`python -c 'import __graft_entry__ as g; g.build()'`" % LIB_PATH)
+            L = ctypes.CDLL(LIB_PATH)
+            P, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+            L.kvq_status_string.restype = ctypes.c_char_p
+            L.kvq_status_string.argtypes = [i32]
+            L.kvq_version.restype = i32
+            L.kvq_version.argtypes = []
+            L.kvq_cache_write.restype = i32
+            L.kvq_cache_write.argtypes = [P, P, P, i32, i32, i32, i32, i32, i32,
+                                          i32, P, P, P, P, P]
+            L.kvq_paged_decode.restype = i32
+            L.kvq_paged_decode.argtypes = [P, P, P, P, P, P, i32, P, i32, i32,
+                                           i32, i32, i32, i32, i32, i32, i32,
+                                           ctypes.c_float, i32, P, P,
+                                           ctypes.c_size_t, P]
+            L.kvq_decode_split_tokens.restype = i32
+            L.kvq_decode_split_tokens.argtypes = [i32] * 5
+            L.kvq_decode_workspace_size.restype = ctypes.c_size_t
+            L.kvq_decode_workspace_size.argtypes = [i32] * 7
+            L.kvq_copy_blocks.restype = i32
+            L.kvq_copy_blocks.argtypes = [P, i32, i32, i32, i32, i32, i32, i32,
+                                          P, P, P, P, P]
+            _lib = L
+    return _lib
+
+
+def _status_string(status: int) -> str:
+    try:
+        return lib().kvq_status_string(status).decode()
+    except Exception:  # pragma: no cover - only used for messages
+        return "?"
+
+
+def _check(status: int, what: str) -> None:
+    if status != 0:
+        raise KvqError(status, what)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _fmt(fmt) -> int:
+    return FORMATS[fmt] if isinstance(fmt, str) else int(fmt)
+
+
+# ------------------------------------------------------------------ pools
+def alloc_pools(num_blocks: int, num_kv_heads: int, block_size: int,
+                head_dim: int, fmt: str, group_size: int = 0, device="cuda"):
+    """Allocate one layer's (k_pool, v_pool, k_scale, v_scale) with torch.
+
+    FP8 scales are returned as ones (the caller fills in its static scales);
+    FP16 has no scales (None)."""
+    dt = POOL_DTYPES[fmt]
+    kp = torch.empty((num_blocks, num_kv_heads, block_size, head_dim), dtype=dt, device=device)
+    vp = torch.empty((num_blocks, num_kv_heads, head_dim, block_size), dtype=dt, device=device)
+    if fmt == "int8":
+        ng = head_dim // group_size
+        ks = torch.empty((num_blocks, num_kv_heads, block_size, ng), dtype=torch.float32, device=device)
+        vs = torch.empty_like(ks)
+    elif fmt == "fp8":
+        ks = torch.ones(num_kv_heads, dtype=torch.float32, device=device)
+        vs = torch.ones_like(ks)
+    else:
+        ks = vs = None
+    return kp, vp, ks, vs
+
+
+def _pool_geometry(k_pool: torch.Tensor, fmt: str):
+    num_blocks, hkv, bs, d = k_pool.shape
+    if k_pool.dtype != POOL_DTYPES[fmt]:
+        raise TypeError("pool dtype %s does not match format %s" % (k_pool.dtype, fmt))
+    return num_blocks, hkv, bs, d
+
+
+# ------------------------------------------------------------------ calls
+def kvq_cache_write(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor,
+                    k_pool: torch.Tensor, v_pool: torch.Tensor,
+                    k_scale: Optional[torch.Tensor], v_scale: Optional[torch.Tensor],
+                    fmt: str, group_size: int = 0, stream=None) -> None:
+    """Quantize k, v ``[T][Hkv][D]`` fp16 into their slots (see kvq.h)."""
+    num_blocks, hkv, bs, d = _pool_geometry(k_pool, fmt)
+    T = k.shape[0]
+    if k.dtype != torch.float16 or v.dtype != torch.float16:
+        raise TypeError("k and v must be float16")
+    if k.shape != (T, hkv, d) or v.shape != k.shape:
+        raise ValueError("k/v shape %s does not match the pool" % (tuple(k.shape),))
+    if slot_mapping.dtype != torch.int64 or slot_mapping.numel() != T:
+        raise ValueError("slot_mapping must be int64 [T]")
+    for t in (k, v, slot_mapping, k_pool, v_pool):
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+    st = lib().kvq_cache_write(_ptr(k), _ptr(v), _ptr(slot_mapping), T, hkv, d, bs,
+                               num_blocks, _fmt(fmt), group_size, _ptr(k_pool),
+                               _ptr(v_pool), _ptr(k_scale), _ptr(v_scale),
+                               _stream(stream))
+    _check(st, "kvq_cache_write")
+
+
+def kvq_decode_split_tokens(num_seqs: int, num_kv_heads: int, block_size: int,
+                            max_context_len: int, split_tokens: int = 0) -> int:
+    return int(lib().kvq_decode_split_tokens(num_seqs, num_kv_heads, block_size,
+                                             max_context_len, split_tokens))
+
+
+def kvq_decode_workspace_size(num_seqs: int, num_q_heads: int, num_kv_heads: int,
+                              head_dim: int, block_size: int, max_context_len: int,
+                              split_tokens: int = 0) -> int:
+    n = int(lib().kvq_decode_workspace_size(num_seqs, num_q_heads, num_kv_heads,
+                                            head_dim, block_size, max_context_len,
+                                            split_tokens))
+    if n == ctypes.c_size_t(-1).value:
+        raise ValueError("invalid workspace arguments")
+    return n
+
+
+def alloc_workspace(nbytes: int, device="cuda") -> Optional[torch.Tensor]:
+    """Zero-filled workspace (the split counters must start at zero)."""
+    if nbytes == 0:
+        return None
+    return torch.zeros(nbytes, dtype=torch.uint8, device=device)
+
+
+def kvq_paged_decode(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
+                     k_scale: Optional[torch.Tensor], v_scale: Optional[torch.Tensor],
+                     block_tables: torch.Tensor, context_lens: torch.Tensor,
+                     max_context_len: int, fmt: str, group_size: int = 0,
+                     softmax_scale: float = 0.0, split_tokens: int = 0,
+                     out: Optional[torch.Tensor] = None,
+                     workspace: Optional[torch.Tensor] = None,
+                     stream=None) -> torch.Tensor:
+    """One decode step of paged attention (see kvq.h).  Returns ``out``."""
+    num_blocks, hkv, bs, d = _pool_geometry(k_pool, fmt)
+    B, hq, dq = q.shape
+    if q.dtype != torch.float16 or dq != d:
+        raise ValueError("q must be float16 [B][Hq][%d]" % d)
+    if block_tables.dtype != torch.int32 or block_tables.dim() != 2 or block_tables.shape[0] != B:
+        raise ValueError("block_tables must be int32 [B][max_blocks]")
+    if context_lens.dtype != torch.int32 or context_lens.numel() != B:
+        raise ValueError("context_lens must be int32 [B]")
+    if out is None:
+        out = torch.empty_like(q)
+    for t in (q, k_pool, v_pool, block_tables, context_lens, out):
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+    ws_need = kvq_decode_workspace_size(B, hq, hkv, d, bs, max_context_len, split_tokens) \
+        if B > 0 else 0
+    if workspace is None and ws_need:
+        workspace = alloc_workspace(ws_need, q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().kvq_paged_decode(_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(k_scale),
+                                _ptr(v_scale), _ptr(block_tables), block_tables.shape[1],
+                                _ptr(context_lens), max_context_len, B, hq, hkv, d, bs,
+                                num_blocks, _fmt(fmt), group_size, softmax_scale,
+                                split_tokens, _ptr(out), _ptr(workspace), ws_bytes,
+                                _stream(stream))
+    _check(st, "kvq_paged_decode")
+    return out
+
+
+def kvq_copy_blocks(block_pairs: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
+                    k_scale: Optional[torch.Tensor], v_scale: Optional[torch.Tensor],
+                    fmt: str, group_size: int = 0, stream=None) -> None:
+    """Copy whole blocks src -> dst (block_pairs int32 [n][2] on the device)."""
+    num_blocks, hkv, bs, d = _pool_geometry(k_pool, fmt)
+    if block_pairs.dtype != torch.int32 or (block_pairs.numel() and block_pairs.shape[-1] != 2):
+        raise ValueError("block_pairs must be int32 [n][2]")
+    n = block_pairs.numel() // 2
+    scale_ok = fmt == "int8"
+    st = lib().kvq_copy_blocks(_ptr(block_pairs), n, hkv, d, bs, num_blocks, _fmt(fmt),
+                               group_size, _ptr(k_pool), _ptr(v_pool),
+                               _ptr(k_scale) if scale_ok else None,
+                               _ptr(v_scale) if scale_ok else None, _stream(stream))
+    _check(st, "kvq_copy_blocks")

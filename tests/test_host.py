@@ -1,0 +1,205 @@
+"""Host-side logic on the CPU: block manager, layouts, and the C-ABI library
+(loads, exports every declared symbol, rejects bad arguments before touching
+any device)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+from paged_quantized_kv_cache_amd import workloads as W
+from paged_quantized_kv_cache_amd.block_manager import BlockManager, PoolExhausted
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+# ------------------------------------------------------------------ blocks
+def test_block_manager_alloc_fork_cow():
+    bm = BlockManager(8, 4, rng=np.random.default_rng(0))
+    bm.add_sequence(0)
+    slots = [bm.append_slot(0)[0] for _ in range(6)]     # 2 blocks
+    b0, b1 = bm.blocks(0)
+    assert slots[:4] == [b0 * 4 + i for i in range(4)]
+    assert slots[4:] == [b1 * 4, b1 * 4 + 1]
+    bm.fork(0, 1)
+    assert bm.refcount[b0] == 2 and bm.refcount[b1] == 2
+    slot, copy = bm.append_slot(1)                      # shared, partial -> COW
+    assert copy is not None and copy[0] == b1
+    nb = copy[1]
+    assert slot == nb * 4 + 2 and bm.blocks(1) == [b0, nb]
+    assert bm.refcount[b1] == 1
+    slot, copy = bm.append_slot(0)                      # now private: in place
+    assert copy is None and slot == b1 * 4 + 2
+    bm.drop_sequence(1)
+    assert bm.refcount[nb] == 0 and bm.refcount[b0] == 1
+    t = bm.tables(2)
+    assert list(t[0, :2]) == [b0, b1] and (t[1] == -1).all()
+
+
+def test_block_manager_exhaustion():
+    bm = BlockManager(2, 16)
+    bm.add_sequence(0)
+    for _ in range(32):
+        bm.append_slot(0)
+    with pytest.raises(PoolExhausted):
+        bm.append_slot(0)
+
+
+@pytest.mark.parametrize("name,over", [
+    ("c1_tiny", {}),
+    ("c3_gqa", dict(B=7, lens="fixed", lens_args=(1, 15, 16, 17, 100, 300, 31))),
+    ("c4_long_bs32", dict(B=3, lens="fixed", lens_args=(1, 33, 95))),
+    ("c5_prefix_mixed", dict(B=10, shared_prefix=64, lens_args=(3, 90), fork_pairs=3)),
+])
+def test_layout_gather_reproduces_contiguous(name, over):
+    """Writing every unique token into its slot (prefill, COW copies, append)
+    and gathering through the tables gives each sequence's tokens in order."""
+    s = W.spec(name, **over)
+    rng = np.random.default_rng(s.seed)
+    lens = W.draw_lengths(s, rng)
+    L = W.build_layout(s, lens, rng)
+    pool = np.full(L.num_blocks * s.BS, -1, np.int64)   # slot -> unique id
+    pool[L.prefill_slots] = L.prefill_ids
+    for src, dst in L.cow_pairs:
+        pool[dst * s.BS:(dst + 1) * s.BS] = pool[src * s.BS:(src + 1) * s.BS]
+    pool[L.append_slots] = L.append_ids
+    for b in range(s.B):
+        n = int(lens[b])
+        t = np.arange(n)
+        slots = L.block_tables[b, t // s.BS] * s.BS + t % s.BS
+        assert np.array_equal(pool[slots], L.seq_tokens[b])
+        assert L.seq_tokens[b][-1] == L.append_ids[b]
+    # every sequence's table is contiguous in logical order and has no gaps
+    assert (L.block_tables[L.block_tables >= 0] < L.num_blocks).all()
+    if s.shared_prefix:
+        pre = s.shared_prefix // s.BS
+        assert (L.block_tables[:, :pre] == L.block_tables[0, :pre]).all()
+        assert L.cow_pairs.shape == (s.fork_pairs, 2)
+    # appended slots are distinct
+    assert np.unique(L.append_slots).size == s.B
+
+
+def test_lengths_recipes():
+    s = W.spec("c3_gqa")
+    lens = W.draw_lengths(s, np.random.default_rng(0))
+    assert lens.min() >= 16 and lens.max() <= 8192
+    assert 1800 < np.median(lens) < 2300
+    s2 = W.spec("c2_mha")
+    l2 = W.draw_lengths(s2, np.random.default_rng(0))
+    assert l2.min() >= 1024 and l2.max() <= 3072
+    s5 = W.spec("c5_prefix_mixed")
+    l5 = W.draw_lengths(s5, np.random.default_rng(0))
+    assert (l5 >= 1024 + 64).all() and (l5 <= 1024 + 4097).all()
+    for k in range(s5.fork_pairs):
+        assert l5[2 * k] == l5[2 * k + 1] and (l5[2 * k] - 1024 - 1) % 16 != 0
+    assert s5.layer_fmts.count("fp16") == 5 and s5.layer_fmts[0] == "fp16"
+    assert s5.layer_fmts[28:] == ("fp16",) * 4
+
+
+def test_generated_inputs_have_outlier_channels():
+    s = W.spec("c3_gqa", B=2)
+    d = W.gen_layer(s, 4000, 0, device="cpu")
+    a = d.k.float().abs().mean(0)                        # [Hkv][D]
+    for h in range(s.Hkv):
+        big = (a[h] > 4).sum().item()
+        assert big == 5                                  # 4% of 128 -> 5 channels
+    assert d.v.float().abs().mean().item() < 1.0
+
+
+# ------------------------------------------------------------------ library
+@pytest.fixture(scope="module")
+def lib():
+    from paged_quantized_kv_cache_amd import build as B
+    from paged_quantized_kv_cache_amd import kvq
+    if B.stale():
+        B.build()
+    return kvq.lib()
+
+
+def _declared_symbols():
+    with open(os.path.join(ROOT, "include", "kvq.h")) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"KVQ_API\s+[\w\s\*]+?\b(kvq_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol(lib):
+    from paged_quantized_kv_cache_amd import kvq
+    names = _declared_symbols()
+    assert set(names) == set(kvq.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", kvq.LIB_PATH],
+                         capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r" T (kvq_\w+)", out))
+    assert exported == set(names)
+
+
+def test_status_strings_and_version(lib):
+    assert lib.kvq_version() >= 100
+    for code in (0, -1, -2, -3, -4, 7):
+        assert lib.kvq_status_string(code)
+
+
+def test_split_planner_and_workspace(lib):
+    from paged_quantized_kv_cache_amd import kvq
+    # short contexts: one split, no workspace
+    assert kvq.kvq_decode_split_tokens(4, 1, 16, 33) >= 33
+    assert kvq.kvq_decode_workspace_size(4, 4, 1, 64, 16, 33) == 0
+    # long contexts are split into spans of at most 1024 tokens
+    span = kvq.kvq_decode_split_tokens(16, 8, 16, 32768)
+    assert span % 16 == 0 and span <= 1024
+    ws = kvq.kvq_decode_workspace_size(16, 32, 8, 128, 16, 32768)
+    nsplit = -(-32768 // span)
+    assert ws >= 16 * 32 * nsplit * (128 + 2) * 4 + 16 * 8 * 4
+    # explicit spans
+    assert kvq.kvq_decode_split_tokens(2, 2, 16, 100, 32) == 32
+    assert kvq.kvq_decode_workspace_size(2, 4, 2, 64, 16, 100, 32) > 0
+    assert lib.kvq_decode_split_tokens(2, 2, 16, 100, 17) == -1
+    with pytest.raises(ValueError):
+        kvq.kvq_decode_workspace_size(2, 4, 2, 64, 16, 0)
+
+
+def test_bad_arguments_rejected_before_any_device_work(lib):
+    P = ctypes.c_void_p
+    dummy = P(16)
+    # unsupported formats / shapes
+    assert lib.kvq_cache_write(dummy, dummy, dummy, 1, 1, 96, 16, 4, 1, 32,
+                               dummy, dummy, dummy, dummy, None) == -2
+    assert lib.kvq_cache_write(dummy, dummy, dummy, 1, 1, 128, 8, 4, 1, 64,
+                               dummy, dummy, dummy, dummy, None) == -2
+    assert lib.kvq_cache_write(dummy, dummy, dummy, 1, 1, 64, 16, 4, 1, 128,
+                               dummy, dummy, dummy, dummy, None) == -2
+    assert lib.kvq_cache_write(dummy, dummy, dummy, 1, 1, 64, 16, 4, 7, 64,
+                               dummy, dummy, dummy, dummy, None) == -2
+    # null pointers
+    assert lib.kvq_cache_write(None, dummy, dummy, 1, 1, 64, 16, 4, 1, 64,
+                               dummy, dummy, dummy, dummy, None) == -1
+    # nothing to do
+    assert lib.kvq_cache_write(None, None, None, 0, 1, 64, 16, 4, 1, 64,
+                               None, None, None, None, None) == 0
+    args = dict(q=dummy, kp=dummy, vp=dummy, ks=dummy, vs=dummy, bt=dummy, mb=4,
+                cl=dummy, mcl=60, B=2, Hq=8, Hkv=2, D=64, BS=16, nb=8, dt=1, G=64,
+                sm=0.0, split=0, out=dummy, ws=None, wsb=0)
+
+    def dec(**kw):
+        a = dict(args, **kw)
+        return lib.kvq_paged_decode(a["q"], a["kp"], a["vp"], a["ks"], a["vs"], a["bt"],
+                                    a["mb"], a["cl"], a["mcl"], a["B"], a["Hq"], a["Hkv"],
+                                    a["D"], a["BS"], a["nb"], a["dt"], a["G"], a["sm"],
+                                    a["split"], a["out"], a["ws"], a["wsb"], None)
+    assert dec(Hq=6, Hkv=4) == -1                 # Hq % Hkv != 0
+    assert dec(Hq=68, Hkv=2) == -2                # more than 16 heads per KV head
+    assert dec(mcl=65) == -1                      # tables too short for the bound
+    assert dec(split=24) == -1                    # not a multiple of 16
+    assert dec(sm=-1.0) == -1
+    assert dec(q=None) == -1
+    assert dec(split=16) == -3                    # needs a workspace
+    assert dec(D=96) == -2
+    assert dec(B=0) == 0
+    assert dec(dt=1, ks=None) == -1
+    assert lib.kvq_copy_blocks(dummy, 1, 1, 64, 16, 4, 1, 64, dummy, dummy, None, None,
+                               None) == -1
+    assert lib.kvq_copy_blocks(None, 0, 1, 64, 16, 4, 1, 64, None, None, None, None,
+                               None) == 0
