@@ -1,0 +1,286 @@
+#!/usr/bin/env python3
+"""Benchmark of the paged INT8 GQA decode hot path on one MI355X.
+
+One step = the whole hot path for one batch: the quantizing cache write of
+one new token per sequence (kvq_cache_write) followed by paged decode
+attention over the INT8 pool (kvq_paged_decode), for every layer of the
+workload.  Inputs are seeded synthetic data resident in HBM before timing.
+
+Prints one JSON line.  `value` is seq-steps/s (sequences x steps / second).
+`roofline` prices the decode kernel (the dominant one) against MI355X HBM
+bandwidth using algorithmic bytes (every valid cached K/V code and scale
+once, plus q, out, table entries and lengths) over its event-timed duration.
+`cpu_baseline` times the CPU oracle on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "paged INT8 GQA decode-attn seq-steps/s + achieved HBM GB/s (% of MI355X peak)"
+HBM_PEAK_GBPS = 8000.0
+DEFAULT_WORKLOAD = "c3_gqa"
+KERNEL_SOURCES = ("kvq_decode.hpp", "kvq_device.hpp", "kvq_api.hip")
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "paged_quantized_kv_cache_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload: str):
+    """HBM bytes per decode launch from committed rocprofv3 counter runs, if
+    they were taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic_%s.json" % workload)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_hash") != kernel_hash():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(case, layer_inputs, spec, max_seqs: int, min_seconds: float = 10.0):
+    """Time the oracle (as it stands) on the first `max_seqs` sequences of the
+    workload: quantize their appended tokens, dequantize their cached K/V and
+    attend in fp64."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from oracle import expected as E
+
+    layers = [0] if spec.layers == 1 else list(range(spec.layers))
+    nseq = min(max_seqs, spec.B)
+    seqs = list(range(nseq))
+    total = 0.0
+    ntok = 0
+    passes = 0
+    for layer in layers:
+        d = case.data[layer] if case.data[layer] is not None else case.gen(layer)
+        ids = np.unique(np.concatenate([case.layout.seq_tokens[b] for b in seqs]))
+        remap = np.full(case.layout.n_unique, -1, np.int64)
+        remap[ids] = np.arange(ids.size)
+        k16 = d.k[torch.from_numpy(ids).to(d.k.device)].cpu().numpy()
+        v16 = d.v[torch.from_numpy(ids).to(d.v.device)].cpu().numpy()
+        q = d.q[:nseq].cpu().numpy()
+        fmt = spec.fmt_of_layer(layer)
+        sk = sv = None
+        if fmt == "fp8":
+            sk = case.pools[layer].k_scale.cpu().numpy()
+            sv = case.pools[layer].v_scale.cpu().numpy()
+        toks = [remap[case.layout.seq_tokens[b]] for b in seqs]
+        t0 = time.perf_counter()
+        kq = E.quantize(k16, fmt, spec.G, sk)
+        vq = E.quantize(v16, fmt, spec.G, sv)
+        E.attention(q, kq, vq, toks)
+        total += time.perf_counter() - t0
+        ntok += int(sum(len(t) for t in toks))
+        if spec.layers > 1:
+            case.data[layer] = None
+    passes = 1
+    if spec.layers == 1:
+        # repeat the same sample until about min_seconds of CPU work
+        while total < min_seconds and passes < 20:
+            t0 = time.perf_counter()
+            kq = E.quantize(k16, fmt, spec.G, sk)
+            vq = E.quantize(v16, fmt, spec.G, sv)
+            E.attention(q, kq, vq, toks)
+            total += time.perf_counter() - t0
+            passes += 1
+    return {
+        "value": nseq * passes / total,
+        "unit": "seq-steps/s",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": "first %d of %d sequences (%d cached tokens per layer-pass, %d layer(s)): "
+                  "quantize every cached and appended token, dequantize, fp64 attention; "
+                  "%d pass(es), %.1f s" % (nseq, spec.B, ntok // len(layers), len(layers),
+                                           passes, total),
+    }
+
+
+def copy_bandwidth(nbytes: int = 2 << 30, reps: int = 5) -> float:
+    """Measured streaming copy (torch) bandwidth, read + write bytes / time."""
+    import torch
+    a = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / reps
+    del a, b
+    return 2 * nbytes / dt / 1e9
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--cpu-seqs", type=int, default=256,
+                    help="sequences in the CPU-oracle sample (0 = skip)")
+    ap.add_argument("--cpu-min-seconds", type=float, default=10.0)
+    ap.add_argument("--copy-calib-bytes", type=int, default=0,
+                    help="also run one plain copy of this many bytes (counter calibration)")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: the decode path has no cross-GPU "
+              "stage in this build (--gpus %d requested)" % args.gpus, file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    from paged_quantized_kv_cache_amd import kvq
+    from paged_quantized_kv_cache_amd import workloads as W
+    from paged_quantized_kv_cache_amd.harness import DecodeCase
+
+    kvq.lib()
+    dev = torch.device("cuda:0")
+    spec = W.spec(args.workload)
+    t_setup = time.perf_counter()
+    case = DecodeCase(spec, device=dev, poison=False)
+    inputs = []
+    for layer in range(spec.layers):
+        case.setup_layer(layer, keep_data=(spec.layers == 1))
+        if spec.layers == 1:
+            k, v = case.append_inputs(layer)
+            q = case.data[layer].q
+        else:
+            d = case.data[layer] if case.data[layer] is not None else None
+            # setup_layer dropped the data; regenerate only what a step needs
+            d = W.gen_layer(spec, case.layout.n_unique, layer, device=dev)
+            k = d.k.index_select(0, case.append_ids).contiguous()
+            v = d.v.index_select(0, case.append_ids).contiguous()
+            q = d.q
+            del d
+        inputs.append((k, v, q.contiguous(), torch.empty_like(q)))
+    ws = case.workspace(0)
+    torch.cuda.synchronize()
+    setup_s = time.perf_counter() - t_setup
+    print("setup %.1fs: %s, %d seqs, %d cached tokens, pool %d blocks" %
+          (setup_s, spec.name, spec.B, int(case.lens.sum()), case.layout.num_blocks),
+          file=sys.stderr, flush=True)
+
+    stream = torch.cuda.current_stream()
+    nl = spec.layers
+
+    def step(events=None):
+        for layer in range(nl):
+            k, v, q, out = inputs[layer]
+            case.append(layer, (k, v))
+            if events is not None:
+                events[layer][0].record(stream)
+            case.decode(layer, q=q, out=out, workspace=ws)
+            if events is not None:
+                events[layer][1].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region: exactly `steps` steps, synchronized on both sides
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(nl)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(ev[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+
+    # decode kernel durations (one launch per layer per step)
+    dec_ms = np.array([[ev[i][l][0].elapsed_time(ev[i][l][1]) for l in range(nl)]
+                       for i in range(args.steps)])
+    per_layer_ms = dec_ms.mean(0)
+    fmts = [spec.fmt_of_layer(l) for l in range(nl)]
+    uniq = None
+    if spec.shared_prefix:
+        uniq = case.layout.n_unique  # shared blocks counted once
+    layer_bytes = [W.algorithmic_bytes(spec, case.lens, f, unique_tokens=uniq) for f in fmts]
+    # dominant kernel: the INT8 decode (all layers of that format)
+    dom = [l for l in range(nl) if fmts[l] == "int8"] or list(range(nl))
+    dom_ms = float(np.mean(per_layer_ms[dom]))
+    dom_bytes = float(np.mean([layer_bytes[l] for l in dom]))
+    achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
+    traffic = load_traffic(spec.name)
+
+    copy_gbps = copy_bandwidth()
+    if args.copy_calib_bytes:
+        a = torch.zeros(args.copy_calib_bytes, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    result = {
+        "metric": METRIC,
+        "value": spec.B / (ms_per_step * 1e-3),
+        "unit": "seq-steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8" if "int8" in fmts else fmts[0],
+        "data": "synthetic (seeded N(0,1) fp16 K/V/Q with outlier channels, "
+                "shuffled block pool)",
+        "config": {
+            "workload": spec.name,
+            "description": spec.description,
+            "num_seqs": spec.B, "layers": nl, "num_q_heads": spec.Hq,
+            "num_kv_heads": spec.Hkv, "head_dim": spec.D, "block_size": spec.BS,
+            "kv_format": fmts[0] if nl == 1 else "mixed",
+            "group_size": spec.G, "cached_tokens": int(case.lens.sum()),
+            "mean_context": float(case.lens.mean()),
+            "max_context": int(case.lens.max()),
+            "split_tokens": kvq.kvq_decode_split_tokens(spec.B, spec.Hkv, spec.BS,
+                                                        case.max_context_len, 0),
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": traffic,
+            "kernel": "paged_decode_kernel (%s)" % ("int8" if "int8" in fmts else fmts[0]),
+            "algorithmic_bytes_per_launch": int(dom_bytes),
+            "avg_launch_ms": round(dom_ms, 5),
+        },
+        "decode_ms_per_layer": [round(float(x), 5) for x in per_layer_ms] if nl > 1 else None,
+        "measured_copy_gbps": round(copy_gbps, 1),
+        "setup_s": round(setup_s, 1),
+    }
+    if args.cpu_seqs > 0:
+        result["cpu_baseline"] = cpu_baseline(case, inputs, spec, args.cpu_seqs,
+                                              args.cpu_min_seconds)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

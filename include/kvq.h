@@ -123,17 +123,19 @@ KVQ_API kvq_status kvq_cache_write(const void *k, const void *v,
  *                 (used to plan the split) and must not exceed
  *                 max_blocks_per_seq * block_size.
  *   softmax_scale 0 selects 1 / sqrt(head_dim).
- *   split_tokens  0 = automatic; otherwise a multiple of 16: every sequence
+ *   split_tokens  0 = automatic; otherwise a multiple of 16 and at most
+ *                 64 * block_size (INVALID_ARG otherwise): every sequence
  *                 is cut into spans of split_tokens logical tokens, each
  *                 attended separately and merged exactly (log-sum-exp).
  *                 The split depends only on logical positions, so results do
  *                 not depend on which physical blocks hold the data.
  *   out           fp16 [num_seqs][num_q_heads][head_dim] (written).
  *   workspace     device scratch of at least kvq_decode_workspace_size(...)
- *                 bytes (may be NULL when that size is 0).  It must be
- *                 zero-filled before its first use; every call leaves it
- *                 ready for the next one.  Calls sharing a workspace must be
- *                 ordered (same stream).
+ *                 bytes (may be NULL when that size is 0); its contents on
+ *                 entry do not matter.  It holds the per-split partial results
+ *                 (running max, sum and unnormalized output) between the split
+ *                 launch and the merge launch of the same call, so calls
+ *                 sharing a workspace must be ordered (same stream).
  */
 KVQ_API kvq_status kvq_paged_decode(const void *q, const void *k_pool,
                             const void *v_pool, const float *k_scale,

@@ -24,6 +24,9 @@ FLAGS = [
     "-fno-fast-math",
     # no packed-fp32 instructions anywhere
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # keep MFMA accumulators in ordinary VGPRs (no AGPR copies around the
+    # online-softmax rescale)
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall", "-Wno-unused-variable", "-Wno-unused-but-set-variable",
 ]
 

@@ -76,8 +76,11 @@ constexpr int kAutoMaxSpan = 1024;
 constexpr int kAutoMinSpan = 256;
 constexpr int kTargetItems = 2048;
 
-int32_t plan_span(int32_t num_seqs, int32_t num_kv_heads, int32_t max_ctx,
-                  int32_t split_tokens)
+// A split covers at most kMaxSplitBlocks blocks (one block id per lane).
+constexpr int kMaxSplitBlocks = 64;
+
+int32_t plan_span(int32_t num_seqs, int32_t num_kv_heads, int32_t block_size,
+                  int32_t max_ctx, int32_t split_tokens)
 {
     if (split_tokens > 0)
         return split_tokens;
@@ -93,32 +96,39 @@ int32_t plan_span(int32_t num_seqs, int32_t num_kv_heads, int32_t max_ctx,
         span = kAutoMinSpan;
     if (span >= max_ctx)
         span = (max_ctx + 15) / 16 * 16;  // one split
+    if (span > (int64_t)kMaxSplitBlocks * block_size)
+        span = (int64_t)kMaxSplitBlocks * block_size;
     return (int32_t)span;
 }
 
 struct WsLayout {
-    size_t cnt_off, ml_off, acc_off, total;
+    size_t ml_off, acc_off, total;
     int32_t span, max_splits;
 };
 
+bool valid_split(int32_t block_size, int32_t split_tokens)
+{
+    return split_tokens >= 0 && split_tokens % 16 == 0 &&
+           split_tokens <= kMaxSplitBlocks * block_size;
+}
+
 bool workspace_layout(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
-                      int32_t head_dim, int32_t max_ctx, int32_t split_tokens,
-                      WsLayout &w)
+                      int32_t head_dim, int32_t block_size, int32_t max_ctx,
+                      int32_t split_tokens, WsLayout &w)
 {
     if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
-        max_ctx < 1 || split_tokens < 0 || split_tokens % 16 != 0)
+        max_ctx < 1 || (block_size != 16 && block_size != 32) ||
+        !valid_split(block_size, split_tokens))
         return false;
-    w.span = plan_span(num_seqs, num_kv_heads, max_ctx, split_tokens);
+    w.span = plan_span(num_seqs, num_kv_heads, block_size, max_ctx, split_tokens);
     w.max_splits = (max_ctx + w.span - 1) / w.span;
     if (w.max_splits <= 1 || num_seqs == 0) {
-        w.cnt_off = w.ml_off = w.acc_off = w.total = 0;
+        w.ml_off = w.acc_off = w.total = 0;
         return true;
     }
     auto up256 = [](size_t x) { return (x + 255) / 256 * 256; };
-    const size_t cnt = (size_t)num_seqs * num_kv_heads * sizeof(int32_t);
     const size_t items = (size_t)num_seqs * num_q_heads * w.max_splits;
-    w.cnt_off = 0;
-    w.ml_off = up256(cnt);
+    w.ml_off = 0;
     w.acc_off = w.ml_off + up256(items * 2 * sizeof(float));
     w.total = w.acc_off + up256(items * head_dim * sizeof(float));
     return true;
@@ -162,6 +172,9 @@ void launch_decode(const DecodeParams &p, int B, int Hkv, int splits, hipStream_
     hipLaunchKernelGGL((paged_decode_kernel<FMT, D, BS, NG>),
                        dim3((unsigned)splits, (unsigned)Hkv, (unsigned)B), dim3(64), 0, s,
                        p);
+    if (splits > 1)
+        hipLaunchKernelGGL((merge_splits_kernel<D>), dim3((unsigned)p.Hq, (unsigned)B),
+                           dim3(64), 0, s, p);
 }
 
 template <int FMT, int D, int BS>
@@ -258,21 +271,19 @@ kvq_status kvq_cache_write(const void *k, const void *v, const int64_t *slot_map
 int32_t kvq_decode_split_tokens(int32_t num_seqs, int32_t num_kv_heads, int32_t block_size,
                                 int32_t max_context_len, int32_t split_tokens)
 {
-    (void)block_size;
-    if (num_seqs < 0 || num_kv_heads <= 0 || max_context_len < 1 || split_tokens < 0 ||
-        split_tokens % 16 != 0)
+    if (num_seqs < 0 || num_kv_heads <= 0 || max_context_len < 1 ||
+        (block_size != 16 && block_size != 32) || !valid_split(block_size, split_tokens))
         return -1;
-    return plan_span(num_seqs, num_kv_heads, max_context_len, split_tokens);
+    return plan_span(num_seqs, num_kv_heads, block_size, max_context_len, split_tokens);
 }
 
 size_t kvq_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                  int32_t head_dim, int32_t block_size,
                                  int32_t max_context_len, int32_t split_tokens)
 {
-    (void)block_size;
     WsLayout w;
-    if (!workspace_layout(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len,
-                          split_tokens, w))
+    if (!workspace_layout(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                          max_context_len, split_tokens, w))
         return SIZE_MAX;
     return w.total;
 }
@@ -304,7 +315,7 @@ kvq_status kvq_paged_decode(const void *q, const void *k_pool, const void *v_poo
         return KVQ_OK;
     if (max_context_len < 1 || (int64_t)max_blocks_per_seq * block_size < max_context_len)
         return KVQ_ERR_INVALID_ARG;
-    if (split_tokens < 0 || split_tokens % 16 != 0)
+    if (!valid_split(block_size, split_tokens))
         return KVQ_ERR_INVALID_ARG;
     if (!(softmax_scale >= 0.0f) || std::isinf(softmax_scale))
         return KVQ_ERR_INVALID_ARG;
@@ -317,8 +328,8 @@ kvq_status kvq_paged_decode(const void *q, const void *k_pool, const void *v_poo
         return KVQ_ERR_INVALID_ARG;
 
     WsLayout w;
-    if (!workspace_layout(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len,
-                          split_tokens, w))
+    if (!workspace_layout(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                          max_context_len, split_tokens, w))
         return KVQ_ERR_INVALID_ARG;
     if (w.total > 0 && (!workspace || workspace_bytes < w.total || !aligned16(workspace)))
         return KVQ_ERR_WORKSPACE;
@@ -336,7 +347,6 @@ kvq_status kvq_paged_decode(const void *q, const void *k_pool, const void *v_poo
     p.context_lens = context_lens;
     p.out = static_cast<f16 *>(out);
     uint8_t *ws = static_cast<uint8_t *>(workspace);
-    p.ws_cnt = w.total ? reinterpret_cast<int32_t *>(ws + w.cnt_off) : nullptr;
     p.ws_ml = w.total ? reinterpret_cast<float *>(ws + w.ml_off) : nullptr;
     p.ws_acc = w.total ? reinterpret_cast<float *>(ws + w.acc_off) : nullptr;
     p.max_blocks = max_blocks_per_seq;

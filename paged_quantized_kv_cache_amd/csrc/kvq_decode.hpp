@@ -30,9 +30,9 @@
 //
 // Online softmax in base 2 (the log2(e) factor rides on the score scale), with
 // a rescale of the running output only when some head's maximum grows.
-// Splits of one (b, h) write (m, l, acc) partials; the last wavefront of the
-// (b, h) to finish (atomic counter) merges them with a log-sum-exp and resets
-// the counter, so a single kernel launch produces the output.
+// Splits of one (b, h) write (m, l, acc) partials that a second, small launch
+// merges with a log-sum-exp; a sequence that fits one split is finished by
+// the split kernel itself.
 #pragma once
 
 #include "kvq_device.hpp"
@@ -50,7 +50,6 @@ struct DecodeParams {
     f16 *out;
     float *ws_acc;    // [B][Hq][max_splits][D]
     float *ws_ml;     // [B][Hq][max_splits][2]
-    int32_t *ws_cnt;  // [B][Hkv]
     int32_t max_blocks;
     int32_t max_ctx;     // host bound on context_lens (<= max_blocks * BS)
     int32_t num_blocks;
@@ -173,20 +172,16 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
         out_scale = 256.0f * p.v_scale[h];
     }
 
-    // ---- block table: a window of 64 consecutive logical blocks in a VGPR
+    // ---- block table: the split's (at most 64) logical blocks, one per lane
     const int32_t *bt = p.block_tables + (int64_t)b * p.max_blocks;
+    const int blk0 = t_begin / BS;
     const int blk_last = (t_end - 1) / BS;
-    int win_base = t_begin / BS;
-    int win = (win_base + lane <= blk_last) ? bt[win_base + lane] : 0;
-
-    auto phys_of = [&](int lblk) -> int {
-        if (lblk - win_base >= 64) {  // wave-uniform
-            win_base = lblk;
-            win = (win_base + lane <= blk_last) ? bt[win_base + lane] : 0;
-        }
-        const int id = __builtin_amdgcn_readlane(win, lblk - win_base);
+    const int win = (blk0 + lane <= blk_last) ? bt[blk0 + lane] : 0;
+    auto tile_phys = [&](int it) -> int {
+        const int id = __builtin_amdgcn_readlane(win, (t_begin + 16 * it) / BS - blk0);
         return min(max(id, 0), p.num_blocks - 1);  // never leave the pool
     };
+    auto tile_off = [&](int it) -> int { return (t_begin + 16 * it) % BS; };
 
     f32x4 o[DT];
 #pragma unroll
@@ -295,19 +290,18 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
     };
 
     // Ping-pong over two tile buffers: the loads of tile i+1 are in flight
-    // while tile i is computed.
+    // while tile i is computed.  Loads are issued unconditionally (past the
+    // end they repeat the last tile) so the wait counts stay static.
     TileData<FMT, D> buf0, buf1;
-    load_tile<FMT, D, BS, NG>(p, buf0, phys_of(t_begin / BS), h, t_begin % BS, col, grp);
+    load_tile<FMT, D, BS, NG>(p, buf0, tile_phys(0), h, tile_off(0), col, grp);
     for (int it = 0; it < ntiles; it += 2) {
-        const int ts = t_begin + 16 * it;
+        const int i1 = min(it + 1, ntiles - 1);
+        load_tile<FMT, D, BS, NG>(p, buf1, tile_phys(i1), h, tile_off(i1), col, grp);
+        process(buf0, t_begin + 16 * it);
+        const int i2 = min(it + 2, ntiles - 1);
+        load_tile<FMT, D, BS, NG>(p, buf0, tile_phys(i2), h, tile_off(i2), col, grp);
         if (it + 1 < ntiles)
-            load_tile<FMT, D, BS, NG>(p, buf1, phys_of((ts + 16) / BS), h, (ts + 16) % BS, col, grp);
-        process(buf0, ts);
-        if (it + 1 >= ntiles)
-            break;
-        if (it + 2 < ntiles)
-            load_tile<FMT, D, BS, NG>(p, buf0, phys_of((ts + 32) / BS), h, (ts + 32) % BS, col, grp);
-        process(buf1, ts + 16);
+            process(buf1, t_begin + 16 * (it + 1));
     }
 
     // ---- epilogue
@@ -337,38 +331,49 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
         if (grp == 0)
             *reinterpret_cast<float2 *>(p.ws_ml + 2 * idx) = make_float2(m, lt);
     }
-    __threadfence();  // publish the partial before counting it
-    int prev = 0;
-    if (lane == 0)
-        prev = atomicAdd(p.ws_cnt + (int64_t)b * p.Hkv + h, 1);
-    prev = __builtin_amdgcn_readfirstlane(prev);
-    if (prev != nsplit - 1)
-        return;
-    __threadfence();  // see every other split's partial
+}
 
-    // ---- last split of (b, h): log-sum-exp merge of its r query heads
-    for (int hh = 0; hh < p.r; ++hh) {
-        const int g = h * p.r + hh;
-        const int64_t base = ((int64_t)b * p.Hq + g) * p.max_splits;
-        float mx = -INFINITY;
-        for (int i = lane; i < nsplit; i += 64)
-            mx = fmaxf(mx, p.ws_ml[2 * (base + i)]);
-        mx = wave_max(mx);
-        float ls = 0.0f;
-        for (int i = lane; i < nsplit; i += 64)
-            ls += p.ws_ml[2 * (base + i) + 1] * __builtin_amdgcn_exp2f(p.ws_ml[2 * (base + i)] - mx);
-        ls = wave_sum(ls);
-        const float inv = 1.0f / ls;
-        for (int d = lane; d < D; d += 64) {
-            float acc = 0.0f;
-            for (int i = 0; i < nsplit; ++i)
-                acc += p.ws_acc[(base + i) * D + d] *
-                       __builtin_amdgcn_exp2f(p.ws_ml[2 * (base + i)] - mx);
-            p.out[((int64_t)b * p.Hq + g) * D + d] = (f16)(acc * inv);
-        }
+// Log-sum-exp merge of the split partials of one (sequence, query head):
+//   M = max_i m_i,  L = sum_i l_i 2^(m_i - M),  out = sum_i acc_i 2^(m_i - M) / L.
+// Runs as its own launch after the split kernel, so the partials written by
+// wavefronts on any XCD are visible without device-wide fences inside the
+// split kernel.  Sequences that were not split were finished by that kernel.
+template <int D>
+__global__ __launch_bounds__(64) void merge_splits_kernel(DecodeParams p)
+{
+    const int g = blockIdx.x;
+    const int b = blockIdx.y;
+    const int lane = threadIdx.x;
+    const int ctx = min(p.context_lens[b], p.max_ctx);
+    const int nsplit = (ctx + p.span - 1) / p.span;
+    if (nsplit <= 1)
+        return;
+    const int64_t base = ((int64_t)b * p.Hq + g) * p.max_splits;
+    float mx = -INFINITY;
+    for (int i = lane; i < nsplit; i += 64)
+        mx = fmaxf(mx, p.ws_ml[2 * (base + i)]);
+    mx = wave_max(mx);
+    float ls = 0.0f;
+    for (int i = lane; i < nsplit; i += 64)
+        ls += p.ws_ml[2 * (base + i) + 1] * __builtin_amdgcn_exp2f(p.ws_ml[2 * (base + i)] - mx);
+    ls = wave_sum(ls);
+    const float inv = 1.0f / ls;
+    constexpr int PER = D / 64;
+    float acc[PER];
+#pragma unroll
+    for (int j = 0; j < PER; ++j)
+        acc[j] = 0.0f;
+    for (int i = 0; i < nsplit; ++i) {
+        const float w = __builtin_amdgcn_exp2f(p.ws_ml[2 * (base + i)] - mx);
+        const float *a = p.ws_acc + (base + i) * D + PER * lane;
+#pragma unroll
+        for (int j = 0; j < PER; ++j)
+            acc[j] += a[j] * w;
     }
-    if (lane == 0)
-        p.ws_cnt[(int64_t)b * p.Hkv + h] = 0;  // ready for the next call
+    f16 *orow = p.out + ((int64_t)b * p.Hq + g) * D + PER * lane;
+#pragma unroll
+    for (int j = 0; j < PER; ++j)
+        orow[j] = (f16)(acc[j] * inv);
 }
 
 }  // namespace kvq

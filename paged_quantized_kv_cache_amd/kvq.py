@@ -175,10 +175,10 @@ def kvq_decode_workspace_size(num_seqs: int, num_q_heads: int, num_kv_heads: int
 
 
 def alloc_workspace(nbytes: int, device="cuda") -> Optional[torch.Tensor]:
-    """Zero-filled workspace (the split counters must start at zero)."""
+    """Decode workspace (contents on entry do not matter)."""
     if nbytes == 0:
         return None
-    return torch.zeros(nbytes, dtype=torch.uint8, device=device)
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
 
 
 def kvq_paged_decode(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,

@@ -124,8 +124,9 @@ def test_decode_within_tolerance(name, gpu):
         got = _host(case.decode(0, split_tokens=split, workspace=ws)).astype(np.float64)
         _check_out(got, ref, "%s split=%d" % (name, split))
         outs[split] = got
-    # splitting changes only the rounding of the merge
-    assert np.max(np.abs(outs[0] - outs[16])) < 4e-3
+    # splitting changes only rounding: the variants agree within twice the bound
+    for split in (16, 64, 1024):
+        assert np.all(np.abs(outs[0] - outs[split]) <= 2 * (ATOL + RTOL * np.abs(ref)))
 
 
 def test_decode_repeat_reuses_workspace(gpu):
@@ -135,7 +136,7 @@ def test_decode_repeat_reuses_workspace(gpu):
     a = case.decode(0, split_tokens=16, workspace=ws).clone()
     for _ in range(3):
         b = case.decode(0, split_tokens=16, workspace=ws)
-        assert torch.equal(a, b)  # counters were reset; results deterministic
+        assert torch.equal(a, b)  # deterministic; stale workspace contents unused
 
 
 def test_results_independent_of_physical_placement(gpu):
@@ -191,20 +192,41 @@ def test_shared_prefix_and_cow(fmt, gpu):
 
 
 def test_cow_leaves_other_sharer_untouched(gpu):
+    """The writer gets a private copy of the shared partial block; the slots
+    filled before the append stay unchanged for the other sharer, which then
+    appends into the original block in place."""
     spec = _prefix_spec("int8")
     case = DecodeCase(spec, device=gpu, gen_device="cpu")
     case.gen(0)
     case.alloc(0)
     case.prefill(0)
     p = case.pools[0]
-    src = torch.from_numpy(case.layout.cow_pairs[:, 0].astype(np.int64)).to(gpu)
-    before = (p.k_pool[src].clone(), p.v_pool[src].clone(), p.k_scale[src].clone())
+    pairs = case.layout.cow_pairs
+    src = torch.from_numpy(pairs[:, 0].astype(np.int64)).to(gpu)
+    dst = torch.from_numpy(pairs[:, 1].astype(np.int64)).to(gpu)
+    before = [t[src].clone() for t in (p.k_pool, p.v_pool, p.k_scale, p.v_scale)]
     case.cow(0)
     case.append(0)
     torch.cuda.synchronize()
-    assert torch.equal(p.k_pool[src], before[0])
-    assert torch.equal(p.v_pool[src], before[1])
-    assert torch.equal(p.k_scale[src], before[2])
+    BS = spec.BS
+    for i in range(pairs.shape[0]):
+        b = 2 * i                                   # the writer of pair i
+        fill = (int(case.lens[b]) - 1) % BS         # slots filled before the append
+        assert fill > 0
+        after_src = [t[src[i]] for t in (p.k_pool, p.v_pool, p.k_scale, p.v_scale)]
+        after_dst = [t[dst[i]] for t in (p.k_pool, p.v_pool, p.k_scale, p.v_scale)]
+        for j, (bef, a_s, a_d) in enumerate(zip(before, after_src, after_dst)):
+            if j == 1:   # V is dim-major: slots on the last axis
+                assert torch.equal(a_s[..., :fill], bef[i][..., :fill])
+                assert torch.equal(a_d[..., :fill], bef[i][..., :fill])
+            else:
+                assert torch.equal(a_s[:, :fill], bef[i][:, :fill])
+                assert torch.equal(a_d[:, :fill], bef[i][:, :fill])
+    # the writers' tables point at the copies, the partners' at the originals
+    bt = case.layout.block_tables
+    for i in range(pairs.shape[0]):
+        last = (int(case.lens[2 * i]) - 1) // BS
+        assert bt[2 * i, last] == pairs[i, 1] and bt[2 * i + 1, last] == pairs[i, 0]
 
 
 def test_constant_keys_give_mean_of_values(gpu):
