@@ -169,9 +169,9 @@ kvq_status dispatch_write_d(const WriteParams &p, int D, int G, hipStream_t s)
 template <int FMT, int D, int BS, int NG>
 void launch_decode(const DecodeParams &p, int B, int Hkv, int splits, hipStream_t s)
 {
-    hipLaunchKernelGGL((paged_decode_kernel<FMT, D, BS, NG>),
-                       dim3((unsigned)splits, (unsigned)Hkv, (unsigned)B), dim3(64), 0, s,
-                       p);
+    const int64_t items = (int64_t)splits * Hkv * B;
+    hipLaunchKernelGGL((paged_decode_kernel<FMT, D, BS, NG>), dim3((unsigned)items),
+                       dim3(64), 0, s, p);
     if (splits > 1)
         hipLaunchKernelGGL((merge_splits_kernel<D>), dim3((unsigned)p.Hq, (unsigned)B),
                            dim3(64), 0, s, p);
@@ -309,7 +309,7 @@ kvq_status kvq_paged_decode(const void *q, const void *k_pool, const void *v_poo
     const int32_t r = num_q_heads / num_kv_heads;
     if (r > 16)
         return KVQ_ERR_UNSUPPORTED;
-    if (num_seqs > 65535)
+    if (num_seqs > 65535 || (int64_t)num_seqs * num_kv_heads > (1 << 24))
         return KVQ_ERR_UNSUPPORTED;
     if (num_seqs == 0)
         return KVQ_OK;
@@ -349,6 +349,7 @@ kvq_status kvq_paged_decode(const void *q, const void *k_pool, const void *v_poo
     uint8_t *ws = static_cast<uint8_t *>(workspace);
     p.ws_ml = w.total ? reinterpret_cast<float *>(ws + w.ml_off) : nullptr;
     p.ws_acc = w.total ? reinterpret_cast<float *>(ws + w.acc_off) : nullptr;
+    p.B = num_seqs;
     p.max_blocks = max_blocks_per_seq;
     p.max_ctx = max_context_len;
     p.num_blocks = num_blocks;

@@ -50,6 +50,7 @@ struct DecodeParams {
     f16 *out;
     float *ws_acc;    // [B][Hq][max_splits][D]
     float *ws_ml;     // [B][Hq][max_splits][2]
+    int32_t B;
     int32_t max_blocks;
     int32_t max_ctx;     // host bound on context_lens (<= max_blocks * BS)
     int32_t num_blocks;
@@ -126,9 +127,15 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
     constexpr int G = D / NG;    // INT8 group size
     static_assert(FMT != FMT_INT8 || G >= 64, "groups must cover a 64-dim chunk");
 
-    const int split = blockIdx.x;
-    const int h = blockIdx.y;
-    const int b = blockIdx.z;
+    // Work-item order: split index slowest, then sequence, then KV head.
+    // Consecutive workgroups are dealt round-robin to the 8 XCDs, so every
+    // XCD receives an equal share of each split index (the first split of
+    // every sequence exists; later ones only for long sequences).
+    const int units = p.B * p.Hkv;
+    const int split = blockIdx.x / units;
+    const int unit = blockIdx.x - split * units;
+    const int b = unit / p.Hkv;
+    const int h = unit - b * p.Hkv;
     const int lane = threadIdx.x;
     const int col = lane & 15;
     const int grp = lane >> 4;
