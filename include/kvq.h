@@ -32,9 +32,17 @@
  *  - Pointers to q, out, pools, scales and workspace must be 16-byte aligned.
  *
  * Pool layout (one layer; the caller keeps one set of pools per layer):
- *   k_pool  [num_blocks][Hkv][block_size][head_dim]   token-major
- *   v_pool  [num_blocks][Hkv][head_dim][block_size]   dim-major
- *   element type: INT8 = int8 codes, FP8 = E4M3 bytes, FP16 = IEEE half.
+ *   k_pool, v_pool  [num_blocks][Hkv][tile], one tile of block_size * head_dim
+ *   elements (EB bytes each: INT8 = int8 codes and FP8 = E4M3 bytes, EB = 1;
+ *   FP16 = IEEE half, EB = 2) per (block, KV head).  Inside a tile, element
+ *   (token t, dim d) sits at byte
+ *     K:  ((d*EB/64) * block_size + t) * 64 + (d*EB) % 64
+ *         (rows of 64 bytes: 64 one-byte dims or 32 fp16 dims of one token)
+ *     V:  ((e * (head_dim/4) + d/4) * (block_size/4) + t/4) * 16
+ *           + ((d%4) % (4/EB)) * 4 * EB + (t%4) * EB,   e = (d%4) / (4/EB)
+ *         (16-byte micro-tiles of 4 tokens x 4/EB dims).
+ *   These orders let every 16-byte load of the decode kernel cover, across a
+ *   wavefront, one contiguous KiB of whole cache lines.
  *   INT8 scales: k_scale, v_scale [num_blocks][Hkv][block_size][head_dim/G]
  *   fp32, one per (token slot, group of G consecutive head_dim elements).
  *   FP8 scales:  k_scale, v_scale [Hkv] fp32, static, read only.

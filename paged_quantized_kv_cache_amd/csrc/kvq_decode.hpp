@@ -12,17 +12,18 @@
 // of a 32-token block), gathering each tile through the block table.
 //
 // Both contractions run on 16x16x16 fp16 MFMA with the head_dim / token axes
-// laid out so that no data moves between lanes except for softmax maxima:
+// laid out so that no data moves between lanes except for softmax maxima.
+// Lane (col, grp) = (lane % 16, lane / 16):
 //   S^T[token][head] = K_tile (16 x D) * Q^T (D x 16)
-//       A operand: lane (col, grp) holds token `col`, 4 head_dim values per
-//       k-step; B operand: q of query head `col` (zero for col >= r).
-//       Output: lane (col, grp) holds the scores of query head `col` for the
-//       tile's tokens 4*grp .. 4*grp+3.
-//   O^T[d][head] += V_tile^T (16 d x 16 tokens) * P^T (16 tokens x 16 heads)
-//       B operand = P^T, which is exactly the softmaxed S^T output already in
-//       the lane; A operand: lane holds d-row `col` of a 16-dim tile for the
-//       tokens 4*grp .. 4*grp+3 -- 4 consecutive bytes of the dim-major V
-//       block.
+//       A operand: token `col`, 4 head dims per k-step; B operand: q of query
+//       head `col` (zero for col >= r), same dims.  Output: the scores of
+//       query head `col` for the tile's tokens 4*grp .. 4*grp+3.
+//   O^T[d][head] += V_tile^T (16 dims x 16 tokens) * P^T (16 tokens x 16 heads)
+//       B operand = P^T, exactly the softmaxed S^T output already in the
+//       lane; A operand: 4 consecutive tokens of one dim, which the V
+//       micro-tile layout stores next to each other.
+// The head_dim order inside an MFMA k-step is a permutation chosen so that
+// each lane's K bytes are contiguous; q is loaded with the same permutation.
 // Codes are converted to exact fp16 (INT8 c, or E4M3 value * 2^-8) right
 // before the MFMA; K group scales multiply the per-group partial dot products
 // (one accumulator per group); V group scales are folded into P (rounded to
@@ -62,13 +63,13 @@ struct DecodeParams {
     float score_scale;  // softmax_scale * log2(e)
 };
 
+// Per-lane registers of one 16-token tile.
 template <int FMT, int D>
 struct TileData {
     static constexpr int EB = FMT == FMT_FP16 ? 2 : 1;
-    static constexpr int KV4 = D * EB / 64;   // 16-byte K loads per lane
-    static constexpr int DT = D / 16;         // 16-dim tiles
-    uint32_t k[4 * KV4];                      // head_dim slice of token `col`
-    uint32_t v[DT * EB];                      // 4 tokens of one d-row
+    static constexpr int NL = D * EB / 64;  // 16-byte K loads (= V loads) per lane
+    uint32_t k[4 * NL];
+    uint32_t v[4 * NL];
     f32x4 sk[2];
     f32x4 sv[2];
 };
@@ -78,35 +79,29 @@ __device__ __forceinline__ void load_tile(const DecodeParams &p, TileData<FMT, D
                                           int phys, int h, int toff, int col, int grp)
 {
     constexpr int EB = TileData<FMT, D>::EB;
-    constexpr int DT = D / 16;
+    constexpr int NL = TileData<FMT, D>::NL;
     const int64_t tile = (int64_t)phys * p.Hkv + h;
-    // K: token-major rows; lane reads row `col`, dims [64c + 16 grp, +16)
-    const uint8_t *krow = p.k_pool + ((tile * BS + toff + col) * D) * EB;
+    const uint8_t *kb = p.k_pool + tile * (BS * D * EB);
+    const uint8_t *vb = p.v_pool + tile * (BS * D * EB);
 #pragma unroll
-    for (int c = 0; c < D / 64; ++c) {
-        const uint8_t *src = krow + (64 * c + 16 * grp) * EB;
-#pragma unroll
-        for (int e = 0; e < EB; ++e) {
-            const uint4 w = *reinterpret_cast<const uint4 *>(src + 16 * e);
-            const int i = 4 * (c * EB + e);
-            t.k[i + 0] = w.x;
-            t.k[i + 1] = w.y;
-            t.k[i + 2] = w.z;
-            t.k[i + 3] = w.w;
-        }
+    for (int x = 0; x < NL; ++x) {
+        // K chunk x of token toff + col: bytes [16 grp, 16 grp + 16) of its row
+        const uint4 w = *reinterpret_cast<const uint4 *>(kb + (x * BS + toff + col) * 64 + 16 * grp);
+        t.k[4 * x + 0] = w.x;
+        t.k[4 * x + 1] = w.y;
+        t.k[4 * x + 2] = w.z;
+        t.k[4 * x + 3] = w.w;
     }
-    // V: dim-major; lane reads d-row 16*tau + col, tokens toff + 4 grp .. +3
-    const uint8_t *vblk = p.v_pool + (tile * D * BS) * EB;
 #pragma unroll
-    for (int tau = 0; tau < DT; ++tau) {
-        const uint8_t *src = vblk + ((int64_t)(16 * tau + col) * BS + toff + 4 * grp) * EB;
-        if constexpr (EB == 1) {
-            t.v[tau] = *reinterpret_cast<const uint32_t *>(src);
-        } else {
-            const uint2 w = *reinterpret_cast<const uint2 *>(src);
-            t.v[2 * tau] = w.x;
-            t.v[2 * tau + 1] = w.y;
-        }
+    for (int x = 0; x < NL; ++x) {
+        // V micro-tile: part e, dim quad col + 16 * g4, token quad toff/4 + grp
+        const int e = x % EB, g4 = x / EB;
+        const uint4 w = *reinterpret_cast<const uint4 *>(
+            vb + (((e * (D / 4) + col + 16 * g4) * (BS / 4)) + toff / 4 + grp) * 16);
+        t.v[4 * x + 0] = w.x;
+        t.v[4 * x + 1] = w.y;
+        t.v[4 * x + 2] = w.z;
+        t.v[4 * x + 3] = w.w;
     }
     if constexpr (FMT == FMT_INT8) {
         const int64_t s0 = (tile * BS + toff + 4 * grp) * NG;
@@ -152,18 +147,30 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
     const bool head_ok = col < p.r;
     const int qhead = h * p.r + col;
 
-    // ---- query operand: q[qhead][64c + 16 grp + 4j + v] for k-step 4c + j
+    // ---- query operand, in the k-step dim order of the K loads:
+    //   1-byte codes: k-step s, lane group grp, element v -> dim
+    //       64 (s/4) + 16 grp + 4 (s%4) + v
+    //   fp16:   32 (s/2) + 8 grp + 4 (s%2) + v
     f16x4 qop[KS];
     {
         const f16 *qrow = p.q + ((int64_t)b * p.Hq + (head_ok ? qhead : h * p.r)) * D;
+        if constexpr (EB == 1) {
 #pragma unroll
-        for (int c = 0; c < D / 64; ++c) {
-            const uint4 w0 = *reinterpret_cast<const uint4 *>(qrow + 64 * c + 16 * grp);
-            const uint4 w1 = *reinterpret_cast<const uint4 *>(qrow + 64 * c + 16 * grp + 8);
-            qop[4 * c + 0] = f16x4_from_u2(w0.x, w0.y);
-            qop[4 * c + 1] = f16x4_from_u2(w0.z, w0.w);
-            qop[4 * c + 2] = f16x4_from_u2(w1.x, w1.y);
-            qop[4 * c + 3] = f16x4_from_u2(w1.z, w1.w);
+            for (int c = 0; c < D / 64; ++c) {
+                const uint4 w0 = *reinterpret_cast<const uint4 *>(qrow + 64 * c + 16 * grp);
+                const uint4 w1 = *reinterpret_cast<const uint4 *>(qrow + 64 * c + 16 * grp + 8);
+                qop[4 * c + 0] = f16x4_from_u2(w0.x, w0.y);
+                qop[4 * c + 1] = f16x4_from_u2(w0.z, w0.w);
+                qop[4 * c + 2] = f16x4_from_u2(w1.x, w1.y);
+                qop[4 * c + 3] = f16x4_from_u2(w1.z, w1.w);
+            }
+        } else {
+#pragma unroll
+            for (int c = 0; c < D / 32; ++c) {
+                const uint4 w = *reinterpret_cast<const uint4 *>(qrow + 32 * c + 8 * grp);
+                qop[2 * c + 0] = f16x4_from_u2(w.x, w.y);
+                qop[2 * c + 1] = f16x4_from_u2(w.z, w.w);
+            }
         }
         if (!head_ok) {
 #pragma unroll
@@ -190,6 +197,7 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
     };
     auto tile_off = [&](int it) -> int { return (t_begin + 16 * it) % BS; };
 
+    // o[tau][v]: output dim 64 (tau / 4) + 16 grp + 4 v + tau % 4, head col
     f32x4 o[DT];
 #pragma unroll
     for (int i = 0; i < DT; ++i)
@@ -206,16 +214,15 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
             sacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
-            const int c = s >> 2, j = s & 3;
             f16x4 a;
             if constexpr (FMT == FMT_INT8) {
-                a = int8x4_to_f16x4(cur.k[4 * c + j]);
+                a = int8x4_to_f16x4(cur.k[s]);
             } else if constexpr (FMT == FMT_FP8) {
-                a = fp8x4_to_f16x4_scaled(cur.k[4 * c + j]);
+                a = fp8x4_to_f16x4_scaled(cur.k[s]);
             } else {
-                a = f16x4_from_u2(cur.k[8 * c + 2 * j], cur.k[8 * c + 2 * j + 1]);
+                a = f16x4_from_u2(cur.k[2 * s], cur.k[2 * s + 1]);
             }
-            const int gi = (FMT == FMT_INT8 && NG == 2) ? c : 0;
+            const int gi = (FMT == FMT_INT8 && NG == 2) ? (s >> 2) : 0;
             sacc[gi] = __builtin_amdgcn_mfma_f32_16x16x16f16(a, qop[s], sacc[gi], 0, 0, 0);
         }
 
@@ -272,17 +279,20 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
                 pop[0][v] = (f16)pr[v];
         }
 
-        // ---- O^T += V^T P^T
+        // ---- O^T += V^T P^T; d-tile tau covers dims 64 (tau/4) + 4 m + tau%4
         const bool partial = ts + 16 > t_end;
 #pragma unroll
         for (int tau = 0; tau < DT; ++tau) {
+            const int g4 = tau >> 2, i = tau & 3;
             f16x4 a;
             if constexpr (FMT == FMT_INT8) {
-                a = int8x4_to_f16x4(cur.v[tau]);
+                a = int8x4_to_f16x4(cur.v[4 * g4 + i]);
             } else if constexpr (FMT == FMT_FP8) {
-                a = fp8x4_to_f16x4_scaled(cur.v[tau]);
+                a = fp8x4_to_f16x4_scaled(cur.v[4 * g4 + i]);
             } else {
-                a = f16x4_from_u2(cur.v[2 * tau], cur.v[2 * tau + 1]);
+                // fp16 micro-tiles hold 2 dims x 4 tokens: part i/2 of quad g4
+                const int x = 2 * g4 + (i >> 1), w = 2 * (i & 1);
+                a = f16x4_from_u2(cur.v[4 * x + w], cur.v[4 * x + w + 1]);
                 if (partial) {  // stale fp16 slots may hold non-finite values
 #pragma unroll
                     for (int v = 0; v < 4; ++v)
@@ -290,10 +300,9 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
                             a[v] = (f16)0.0f;
                 }
             }
-            const int gi = (FMT == FMT_INT8 && NG == 2) ? (16 * tau) / G : 0;
+            const int gi = (FMT == FMT_INT8 && NG == 2) ? (64 * g4) / G : 0;
             o[tau] = __builtin_amdgcn_mfma_f32_16x16x16f16(a, pop[gi], o[tau], 0, 0, 0);
         }
-
     };
 
     // Ping-pong over two tile buffers: the loads of tile i+1 are in flight
@@ -311,33 +320,39 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
             process(buf1, t_begin + 16 * (it + 1));
     }
 
-    // ---- epilogue
+    // ---- epilogue: lane holds dims 64 g4 + 16 grp + (0..15) of head col
     float lt = l + __shfl_xor(l, 16);
     lt += __shfl_xor(lt, 32);
-
+    if (!head_ok)
+        return;
     if (nsplit == 1) {
-        if (head_ok) {
-            const float inv = out_scale / lt;
-            f16 *orow = p.out + ((int64_t)b * p.Hq + qhead) * D + 4 * grp;
+        const float inv = out_scale / lt;
+        f16 *orow = p.out + ((int64_t)b * p.Hq + qhead) * D + 16 * grp;
 #pragma unroll
-            for (int tau = 0; tau < DT; ++tau) {
-                const f16x4 hv = {(f16)(o[tau][0] * inv), (f16)(o[tau][1] * inv),
-                                  (f16)(o[tau][2] * inv), (f16)(o[tau][3] * inv)};
-                *reinterpret_cast<f16x4 *>(orow + 16 * tau) = hv;
-            }
+        for (int g4 = 0; g4 < D / 64; ++g4) {
+            f16x4 hv[4];
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+                hv[v] = f16x4{(f16)(o[4 * g4 + 0][v] * inv), (f16)(o[4 * g4 + 1][v] * inv),
+                              (f16)(o[4 * g4 + 2][v] * inv), (f16)(o[4 * g4 + 3][v] * inv)};
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+                *reinterpret_cast<f16x4 *>(orow + 64 * g4 + 4 * v) = hv[v];
         }
         return;
     }
-
-    if (head_ok) {
-        const int64_t idx = ((int64_t)b * p.Hq + qhead) * p.max_splits + split;
-        float *wacc = p.ws_acc + idx * D + 4 * grp;
+    const int64_t idx = ((int64_t)b * p.Hq + qhead) * p.max_splits + split;
+    float *wacc = p.ws_acc + idx * D + 16 * grp;
 #pragma unroll
-        for (int tau = 0; tau < DT; ++tau)
-            *reinterpret_cast<f32x4 *>(wacc + 16 * tau) = o[tau] * out_scale;
-        if (grp == 0)
-            *reinterpret_cast<float2 *>(p.ws_ml + 2 * idx) = make_float2(m, lt);
-    }
+    for (int g4 = 0; g4 < D / 64; ++g4)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const f32x4 w = {o[4 * g4 + 0][v] * out_scale, o[4 * g4 + 1][v] * out_scale,
+                             o[4 * g4 + 2][v] * out_scale, o[4 * g4 + 3][v] * out_scale};
+            *reinterpret_cast<f32x4 *>(wacc + 64 * g4 + 4 * v) = w;
+        }
+    if (grp == 0)
+        *reinterpret_cast<float2 *>(p.ws_ml + 2 * idx) = make_float2(m, lt);
 }
 
 // Log-sum-exp merge of the split partials of one (sequence, query head):

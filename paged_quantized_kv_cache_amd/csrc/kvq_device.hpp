@@ -89,6 +89,28 @@ __device__ __forceinline__ uint32_t e4m3_rne_sat(float y)
     return sign | (r - (120u << 3));  // exponent bias 127 -> 7
 }
 
+// ---------------------------------------------------------------- layouts
+// Byte offset of element (token t, dim d) inside one (block, KV head) tile,
+// EB bytes per element.  Both layouts are arranged so that every 16-byte
+// load the decode kernel issues for a 16-token tile lands, across the 64
+// lanes, on one contiguous 1 KiB run (whole 128-byte lines).
+//
+// K: rows of 64 bytes -- [D*EB/64 chunks][BS tokens][64 bytes]; a chunk is
+//    64 int8/E4M3 dims or 32 fp16 dims of one token.
+template <int D, int EB>
+__host__ __device__ constexpr int k_offset(int BS, int t, int d)
+{
+    return ((d * EB / 64) * BS + t) * 64 + (d * EB) % 64;
+}
+// V: 16-byte micro-tiles of 4 tokens x (4 / EB) dims --
+//    [EB][D/4][BS/4][4/EB dims][4 tokens][EB bytes]; e = (d % 4) / (4 / EB).
+template <int D, int EB>
+__host__ __device__ constexpr int v_offset(int BS, int t, int d)
+{
+    return (((((d % 4) / (4 / EB)) * (D / 4) + d / 4) * (BS / 4) + t / 4) * 16 +
+            ((d % 4) % (4 / EB)) * 4 * EB + (t % 4) * EB);
+}
+
 __device__ __forceinline__ float wave_max(float x)
 {
 #pragma unroll

@@ -8,9 +8,9 @@
 // each lane D/32 consecutive elements of the head.  A group of G elements is
 // spread over G/(D/32) neighbouring lanes; its absmax is reduced across them
 // with xor shuffles, so the scale and the codes come out in one pass.  K codes
-// are stored token-major (one dword per lane), V codes dim-major (the layout
-// the decode kernel's PV operand reads), scales next to the K/V codes of
-// their slot.
+// go to 64-byte token rows (one dword per lane), V codes to 4x4 micro-tiles
+// (the layouts the decode kernel reads, see k_offset / v_offset), scales to
+// the slot's entry of the scale arrays.
 #pragma once
 
 #include "kvq_device.hpp"
@@ -103,35 +103,31 @@ __global__ __launch_bounds__(64 * kWriteWaves) void cache_write_kernel(WritePara
             code[i] = e4m3_rne_sat(x[i] / S);
     }
 
-    if constexpr (FMT == FMT_FP16) {
-        // K: [blk][h][off][d]; V: [blk][h][d][off] (2-byte elements)
-        f16 *kp = reinterpret_cast<f16 *>(p.k_pool);
-        f16 *vp = reinterpret_cast<f16 *>(p.v_pool);
-        if (!is_v) {
-            f16 *dst = kp + (head_base * BS + off) * D + e0;
-#pragma unroll
-            for (int i = 0; i < EPL; ++i)
-                dst[i] = src[i];
+    // Tile layouts: see k_offset / v_offset (kvq_device.hpp).
+    constexpr int EB = FMT == FMT_FP16 ? 2 : 1;
+    uint8_t *tile = (is_v ? p.v_pool : p.k_pool) + head_base * ((int64_t)BS * D * EB);
+    if (!is_v) {
+        // EPL consecutive dims of one token are contiguous in a K row
+        uint8_t *dst = tile + k_offset<D, EB>(BS, off, e0);
+        if constexpr (FMT == FMT_FP16) {
+            if constexpr (EPL == 4)
+                *reinterpret_cast<uint2 *>(dst) = *reinterpret_cast<const uint2 *>(src);
+            else
+                *reinterpret_cast<uint32_t *>(dst) = *reinterpret_cast<const uint32_t *>(src);
+        } else if constexpr (EPL == 4) {
+            *reinterpret_cast<uint32_t *>(dst) =
+                code[0] | (code[1] << 8) | (code[2] << 16) | (code[3] << 24);
         } else {
-            f16 *dst = vp + (head_base * D + e0) * BS + off;
-#pragma unroll
-            for (int i = 0; i < EPL; ++i)
-                dst[(int64_t)i * BS] = src[i];
+            *reinterpret_cast<uint16_t *>(dst) = (uint16_t)(code[0] | (code[1] << 8));
         }
     } else {
-        if (!is_v) {
-            uint8_t *dst = p.k_pool + (head_base * BS + off) * D + e0;
-            if constexpr (EPL == 4) {
-                *reinterpret_cast<uint32_t *>(dst) =
-                    code[0] | (code[1] << 8) | (code[2] << 16) | (code[3] << 24);
-            } else {
-                *reinterpret_cast<uint16_t *>(dst) = (uint16_t)(code[0] | (code[1] << 8));
-            }
-        } else {
-            uint8_t *dst = p.v_pool + (head_base * D + e0) * BS + off;
 #pragma unroll
-            for (int i = 0; i < EPL; ++i)
-                dst[(int64_t)i * BS] = (uint8_t)code[i];
+        for (int i = 0; i < EPL; ++i) {
+            uint8_t *dst = tile + v_offset<D, EB>(BS, off, e0 + i);
+            if constexpr (FMT == FMT_FP16)
+                *reinterpret_cast<f16 *>(dst) = src[i];
+            else
+                *dst = (uint8_t)code[i];
         }
     }
 }

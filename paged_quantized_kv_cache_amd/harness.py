@@ -156,8 +156,13 @@ class DecodeCase:
     def gather_codes(self, layer: int, seqs=None):
         """Read the pools back through the block tables: per sequence,
         contiguous ``[ctx][Hkv][D]`` codes and ``[ctx][Hkv][D/G]`` scales
-        (host numpy), in logical token order."""
+        (host numpy), in logical token order.  Tile element orders follow the
+        layout documented in include/kvq.h."""
         p, s = self.pools[layer], self.spec
+        eb = 2 if p.fmt == "fp16" else 1
+        koff, voff = tile_offsets(s.BS, s.D, eb)
+        kflat = p.k_pool.view(torch.uint8).reshape(p.k_pool.shape[0], s.Hkv, -1)
+        vflat = p.v_pool.view(torch.uint8).reshape(p.v_pool.shape[0], s.Hkv, -1)
         bt = self.layout.block_tables
         out = []
         for b in (range(s.B) if seqs is None else seqs):
@@ -165,10 +170,33 @@ class DecodeCase:
             t = np.arange(n)
             blk = torch.from_numpy(bt[b, t // s.BS].astype(np.int64)).to(self.device)
             off = torch.from_numpy((t % s.BS).astype(np.int64)).to(self.device)
-            item = {"k": p.k_pool[blk, :, off, :].cpu().numpy(),      # [n][Hkv][D]
-                    "v": p.v_pool[blk, :, :, off].cpu().numpy()}      # [n][Hkv][D]
+            item = {}
+            for name, flat, offs in (("k", kflat, koff), ("v", vflat, voff)):
+                o = torch.from_numpy(offs).to(self.device)[off]       # [n][D][eb]
+                rows = flat[blk]                                        # [n][Hkv][bytes]
+                g = torch.gather(rows, 2, o.reshape(n, 1, -1).expand(n, s.Hkv, -1))
+                g = g.reshape(n, s.Hkv, s.D, eb).contiguous().cpu().numpy()
+                if eb == 2:
+                    g = g.view(np.float16).reshape(n, s.Hkv, s.D)
+                else:
+                    g = g.reshape(n, s.Hkv, s.D).view(
+                        np.int8 if p.fmt == "int8" else np.uint8)
+                item[name] = g
             if p.fmt == "int8":
                 item["k_scale"] = p.k_scale[blk, :, off, :].cpu().numpy()
                 item["v_scale"] = p.v_scale[blk, :, off, :].cpu().numpy()
             out.append(item)
         return out
+
+
+def tile_offsets(BS: int, D: int, eb: int):
+    """Byte offsets ``[BS][D][eb]`` of every element of a K and a V tile."""
+    t = np.arange(BS)[:, None]
+    d = np.arange(D)[None, :]
+    k = ((d * eb) // 64 * BS + t) * 64 + (d * eb) % 64
+    per = 4 // eb                                   # dims per V micro-tile
+    e = (d % 4) // per
+    v = (((e * (D // 4) + d // 4) * (BS // 4) + t // 4) * 16
+         + ((d % 4) % per) * 4 * eb + (t % 4) * eb)
+    byte = np.arange(eb)[None, None, :]
+    return ((k[..., None] + byte).astype(np.int64), (v[..., None] + byte).astype(np.int64))

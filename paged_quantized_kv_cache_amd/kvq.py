@@ -5,11 +5,11 @@ current HIP stream are passed through, status codes become exceptions.  Every
 step of the computation runs in the library's HIP kernels; there is no CPU or
 PyTorch fallback -- if ``libkvq.so`` is missing, every call raises.
 
-Pool layout (per layer):
-  k_pool [num_blocks][Hkv][block_size][head_dim], v_pool [num_blocks][Hkv]
-  [head_dim][block_size]; element int8 (INT8), uint8 (FP8 E4M3 bytes) or
-  float16 (FP16).  INT8 scales [num_blocks][Hkv][block_size][head_dim/G]
-  fp32; FP8 scales [Hkv] fp32.
+Pool tensors (per layer) have shape [num_blocks][Hkv][block_size][head_dim]
+with element int8 (INT8), uint8 (FP8 E4M3 bytes) or float16 (FP16); the
+element order inside each (block, head) tile is the library's K / V tile
+layout (include/kvq.h), not row-major.  INT8 scales
+[num_blocks][Hkv][block_size][head_dim/G] fp32; FP8 scales [Hkv] fp32.
 """
 from __future__ import annotations
 
@@ -113,7 +113,7 @@ def alloc_pools(num_blocks: int, num_kv_heads: int, block_size: int,
     FP16 has no scales (None)."""
     dt = POOL_DTYPES[fmt]
     kp = torch.empty((num_blocks, num_kv_heads, block_size, head_dim), dtype=dt, device=device)
-    vp = torch.empty((num_blocks, num_kv_heads, head_dim, block_size), dtype=dt, device=device)
+    vp = torch.empty((num_blocks, num_kv_heads, block_size, head_dim), dtype=dt, device=device)
     if fmt == "int8":
         ng = head_dim // group_size
         ks = torch.empty((num_blocks, num_kv_heads, block_size, ng), dtype=torch.float32, device=device)

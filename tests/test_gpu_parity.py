@@ -16,7 +16,7 @@ import torch
 import oracle
 from oracle import expected as E
 from paged_quantized_kv_cache_amd import workloads as W
-from paged_quantized_kv_cache_amd.harness import DecodeCase
+from paged_quantized_kv_cache_amd.harness import DecodeCase, tile_offsets
 
 pytestmark = pytest.mark.gpu
 
@@ -202,30 +202,30 @@ def test_cow_leaves_other_sharer_untouched(gpu):
     case.prefill(0)
     p = case.pools[0]
     pairs = case.layout.cow_pairs
-    src = torch.from_numpy(pairs[:, 0].astype(np.int64)).to(gpu)
-    dst = torch.from_numpy(pairs[:, 1].astype(np.int64)).to(gpu)
-    before = [t[src].clone() for t in (p.k_pool, p.v_pool, p.k_scale, p.v_scale)]
+    koff, voff = tile_offsets(spec.BS, spec.D, 1)
+
+    def slots(pool, blk, offs, fill):
+        flat = pool[int(blk)].view(torch.uint8).reshape(spec.Hkv, -1).cpu().numpy()
+        return flat[:, offs[:fill].ravel()]
+
+    fills = [(int(case.lens[2 * i]) - 1) % spec.BS for i in range(pairs.shape[0])]
+    before = [(slots(p.k_pool, s_, koff, f), slots(p.v_pool, s_, voff, f),
+               p.k_scale[int(s_), :, :f].clone(), p.v_scale[int(s_), :, :f].clone())
+              for (s_, _), f in zip(pairs, fills)]
     case.cow(0)
     case.append(0)
     torch.cuda.synchronize()
-    BS = spec.BS
-    for i in range(pairs.shape[0]):
-        b = 2 * i                                   # the writer of pair i
-        fill = (int(case.lens[b]) - 1) % BS         # slots filled before the append
-        assert fill > 0
-        after_src = [t[src[i]] for t in (p.k_pool, p.v_pool, p.k_scale, p.v_scale)]
-        after_dst = [t[dst[i]] for t in (p.k_pool, p.v_pool, p.k_scale, p.v_scale)]
-        for j, (bef, a_s, a_d) in enumerate(zip(before, after_src, after_dst)):
-            if j == 1:   # V is dim-major: slots on the last axis
-                assert torch.equal(a_s[..., :fill], bef[i][..., :fill])
-                assert torch.equal(a_d[..., :fill], bef[i][..., :fill])
-            else:
-                assert torch.equal(a_s[:, :fill], bef[i][:, :fill])
-                assert torch.equal(a_d[:, :fill], bef[i][:, :fill])
+    for (src, dst), f, bef in zip(pairs, fills, before):
+        assert f > 0
+        for blk in (src, dst):
+            assert np.array_equal(slots(p.k_pool, blk, koff, f), bef[0])
+            assert np.array_equal(slots(p.v_pool, blk, voff, f), bef[1])
+            assert torch.equal(p.k_scale[int(blk), :, :f], bef[2])
+            assert torch.equal(p.v_scale[int(blk), :, :f], bef[3])
     # the writers' tables point at the copies, the partners' at the originals
     bt = case.layout.block_tables
     for i in range(pairs.shape[0]):
-        last = (int(case.lens[2 * i]) - 1) // BS
+        last = (int(case.lens[2 * i]) - 1) // spec.BS
         assert bt[2 * i, last] == pairs[i, 1] and bt[2 * i + 1, last] == pairs[i, 0]
 
 
