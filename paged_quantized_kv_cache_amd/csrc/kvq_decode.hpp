@@ -83,10 +83,12 @@ __device__ __forceinline__ void load_tile(const DecodeParams &p, TileData<FMT, D
     const int64_t tile = (int64_t)phys * p.Hkv + h;
     const uint8_t *kb = p.k_pool + tile * (BS * D * EB);
     const uint8_t *vb = p.v_pool + tile * (BS * D * EB);
+    // K/V codes are read once per step: nontemporal loads keep them from
+    // displacing reusable lines (block tables, scales, q) in the caches.
 #pragma unroll
     for (int x = 0; x < NL; ++x) {
         // K chunk x of token toff + col: bytes [16 grp, 16 grp + 16) of its row
-        const uint4 w = *reinterpret_cast<const uint4 *>(kb + (x * BS + toff + col) * 64 + 16 * grp);
+        const u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(kb + (x * BS + toff + col) * 64 + 16 * grp));
         t.k[4 * x + 0] = w.x;
         t.k[4 * x + 1] = w.y;
         t.k[4 * x + 2] = w.z;
@@ -96,8 +98,8 @@ __device__ __forceinline__ void load_tile(const DecodeParams &p, TileData<FMT, D
     for (int x = 0; x < NL; ++x) {
         // V micro-tile: part e, dim quad col + 16 * g4, token quad toff/4 + grp
         const int e = x % EB, g4 = x / EB;
-        const uint4 w = *reinterpret_cast<const uint4 *>(
-            vb + (((e * (D / 4) + col + 16 * g4) * (BS / 4)) + toff / 4 + grp) * 16);
+        const u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(
+            vb + (((e * (D / 4) + col + 16 * g4) * (BS / 4)) + toff / 4 + grp) * 16));
         t.v[4 * x + 0] = w.x;
         t.v[4 * x + 1] = w.y;
         t.v[4 * x + 2] = w.z;
