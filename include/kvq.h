@@ -38,9 +38,10 @@
  *   (token t, dim d) sits at byte
  *     K:  ((d*EB/64) * block_size + t) * 64 + (d*EB) % 64
  *         (rows of 64 bytes: 64 one-byte dims or 32 fp16 dims of one token)
- *     V:  ((e * (head_dim/4) + d/4) * (block_size/4) + t/4) * 16
+ *     V:  ((((t/16) * EB + e) * (head_dim/4) + d/4) * 4 + (t%16)/4) * 16
  *           + ((d%4) % (4/EB)) * 4 * EB + (t%4) * EB,   e = (d%4) / (4/EB)
- *         (16-byte micro-tiles of 4 tokens x 4/EB dims).
+ *         (16-byte micro-tiles of 4 tokens x 4/EB dims, grouped per 16-token
+ *         half of a block).
  *   These orders let every 16-byte load of the decode kernel cover, across a
  *   wavefront, one contiguous KiB of whole cache lines.
  *   INT8 scales: k_scale, v_scale [num_blocks][Hkv][block_size][head_dim/G]

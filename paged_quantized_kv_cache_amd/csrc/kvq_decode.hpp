@@ -70,9 +70,19 @@ struct TileData {
     static constexpr int NL = D * EB / 64;  // 16-byte K loads (= V loads) per lane
     uint32_t k[4 * NL];
     uint32_t v[4 * NL];
-    f32x4 sk[2];
-    f32x4 sv[2];
+    // INT8: one scale per lane.  Row grp (lanes 16 grp .. 16 grp + 15) holds
+    // the scales of the tile's tokens 4 grp .. 4 grp + 3: entry e of the row
+    // is K (e < 4 NG) or V, token 4 grp + (e % 4NG) / NG, group e % NG.
+    float sc;
 };
+
+// Broadcast entry `idx` of each 16-lane row to the whole row (ds_swizzle in
+// bit mode: source lane = (lane & 0x10) | idx within each 32-lane half).
+template <int idx>
+__device__ __forceinline__ float row_bcast(float x)
+{
+    return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x10 | (idx << 5)));
+}
 
 template <int FMT, int D, int BS, int NG>
 __device__ __forceinline__ void load_tile(const DecodeParams &p, TileData<FMT, D> &t,
@@ -99,19 +109,17 @@ __device__ __forceinline__ void load_tile(const DecodeParams &p, TileData<FMT, D
         // V micro-tile: part e, dim quad col + 16 * g4, token quad toff/4 + grp
         const int e = x % EB, g4 = x / EB;
         const u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(
-            vb + (((e * (D / 4) + col + 16 * g4) * (BS / 4)) + toff / 4 + grp) * 16));
+            vb + ((((toff / 16) * EB + e) * (D / 4) + col + 16 * g4) * 4 + grp) * 16));
         t.v[4 * x + 0] = w.x;
         t.v[4 * x + 1] = w.y;
         t.v[4 * x + 2] = w.z;
         t.v[4 * x + 3] = w.w;
     }
     if constexpr (FMT == FMT_INT8) {
-        const int64_t s0 = (tile * BS + toff + 4 * grp) * NG;
-#pragma unroll
-        for (int i = 0; i < NG; ++i) {
-            t.sk[i] = *reinterpret_cast<const f32x4 *>(p.k_scale + s0 + 4 * i);
-            t.sv[i] = *reinterpret_cast<const f32x4 *>(p.v_scale + s0 + 4 * i);
-        }
+        const int e = col % (8 * NG);
+        const float *arr = e < 4 * NG ? p.k_scale : p.v_scale;
+        const int w = e % (4 * NG);
+        t.sc = arr[(tile * BS + toff + 4 * grp + w / NG) * NG + w % NG];
     }
 }
 
@@ -209,6 +217,16 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
 
     // One tile of 16 tokens starting at logical token ts, data in `cur`.
     auto process = [&](const TileData<FMT, D> &cur, const int ts) {
+        // ---- this lane's scales: sk[v][j], sv[v][j] of tokens 4 grp + v
+        float sk[4][NG], sv[4][NG];
+        if constexpr (FMT == FMT_INT8) {
+            static_for<0, 4 * NG>([&](auto I) {
+                constexpr int i = decltype(I)::value;
+                sk[i / NG][i % NG] = row_bcast<i>(cur.sc);
+                sv[i / NG][i % NG] = row_bcast<4 * NG + i>(cur.sc);
+            });
+        }
+
         // ---- S^T = K Q^T, one accumulator per INT8 group
         f32x4 sacc[NG];
 #pragma unroll
@@ -235,9 +253,9 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
         for (int v = 0; v < 4; ++v) {
             float acc;
             if constexpr (FMT == FMT_INT8) {
-                acc = sacc[0][v] * cur.sk[(NG * v) >> 2][(NG * v) & 3];
+                acc = sacc[0][v] * sk[v][0];
                 if constexpr (NG == 2)
-                    acc += sacc[1][v] * cur.sk[(2 * v + 1) >> 2][(2 * v + 1) & 3];
+                    acc += sacc[1][v] * sk[v][1];
             } else {
                 acc = sacc[0][v];
             }
@@ -271,8 +289,7 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
             for (int j = 0; j < NG; ++j) {
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
-                    const float sv = cur.sv[(NG * v + j) >> 2][(NG * v + j) & 3];
-                    pop[j][v] = (f16)((tok0 + v < t_end) ? pr[v] * sv : 0.0f);
+                    pop[j][v] = (f16)((tok0 + v < t_end) ? pr[v] * sv[v][j] : 0.0f);
                 }
             }
         } else {

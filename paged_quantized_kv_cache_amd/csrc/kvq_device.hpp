@@ -14,6 +14,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace kvq {
 
 enum { FMT_FP16 = 0, FMT_INT8 = 1, FMT_FP8 = 2 };
@@ -23,6 +25,16 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Compile-time loop: f(std::integral_constant<int, i>) for i in [B, E).
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F &&f)
+{
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>{});
+        static_for<B + 1, E>(f);
+    }
+}
 
 template <typename To, typename From>
 __device__ __forceinline__ To bit_cast(const From &x)
@@ -103,12 +115,13 @@ __host__ __device__ constexpr int k_offset(int BS, int t, int d)
 {
     return ((d * EB / 64) * BS + t) * 64 + (d * EB) % 64;
 }
-// V: 16-byte micro-tiles of 4 tokens x (4 / EB) dims --
-//    [EB][D/4][BS/4][4/EB dims][4 tokens][EB bytes]; e = (d % 4) / (4 / EB).
+// V: 16-byte micro-tiles of 4 tokens x (4 / EB) dims, grouped per 16-token
+//    half of the block -- [BS/16][EB][D/4][4][4/EB dims][4 tokens][EB bytes]
+//    with e = (d % 4) / (4 / EB).
 template <int D, int EB>
 __host__ __device__ constexpr int v_offset(int BS, int t, int d)
 {
-    return (((((d % 4) / (4 / EB)) * (D / 4) + d / 4) * (BS / 4) + t / 4) * 16 +
+    return (((((t / 16) * EB + (d % 4) / (4 / EB)) * (D / 4) + d / 4) * 4 + (t % 16) / 4) * 16 +
             ((d % 4) % (4 / EB)) * 4 * EB + (t % 4) * EB);
 }
 

@@ -196,7 +196,7 @@ def tile_offsets(BS: int, D: int, eb: int):
     k = ((d * eb) // 64 * BS + t) * 64 + (d * eb) % 64
     per = 4 // eb                                   # dims per V micro-tile
     e = (d % 4) // per
-    v = (((e * (D // 4) + d // 4) * (BS // 4) + t // 4) * 16
+    v = (((((t // 16) * eb + e) * (D // 4) + d // 4) * 4 + (t % 16) // 4) * 16
          + ((d % 4) % per) * 4 * eb + (t % 4) * eb)
     byte = np.arange(eb)[None, None, :]
     return ((k[..., None] + byte).astype(np.int64), (v[..., None] + byte).astype(np.int64))
