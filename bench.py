@@ -254,8 +254,7 @@ def main(argv=None) -> int:
             "group_size": spec.G, "cached_tokens": int(case.lens.sum()),
             "mean_context": float(case.lens.mean()),
             "max_context": int(case.lens.max()),
-            "split_tokens": kvq.kvq_decode_split_tokens(spec.B, spec.Hkv, spec.BS,
-                                                        case.max_context_len, 0),
+            "partition": "balanced runs over the GPU's resident wavefronts",
         },
         "roofline": {
             "bound": "hbm",

@@ -132,19 +132,21 @@ KVQ_API kvq_status kvq_cache_write(const void *k, const void *v,
  *                 (used to plan the split) and must not exceed
  *                 max_blocks_per_seq * block_size.
  *   softmax_scale 0 selects 1 / sqrt(head_dim).
- *   split_tokens  0 = automatic; otherwise a multiple of 16 and at most
- *                 64 * block_size (INVALID_ARG otherwise): every sequence
- *                 is cut into spans of split_tokens logical tokens, each
- *                 attended separately and merged exactly (log-sum-exp).
- *                 The split depends only on logical positions, so results do
- *                 not depend on which physical blocks hold the data.
+ *   split_tokens  how the work is cut (the cut depends only on the lengths,
+ *                 never on which physical blocks hold the data):
+ *                 0 = balanced: the batch's 16-token tiles, taken unit by
+ *                 unit ((sequence, KV head) units, sequence-major), are dealt
+ *                 in equal contiguous runs to as many wavefronts as the GPU
+ *                 holds at once; a unit cut by run boundaries is finished by
+ *                 an exact log-sum-exp merge of its pieces.
+ *                 > 0 (a multiple of 16): every unit is cut into spans of
+ *                 split_tokens logical tokens, merged the same way.
  *   out           fp16 [num_seqs][num_q_heads][head_dim] (written).
  *   workspace     device scratch of at least kvq_decode_workspace_size(...)
- *                 bytes (may be NULL when that size is 0); its contents on
- *                 entry do not matter.  It holds the per-split partial results
- *                 (running max, sum and unnormalized output) between the split
- *                 launch and the merge launch of the same call, so calls
- *                 sharing a workspace must be ordered (same stream).
+ *                 bytes (required); its contents on entry do not matter.  It
+ *                 holds the run plan and the partial results of cut units
+ *                 between the launches of one call, so calls sharing a
+ *                 workspace must be ordered (same stream).
  */
 KVQ_API kvq_status kvq_paged_decode(const void *q, const void *k_pool,
                             const void *v_pool, const float *k_scale,
@@ -159,14 +161,9 @@ KVQ_API kvq_status kvq_paged_decode(const void *q, const void *k_pool,
                             int32_t split_tokens, void *out, void *workspace,
                             size_t workspace_bytes, void *stream);
 
-/* Logical tokens per split chosen by kvq_paged_decode for these arguments
- * (split_tokens as passed to it); returns -1 for invalid arguments. */
-KVQ_API int32_t kvq_decode_split_tokens(int32_t num_seqs, int32_t num_kv_heads,
-                                int32_t block_size, int32_t max_context_len,
-                                int32_t split_tokens);
-
-/* Workspace bytes kvq_paged_decode needs for these arguments (0 when no
- * sequence is split).  Returns SIZE_MAX for invalid arguments. */
+/* Workspace bytes kvq_paged_decode needs for these arguments on the
+ * current device (an upper bound over formats and kernel occupancy).
+ * Returns SIZE_MAX for invalid arguments. */
 KVQ_API size_t kvq_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads,
                                  int32_t num_kv_heads, int32_t head_dim,
                                  int32_t block_size, int32_t max_context_len,

@@ -5,6 +5,7 @@
 // printing, no fallback to another format or path.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cmath>
 #include <cstdint>
@@ -22,8 +23,9 @@ using namespace kvq;
 constexpr int kMaxDevices = 64;
 // 0 = unknown, 1 = gfx950, 2 = other device
 std::atomic<int> g_arch_ok[kMaxDevices];
+std::atomic<int> g_cus[kMaxDevices];
 
-kvq_status check_device()
+kvq_status check_device(int *dev_out = nullptr)
 {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0)
@@ -36,9 +38,22 @@ kvq_status check_device()
         if (hipGetDeviceProperties(&prop, dev) != hipSuccess)
             return KVQ_ERR_HIP;
         state = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+        g_cus[dev].store(prop.multiProcessorCount, std::memory_order_relaxed);
         g_arch_ok[dev].store(state, std::memory_order_relaxed);
     }
+    if (dev_out)
+        *dev_out = dev;
     return state == 1 ? KVQ_OK : KVQ_ERR_UNSUPPORTED;
+}
+
+// Compute units of the current device (256 on MI355X if the query fails).
+int device_cus()
+{
+    int dev = 0;
+    if (check_device(&dev) == KVQ_ERR_HIP || dev >= kMaxDevices)
+        return 256;
+    const int c = g_cus[dev].load(std::memory_order_relaxed);
+    return c > 0 ? c : 256;
 }
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -66,71 +81,48 @@ kvq_status launch_status()
     return hipGetLastError() == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
 }
 
-// ---------------------------------------------------------------- split plan
-// Tokens per split.  Splits are spans of logical tokens (multiples of 16), so
-// they never depend on where blocks sit in the pool.  The automatic choice
-// cuts long contexts into spans of at most 1024 tokens (bounded per-item work
-// keeps skewed length mixes balanced across the 256 CUs) and shortens spans
-// when there are too few (sequence, KV head) units to occupy the GPU.
-constexpr int kAutoMaxSpan = 1024;
-constexpr int kAutoMinSpan = 256;
-constexpr int kTargetItems = 2048;
+// ---------------------------------------------------------------- run plan
+// split_tokens == 0: balanced runs, one per wavefront the GPU holds at once
+// (compute units x resident wavefronts per CU for the kernel instance), at
+// most one run per 4 tiles of the largest possible batch.  split_tokens > 0:
+// one run per span; the launch covers the largest possible count.
+constexpr int kMaxWavesPerCU = 32;  // hardware bound used for workspace sizing
 
-// A split covers at most kMaxSplitBlocks blocks (one block id per lane).
-constexpr int kMaxSplitBlocks = 64;
+bool valid_split(int32_t split_tokens)
+{
+    return split_tokens >= 0 && split_tokens % 16 == 0;
+}
 
-int32_t plan_span(int32_t num_seqs, int32_t num_kv_heads, int32_t block_size,
-                  int32_t max_ctx, int32_t split_tokens)
+int64_t max_tiles(int32_t num_seqs, int32_t num_kv_heads, int32_t max_ctx)
+{
+    return (int64_t)num_seqs * num_kv_heads * ((max_ctx + 15) / 16);
+}
+
+int64_t runs_bound(int32_t num_seqs, int32_t num_kv_heads, int32_t max_ctx,
+                   int32_t split_tokens, int64_t balanced_runs)
 {
     if (split_tokens > 0)
-        return split_tokens;
-    const int64_t units = (int64_t)num_seqs * num_kv_heads;
-    int64_t want = (kTargetItems + units - 1) / units;  // splits per unit
-    if (want < 1)
-        want = 1;
-    int64_t span = (max_ctx + want - 1) / want;
-    span = (span + 15) / 16 * 16;
-    if (span > kAutoMaxSpan)
-        span = kAutoMaxSpan;
-    if (span < kAutoMinSpan)
-        span = kAutoMinSpan;
-    if (span >= max_ctx)
-        span = (max_ctx + 15) / 16 * 16;  // one split
-    if (span > (int64_t)kMaxSplitBlocks * block_size)
-        span = (int64_t)kMaxSplitBlocks * block_size;
-    return (int32_t)span;
+        return (int64_t)num_seqs * num_kv_heads * ((max_ctx + split_tokens - 1) / split_tokens);
+    const int64_t t = max_tiles(num_seqs, num_kv_heads, max_ctx);
+    int64_t w = std::min<int64_t>(balanced_runs, (t + 3) / 4);
+    return std::max<int64_t>(w, 1);
 }
 
 struct WsLayout {
-    size_t ml_off, acc_off, total;
-    int32_t span, max_splits;
+    size_t s_off, meta_off, rec_off, ml_off, acc_off, total;
 };
 
-bool valid_split(int32_t block_size, int32_t split_tokens)
+bool workspace_layout(int32_t num_seqs, int32_t r, int32_t head_dim, int64_t runs, WsLayout &w)
 {
-    return split_tokens >= 0 && split_tokens % 16 == 0 &&
-           split_tokens <= kMaxSplitBlocks * block_size;
-}
-
-bool workspace_layout(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
-                      int32_t head_dim, int32_t block_size, int32_t max_ctx,
-                      int32_t split_tokens, WsLayout &w)
-{
-    if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
-        max_ctx < 1 || (block_size != 16 && block_size != 32) ||
-        !valid_split(block_size, split_tokens))
+    if (num_seqs < 0 || r <= 0 || head_dim <= 0 || runs < 0)
         return false;
-    w.span = plan_span(num_seqs, num_kv_heads, block_size, max_ctx, split_tokens);
-    w.max_splits = (max_ctx + w.span - 1) / w.span;
-    if (w.max_splits <= 1 || num_seqs == 0) {
-        w.ml_off = w.acc_off = w.total = 0;
-        return true;
-    }
     auto up256 = [](size_t x) { return (x + 255) / 256 * 256; };
-    const size_t items = (size_t)num_seqs * num_q_heads * w.max_splits;
-    w.ml_off = 0;
-    w.acc_off = w.ml_off + up256(items * 2 * sizeof(float));
-    w.total = w.acc_off + up256(items * head_dim * sizeof(float));
+    w.s_off = 0;
+    w.meta_off = up256((size_t)(num_seqs + 1) * sizeof(int32_t));
+    w.rec_off = w.meta_off + 256;
+    w.ml_off = w.rec_off + up256((size_t)runs * sizeof(PlanRecord));
+    w.acc_off = w.ml_off + up256((size_t)runs * 2 * r * 2 * sizeof(float));
+    w.total = w.acc_off + up256((size_t)runs * 2 * r * head_dim * sizeof(float));
     return true;
 }
 
@@ -166,44 +158,98 @@ kvq_status dispatch_write_d(const WriteParams &p, int D, int G, hipStream_t s)
     return D == 64 ? dispatch_write_g<FMT, 64>(p, G, s) : dispatch_write_g<FMT, 128>(p, G, s);
 }
 
+// Resident 64-lane workgroups per CU for a kernel instance (cached per device).
 template <int FMT, int D, int BS, int NG>
-void launch_decode(const DecodeParams &p, int B, int Hkv, int splits, hipStream_t s)
+int waves_per_cu()
 {
-    const int64_t items = (int64_t)splits * Hkv * B;
-    hipLaunchKernelGGL((paged_decode_kernel<FMT, D, BS, NG>), dim3((unsigned)items),
-                       dim3(64), 0, s, p);
-    if (splits > 1)
-        hipLaunchKernelGGL((merge_splits_kernel<D>), dim3((unsigned)p.Hq, (unsigned)B),
+    static std::atomic<int> cache[kMaxDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return 4;
+    int v = cache[dev].load(std::memory_order_relaxed);
+    if (v == 0) {
+        int n = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                &n, reinterpret_cast<const void *>(&paged_decode_kernel<FMT, D, BS, NG>), 64,
+                0) != hipSuccess || n <= 0)
+            n = 4;
+        v = std::min(n, kMaxWavesPerCU);
+        cache[dev].store(v, std::memory_order_relaxed);
+    }
+    return v;
+}
+
+struct LaunchPlan {
+    int32_t split_tokens;
+    int32_t max_ctx;
+    size_t ws_bytes;
+    uint8_t *ws;
+};
+
+template <int FMT, int D, int BS, int NG>
+kvq_status launch_decode(DecodeParams p, const LaunchPlan &lp, hipStream_t s)
+{
+    const int64_t balanced = (int64_t)device_cus() * waves_per_cu<FMT, D, BS, NG>();
+    const int64_t runs = runs_bound(p.B, p.Hkv, lp.max_ctx, lp.split_tokens, balanced);
+    if (runs > (1 << 30))
+        return KVQ_ERR_UNSUPPORTED;
+    WsLayout w;
+    workspace_layout(p.B, p.r, D, runs, w);
+    if (!lp.ws || lp.ws_bytes < w.total)
+        return KVQ_ERR_WORKSPACE;
+    int32_t *S = reinterpret_cast<int32_t *>(lp.ws + w.s_off);
+    int32_t *meta = reinterpret_cast<int32_t *>(lp.ws + w.meta_off);
+    PlanRecord *rec = reinterpret_cast<PlanRecord *>(lp.ws + w.rec_off);
+    p.plan_S = S;
+    p.plan_meta = meta;
+    p.plan_rec = rec;
+    p.ws_ml = reinterpret_cast<float *>(lp.ws + w.ml_off);
+    p.ws_acc = reinterpret_cast<float *>(lp.ws + w.acc_off);
+    p.W = (int32_t)runs;
+
+    PlanParams pp;
+    pp.context_lens = p.context_lens;
+    pp.S = S;
+    pp.rec = rec;
+    pp.meta = meta;
+    pp.B = p.B;
+    pp.Hkv = p.Hkv;
+    pp.max_ctx = lp.max_ctx;
+    pp.W = (int32_t)runs;
+    pp.span_tiles = lp.split_tokens / 16;
+    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, pp);
+    hipLaunchKernelGGL((paged_decode_kernel<FMT, D, BS, NG>), dim3((unsigned)runs), dim3(64), 0,
+                       s, p);
+    if (runs > 1)
+        hipLaunchKernelGGL((merge_runs_kernel<D>), dim3((unsigned)(runs - 1), (unsigned)p.r),
                            dim3(64), 0, s, p);
+    return launch_status();
 }
 
 template <int FMT, int D, int BS>
-kvq_status dispatch_decode_ng(const DecodeParams &p, int B, int Hkv, int splits, int G,
-                              hipStream_t s)
+kvq_status dispatch_decode_ng(const DecodeParams &p, const LaunchPlan &lp, int G, hipStream_t s)
 {
     if constexpr (FMT == FMT_INT8) {
         const int NG = D / G;
         if (NG == 1)
-            launch_decode<FMT, D, BS, 1>(p, B, Hkv, splits, s);
-        else if constexpr (D == 128)
-            launch_decode<FMT, D, BS, 2>(p, B, Hkv, splits, s);
-        else
-            return KVQ_ERR_UNSUPPORTED;
+            return launch_decode<FMT, D, BS, 1>(p, lp, s);
+        if constexpr (D == 128)
+            return launch_decode<FMT, D, BS, 2>(p, lp, s);
+        return KVQ_ERR_UNSUPPORTED;
     } else {
-        launch_decode<FMT, D, BS, 1>(p, B, Hkv, splits, s);
+        return launch_decode<FMT, D, BS, 1>(p, lp, s);
     }
-    return launch_status();
 }
 
 template <int FMT>
-kvq_status dispatch_decode(const DecodeParams &p, int B, int Hkv, int splits, int D,
-                           int BS, int G, hipStream_t s)
+kvq_status dispatch_decode(const DecodeParams &p, const LaunchPlan &lp, int D, int BS, int G,
+                           hipStream_t s)
 {
     if (D == 64)
-        return BS == 16 ? dispatch_decode_ng<FMT, 64, 16>(p, B, Hkv, splits, G, s)
-                        : dispatch_decode_ng<FMT, 64, 32>(p, B, Hkv, splits, G, s);
-    return BS == 16 ? dispatch_decode_ng<FMT, 128, 16>(p, B, Hkv, splits, G, s)
-                    : dispatch_decode_ng<FMT, 128, 32>(p, B, Hkv, splits, G, s);
+        return BS == 16 ? dispatch_decode_ng<FMT, 64, 16>(p, lp, G, s)
+                        : dispatch_decode_ng<FMT, 64, 32>(p, lp, G, s);
+    return BS == 16 ? dispatch_decode_ng<FMT, 128, 16>(p, lp, G, s)
+                    : dispatch_decode_ng<FMT, 128, 32>(p, lp, G, s);
 }
 
 }  // namespace
@@ -268,22 +314,20 @@ kvq_status kvq_cache_write(const void *k, const void *v, const int64_t *slot_map
     }
 }
 
-int32_t kvq_decode_split_tokens(int32_t num_seqs, int32_t num_kv_heads, int32_t block_size,
-                                int32_t max_context_len, int32_t split_tokens)
-{
-    if (num_seqs < 0 || num_kv_heads <= 0 || max_context_len < 1 ||
-        (block_size != 16 && block_size != 32) || !valid_split(block_size, split_tokens))
-        return -1;
-    return plan_span(num_seqs, num_kv_heads, block_size, max_context_len, split_tokens);
-}
-
 size_t kvq_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                  int32_t head_dim, int32_t block_size,
                                  int32_t max_context_len, int32_t split_tokens)
 {
+    (void)block_size;
+    if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
+        num_q_heads % num_kv_heads != 0 || head_dim <= 0 || max_context_len < 1 ||
+        !valid_split(split_tokens))
+        return SIZE_MAX;
+    const int64_t balanced = (int64_t)device_cus() * kMaxWavesPerCU;
+    const int64_t runs = runs_bound(num_seqs, num_kv_heads, max_context_len, split_tokens,
+                                    balanced);
     WsLayout w;
-    if (!workspace_layout(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
-                          max_context_len, split_tokens, w))
+    if (!workspace_layout(num_seqs, num_q_heads / num_kv_heads, head_dim, runs, w))
         return SIZE_MAX;
     return w.total;
 }
@@ -309,14 +353,14 @@ kvq_status kvq_paged_decode(const void *q, const void *k_pool, const void *v_poo
     const int32_t r = num_q_heads / num_kv_heads;
     if (r > 16)
         return KVQ_ERR_UNSUPPORTED;
-    if (num_seqs > 65535 || (int64_t)num_seqs * num_kv_heads > (1 << 24))
-        return KVQ_ERR_UNSUPPORTED;
     if (num_seqs == 0)
         return KVQ_OK;
     if (max_context_len < 1 || (int64_t)max_blocks_per_seq * block_size < max_context_len)
         return KVQ_ERR_INVALID_ARG;
-    if (!valid_split(block_size, split_tokens))
+    if (!valid_split(split_tokens))
         return KVQ_ERR_INVALID_ARG;
+    if (max_tiles(num_seqs, num_kv_heads, max_context_len) >= (int64_t)1 << 30)
+        return KVQ_ERR_UNSUPPORTED;
     if (!(softmax_scale >= 0.0f) || std::isinf(softmax_scale))
         return KVQ_ERR_INVALID_ARG;
     if (!q || !k_pool || !v_pool || !block_tables || !context_lens || !out)
@@ -324,14 +368,9 @@ kvq_status kvq_paged_decode(const void *q, const void *k_pool, const void *v_poo
     if (dtype != KVQ_FP16 && (!k_scale || !v_scale))
         return KVQ_ERR_INVALID_ARG;
     if (!aligned16(q) || !aligned16(out) || !aligned16(k_pool) || !aligned16(v_pool) ||
-        (dtype == KVQ_INT8 && (!aligned16(k_scale) || !aligned16(v_scale))))
+        (workspace && !aligned16(workspace)))
         return KVQ_ERR_INVALID_ARG;
-
-    WsLayout w;
-    if (!workspace_layout(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
-                          max_context_len, split_tokens, w))
-        return KVQ_ERR_INVALID_ARG;
-    if (w.total > 0 && (!workspace || workspace_bytes < w.total || !aligned16(workspace)))
+    if (!workspace)
         return KVQ_ERR_WORKSPACE;
     st = check_device();
     if (st != KVQ_OK)
@@ -346,9 +385,6 @@ kvq_status kvq_paged_decode(const void *q, const void *k_pool, const void *v_poo
     p.block_tables = block_tables;
     p.context_lens = context_lens;
     p.out = static_cast<f16 *>(out);
-    uint8_t *ws = static_cast<uint8_t *>(workspace);
-    p.ws_ml = w.total ? reinterpret_cast<float *>(ws + w.ml_off) : nullptr;
-    p.ws_acc = w.total ? reinterpret_cast<float *>(ws + w.acc_off) : nullptr;
     p.B = num_seqs;
     p.max_blocks = max_blocks_per_seq;
     p.max_ctx = max_context_len;
@@ -356,21 +392,21 @@ kvq_status kvq_paged_decode(const void *q, const void *k_pool, const void *v_poo
     p.Hq = num_q_heads;
     p.Hkv = num_kv_heads;
     p.r = r;
-    p.span = w.span;
-    p.max_splits = w.max_splits;
     const float sm = softmax_scale > 0.0f ? softmax_scale : 1.0f / std::sqrt((float)head_dim);
     p.score_scale = sm * 1.4426950408889634f;  // log2(e): softmax in base 2
+    LaunchPlan lp;
+    lp.split_tokens = split_tokens;
+    lp.max_ctx = max_context_len;
+    lp.ws_bytes = workspace_bytes;
+    lp.ws = static_cast<uint8_t *>(workspace);
     hipStream_t s = static_cast<hipStream_t>(stream);
     switch (dtype) {
     case KVQ_INT8:
-        return dispatch_decode<FMT_INT8>(p, num_seqs, num_kv_heads, w.max_splits, head_dim,
-                                         block_size, group_size, s);
+        return dispatch_decode<FMT_INT8>(p, lp, head_dim, block_size, group_size, s);
     case KVQ_FP8_E4M3:
-        return dispatch_decode<FMT_FP8>(p, num_seqs, num_kv_heads, w.max_splits, head_dim,
-                                        block_size, group_size, s);
+        return dispatch_decode<FMT_FP8>(p, lp, head_dim, block_size, group_size, s);
     default:
-        return dispatch_decode<FMT_FP16>(p, num_seqs, num_kv_heads, w.max_splits, head_dim,
-                                         block_size, group_size, s);
+        return dispatch_decode<FMT_FP16>(p, lp, head_dim, block_size, group_size, s);
     }
 }
 

@@ -40,6 +40,26 @@
 
 namespace kvq {
 
+// Work partition.  The batch is viewed as one sequence of 16-token tiles:
+// units (sequence b, KV head h) in order b-major, h-minor, each unit holding
+// n_b = ceil(ctx_b / 16) tiles.  A plan kernel scans the lengths and gives
+// every launched wavefront one contiguous run [g0, g1) of this sequence:
+//   balanced:   W runs of equal length (T / W tiles each, T = total tiles),
+//               W = the number of wavefronts the GPU holds at once, so every
+//               wavefront gets the same work whatever the length mix;
+//   fixed span: one run per span of `span` tokens of every unit.
+// A run may cover the end of one unit, whole units, and the start of
+// another.  A unit finished inside one run is written out directly; a unit
+// cut by run boundaries leaves (m, l, acc) partials that the boundary merge
+// kernel combines.  The partition depends only on the lengths, never on
+// where blocks sit in the pool.
+struct PlanRecord {
+    int32_t b;   // sequence holding tile g0
+    int32_t g0;  // first tile of the run
+    int32_t g1;  // one past the last tile
+    int32_t pad;
+};
+
 struct DecodeParams {
     const f16 *q;
     const uint8_t *k_pool;
@@ -49,8 +69,11 @@ struct DecodeParams {
     const int32_t *block_tables;
     const int32_t *context_lens;
     f16 *out;
-    float *ws_acc;    // [B][Hq][max_splits][D]
-    float *ws_ml;     // [B][Hq][max_splits][2]
+    const int32_t *plan_S;       // [B + 1] tiles before each sequence (per KV head)
+    const PlanRecord *plan_rec;  // [W]
+    const int32_t *plan_meta;    // [0] = runs in use
+    float *ws_acc;               // [W][2 slots][r][D]
+    float *ws_ml;                // [W][2 slots][r][2]
     int32_t B;
     int32_t max_blocks;
     int32_t max_ctx;     // host bound on context_lens (<= max_blocks * BS)
@@ -58,10 +81,109 @@ struct DecodeParams {
     int32_t Hq;
     int32_t Hkv;
     int32_t r;
-    int32_t span;
-    int32_t max_splits;
-    float score_scale;  // softmax_scale * log2(e)
+    int32_t W;           // wavefronts launched
+    float score_scale;   // softmax_scale * log2(e)
 };
+
+struct PlanParams {
+    const int32_t *context_lens;
+    int32_t *S;
+    PlanRecord *rec;
+    int32_t *meta;
+    int32_t B;
+    int32_t Hkv;
+    int32_t max_ctx;
+    int32_t W;            // balanced: runs wanted; fixed span: runs launched
+    int32_t span_tiles;   // 0: balanced; else tiles per span
+};
+
+__device__ __forceinline__ int ctx_tiles(const int32_t *lens, int b, int max_ctx)
+{
+    const int ctx = min(max(lens[b], 0), max_ctx);
+    return (ctx + 15) >> 4;
+}
+
+constexpr int kPlanThreads = 1024;
+constexpr int kPlanLdsSeqs = 8192;  // sequences whose tile prefix fits in LDS
+
+// One workgroup: exclusive scan of the tile counts, then the run records.
+__global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanParams p)
+{
+    __shared__ int32_t sc_t[kPlanThreads];
+    __shared__ int32_t sc_i[kPlanThreads];
+    __shared__ int32_t s_S[kPlanLdsSeqs + 1];
+    const int tid = threadIdx.x;
+    const int per = (p.B + kPlanThreads - 1) / kPlanThreads;
+    const int b0 = min(p.B, tid * per), b1 = min(p.B, b0 + per);
+    int st = 0, si = 0;
+    for (int b = b0; b < b1; ++b) {
+        const int n = ctx_tiles(p.context_lens, b, p.max_ctx);
+        st += n;
+        if (p.span_tiles)
+            si += (n + p.span_tiles - 1) / p.span_tiles;
+    }
+    sc_t[tid] = st;
+    sc_i[tid] = si;
+    __syncthreads();
+    for (int o = 1; o < kPlanThreads; o <<= 1) {  // inclusive scans
+        const int at = tid >= o ? sc_t[tid - o] : 0;
+        const int ai = tid >= o ? sc_i[tid - o] : 0;
+        __syncthreads();
+        sc_t[tid] += at;
+        sc_i[tid] += ai;
+        __syncthreads();
+    }
+    const int tot_t = sc_t[kPlanThreads - 1];
+    const int tot_i = sc_i[kPlanThreads - 1];
+    const int T = p.Hkv * tot_t;
+    const int W = p.span_tiles ? p.Hkv * tot_i : min(p.W, T);
+    const bool lds = p.B <= kPlanLdsSeqs;
+    int off_t = sc_t[tid] - st, off_i = sc_i[tid] - si;
+    for (int b = b0; b < b1; ++b) {
+        const int n = ctx_tiles(p.context_lens, b, p.max_ctx);
+        p.S[b] = off_t;
+        if (lds)
+            s_S[b] = off_t;
+        if (p.span_tiles) {
+            const int lo = p.Hkv * off_t;
+            const int m = (n + p.span_tiles - 1) / p.span_tiles;
+            for (int h = 0; h < p.Hkv; ++h)
+                for (int k = 0; k < m; ++k) {
+                    const int g0 = lo + h * n + k * p.span_tiles;
+                    p.rec[p.Hkv * off_i + h * m + k] =
+                        PlanRecord{b, g0, min(lo + (h + 1) * n, g0 + p.span_tiles), 0};
+                }
+            off_i += m;
+        }
+        off_t += n;
+    }
+    if (tid == kPlanThreads - 1) {
+        p.S[p.B] = tot_t;
+        if (lds)
+            s_S[p.B] = tot_t;
+        p.meta[0] = W;
+    }
+    if (p.span_tiles || T == 0)
+        return;
+    __syncthreads();
+    __threadfence_block();
+    // balanced runs: run w = [w T / W, (w + 1) T / W); its sequence is the
+    // last b with Hkv * S[b] <= g0 (binary search over the prefix)
+    const int32_t *S = lds ? s_S : p.S;
+    for (int w = tid; w < W; w += kPlanThreads) {
+        const int g0 = (int)((int64_t)w * T / W);
+        const int g1 = (int)((int64_t)(w + 1) * T / W);
+        int lo = 0, hi = p.B;  // invariant: Hkv * S[lo] <= g0 < Hkv * S[hi + 1]
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (p.Hkv * S[mid] <= g0)
+                lo = mid;
+            else
+                hi = mid - 1;
+        }
+        p.rec[w] = PlanRecord{lo, g0, g1, 0};
+    }
+}
 
 // Per-lane registers of one 16-token tile.
 template <int FMT, int D>
@@ -130,291 +252,332 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
     constexpr int DT = D / 16;   // 16-dim output tiles
     constexpr int EB = TileData<FMT, D>::EB;
     constexpr int G = D / NG;    // INT8 group size
+    constexpr int WIN = 64 * BS / 16;  // tiles covered by one 64-block window
     static_assert(FMT != FMT_INT8 || G >= 64, "groups must cover a 64-dim chunk");
 
-    // Work-item order: split index slowest, then sequence, then KV head.
-    // Consecutive workgroups are dealt round-robin to the 8 XCDs, so every
-    // XCD receives an equal share of each split index (the first split of
-    // every sequence exists; later ones only for long sequences).
-    const int units = p.B * p.Hkv;
-    const int split = blockIdx.x / units;
-    const int unit = blockIdx.x - split * units;
-    const int b = unit / p.Hkv;
-    const int h = unit - b * p.Hkv;
+    const int w = blockIdx.x;
+    if (w >= p.plan_meta[0])
+        return;
+    const PlanRecord rec = p.plan_rec[w];
     const int lane = threadIdx.x;
     const int col = lane & 15;
     const int grp = lane >> 4;
-
-    // Device lengths beyond the host bound are clamped so that no table entry
-    // or workspace slot outside the caller's buffers is ever addressed.
-    const int ctx = min(p.context_lens[b], p.max_ctx);
-    const int t_begin = split * p.span;
-    if (t_begin >= ctx)
-        return;
-    const int t_end = min(ctx, t_begin + p.span);
-    const int nsplit = (ctx + p.span - 1) / p.span;
-    const int ntiles = (t_end - t_begin + 15) >> 4;
     const bool head_ok = col < p.r;
-    const int qhead = h * p.r + col;
 
-    // ---- query operand, in the k-step dim order of the K loads:
-    //   1-byte codes: k-step s, lane group grp, element v -> dim
-    //       64 (s/4) + 16 grp + 4 (s%4) + v
-    //   fp16:   32 (s/2) + 8 grp + 4 (s%2) + v
-    f16x4 qop[KS];
-    {
-        const f16 *qrow = p.q + ((int64_t)b * p.Hq + (head_ok ? qhead : h * p.r)) * D;
-        if constexpr (EB == 1) {
-#pragma unroll
-            for (int c = 0; c < D / 64; ++c) {
-                const uint4 w0 = *reinterpret_cast<const uint4 *>(qrow + 64 * c + 16 * grp);
-                const uint4 w1 = *reinterpret_cast<const uint4 *>(qrow + 64 * c + 16 * grp + 8);
-                qop[4 * c + 0] = f16x4_from_u2(w0.x, w0.y);
-                qop[4 * c + 1] = f16x4_from_u2(w0.z, w0.w);
-                qop[4 * c + 2] = f16x4_from_u2(w1.x, w1.y);
-                qop[4 * c + 3] = f16x4_from_u2(w1.z, w1.w);
-            }
-        } else {
-#pragma unroll
-            for (int c = 0; c < D / 32; ++c) {
-                const uint4 w = *reinterpret_cast<const uint4 *>(qrow + 32 * c + 8 * grp);
-                qop[2 * c + 0] = f16x4_from_u2(w.x, w.y);
-                qop[2 * c + 1] = f16x4_from_u2(w.z, w.w);
-            }
-        }
-        if (!head_ok) {
-#pragma unroll
-            for (int s = 0; s < KS; ++s)
-                qop[s] = f16x4{0, 0, 0, 0};
-        }
-    }
+    float score_scale0 = p.score_scale;
 
-    float score_scale = p.score_scale;
-    float out_scale = 1.0f;
-    if constexpr (FMT == FMT_FP8) {
-        score_scale *= 256.0f * p.k_scale[h];
-        out_scale = 256.0f * p.v_scale[h];
-    }
+    // Attend over tiles [t0, t1) of unit (b, h); ctx clamped to the host bound.
+    auto attend = [&](const int b, const int h, const int ctx, const int n, const int t0,
+                      const int t1) {
+        const int qhead = h * p.r + col;
+        const int t_end = min(ctx, 16 * t1);  // token bound of this run
 
-    // ---- block table: the split's (at most 64) logical blocks, one per lane
-    const int32_t *bt = p.block_tables + (int64_t)b * p.max_blocks;
-    const int blk0 = t_begin / BS;
-    const int blk_last = (t_end - 1) / BS;
-    const int win = (blk0 + lane <= blk_last) ? bt[blk0 + lane] : 0;
-    auto tile_phys = [&](int it) -> int {
-        const int id = __builtin_amdgcn_readlane(win, (t_begin + 16 * it) / BS - blk0);
-        return min(max(id, 0), p.num_blocks - 1);  // never leave the pool
-    };
-    auto tile_off = [&](int it) -> int { return (t_begin + 16 * it) % BS; };
-
-    // o[tau][v]: output dim 64 (tau / 4) + 16 grp + 4 v + tau % 4, head col
-    f32x4 o[DT];
+        // ---- query operand, in the k-step dim order of the K loads:
+        //   1-byte codes: k-step s, lane group grp, element v -> dim
+        //       64 (s/4) + 16 grp + 4 (s%4) + v
+        //   fp16:   32 (s/2) + 8 grp + 4 (s%2) + v
+        f16x4 qop[KS];
+        {
+            const f16 *qrow = p.q + ((int64_t)b * p.Hq + (head_ok ? qhead : h * p.r)) * D;
+            if constexpr (EB == 1) {
 #pragma unroll
-    for (int i = 0; i < DT; ++i)
-        o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m = -INFINITY;
-    float l = 0.0f;
-
-    // One tile of 16 tokens starting at logical token ts, data in `cur`.
-    auto process = [&](const TileData<FMT, D> &cur, const int ts) {
-        // ---- this lane's scales: sk[v][j], sv[v][j] of tokens 4 grp + v
-        float sk[4][NG], sv[4][NG];
-        if constexpr (FMT == FMT_INT8) {
-            static_for<0, 4 * NG>([&](auto I) {
-                constexpr int i = decltype(I)::value;
-                sk[i / NG][i % NG] = row_bcast<i>(cur.sc);
-                sv[i / NG][i % NG] = row_bcast<4 * NG + i>(cur.sc);
-            });
-        }
-
-        // ---- S^T = K Q^T, one accumulator per INT8 group
-        f32x4 sacc[NG];
-#pragma unroll
-        for (int i = 0; i < NG; ++i)
-            sacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < KS; ++s) {
-            f16x4 a;
-            if constexpr (FMT == FMT_INT8) {
-                a = int8x4_to_f16x4(cur.k[s]);
-            } else if constexpr (FMT == FMT_FP8) {
-                a = fp8x4_to_f16x4_scaled(cur.k[s]);
+                for (int c = 0; c < D / 64; ++c) {
+                    const uint4 w0 = *reinterpret_cast<const uint4 *>(qrow + 64 * c + 16 * grp);
+                    const uint4 w1 = *reinterpret_cast<const uint4 *>(qrow + 64 * c + 16 * grp + 8);
+                    qop[4 * c + 0] = f16x4_from_u2(w0.x, w0.y);
+                    qop[4 * c + 1] = f16x4_from_u2(w0.z, w0.w);
+                    qop[4 * c + 2] = f16x4_from_u2(w1.x, w1.y);
+                    qop[4 * c + 3] = f16x4_from_u2(w1.z, w1.w);
+                }
             } else {
-                a = f16x4_from_u2(cur.k[2 * s], cur.k[2 * s + 1]);
-            }
-            const int gi = (FMT == FMT_INT8 && NG == 2) ? (s >> 2) : 0;
-            sacc[gi] = __builtin_amdgcn_mfma_f32_16x16x16f16(a, qop[s], sacc[gi], 0, 0, 0);
-        }
-
-        // ---- scores of tokens ts + 4 grp + v for query head col (base 2)
-        const int tok0 = ts + 4 * grp;
-        float z[4];
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            float acc;
-            if constexpr (FMT == FMT_INT8) {
-                acc = sacc[0][v] * sk[v][0];
-                if constexpr (NG == 2)
-                    acc += sacc[1][v] * sk[v][1];
-            } else {
-                acc = sacc[0][v];
-            }
-            z[v] = (tok0 + v < t_end) ? acc * score_scale : -INFINITY;
-        }
-
-        // ---- online softmax
-        float mt = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
-        mt = fmaxf(mt, __shfl_xor(mt, 16));
-        mt = fmaxf(mt, __shfl_xor(mt, 32));
-        if (__builtin_amdgcn_ballot_w64(mt > m)) {
-            const float mn = fmaxf(m, mt);
-            const float alpha = __builtin_amdgcn_exp2f(m - mn);
-            l *= alpha;
-#pragma unroll
-            for (int i = 0; i < DT; ++i)
-                o[i] *= alpha;
-            m = mn;
-        }
-        float pr[4];
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            pr[v] = __builtin_amdgcn_exp2f(z[v] - m);
-            l += pr[v];
-        }
-
-        // ---- P^T operands (V group scales folded in for INT8)
-        f16x4 pop[NG];
-        if constexpr (FMT == FMT_INT8) {
-#pragma unroll
-            for (int j = 0; j < NG; ++j) {
-#pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    pop[j][v] = (f16)((tok0 + v < t_end) ? pr[v] * sv[v][j] : 0.0f);
+                for (int c = 0; c < D / 32; ++c) {
+                    const uint4 w4 = *reinterpret_cast<const uint4 *>(qrow + 32 * c + 8 * grp);
+                    qop[2 * c + 0] = f16x4_from_u2(w4.x, w4.y);
+                    qop[2 * c + 1] = f16x4_from_u2(w4.z, w4.w);
                 }
             }
-        } else {
+            if (!head_ok) {
 #pragma unroll
-            for (int v = 0; v < 4; ++v)
-                pop[0][v] = (f16)pr[v];
+                for (int s = 0; s < KS; ++s)
+                    qop[s] = f16x4{0, 0, 0, 0};
+            }
+        }
+        float score_scale = score_scale0;
+        float out_scale = 1.0f;
+        if constexpr (FMT == FMT_FP8) {
+            score_scale *= 256.0f * p.k_scale[h];
+            out_scale = 256.0f * p.v_scale[h];
         }
 
-        // ---- O^T += V^T P^T; d-tile tau covers dims 64 (tau/4) + 4 m + tau%4
-        const bool partial = ts + 16 > t_end;
+        // o[tau][v]: output dim 64 (tau / 4) + 16 grp + 4 v + tau % 4, head col
+        f32x4 o[DT];
 #pragma unroll
-        for (int tau = 0; tau < DT; ++tau) {
-            const int g4 = tau >> 2, i = tau & 3;
-            f16x4 a;
+        for (int i = 0; i < DT; ++i)
+            o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+        float m = -INFINITY;
+        float l = 0.0f;
+
+        // One tile of 16 tokens starting at logical token ts, data in `cur`.
+        auto process = [&](const TileData<FMT, D> &cur, const int ts) {
+            // ---- this lane's scales: sk[v][j], sv[v][j] of tokens 4 grp + v
+            float sk[4][NG], sv[4][NG];
             if constexpr (FMT == FMT_INT8) {
-                a = int8x4_to_f16x4(cur.v[4 * g4 + i]);
-            } else if constexpr (FMT == FMT_FP8) {
-                a = fp8x4_to_f16x4_scaled(cur.v[4 * g4 + i]);
-            } else {
-                // fp16 micro-tiles hold 2 dims x 4 tokens: part i/2 of quad g4
-                const int x = 2 * g4 + (i >> 1), w = 2 * (i & 1);
-                a = f16x4_from_u2(cur.v[4 * x + w], cur.v[4 * x + w + 1]);
-                if (partial) {  // stale fp16 slots may hold non-finite values
+                static_for<0, 4 * NG>([&](auto I) {
+                    constexpr int i = decltype(I)::value;
+                    sk[i / NG][i % NG] = row_bcast<i>(cur.sc);
+                    sv[i / NG][i % NG] = row_bcast<4 * NG + i>(cur.sc);
+                });
+            }
+            // ---- S^T = K Q^T, one accumulator per INT8 group
+            f32x4 sacc[NG];
+#pragma unroll
+            for (int i = 0; i < NG; ++i)
+                sacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < KS; ++s) {
+                f16x4 a;
+                if constexpr (FMT == FMT_INT8) {
+                    a = int8x4_to_f16x4(cur.k[s]);
+                } else if constexpr (FMT == FMT_FP8) {
+                    a = fp8x4_to_f16x4_scaled(cur.k[s]);
+                } else {
+                    a = f16x4_from_u2(cur.k[2 * s], cur.k[2 * s + 1]);
+                }
+                const int gi = (FMT == FMT_INT8 && NG == 2) ? (s >> 2) : 0;
+                sacc[gi] = __builtin_amdgcn_mfma_f32_16x16x16f16(a, qop[s], sacc[gi], 0, 0, 0);
+            }
+            // ---- scores of tokens ts + 4 grp + v for query head col (base 2)
+            const int tok0 = ts + 4 * grp;
+            float z[4];
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                float acc;
+                if constexpr (FMT == FMT_INT8) {
+                    acc = sacc[0][v] * sk[v][0];
+                    if constexpr (NG == 2)
+                        acc += sacc[1][v] * sk[v][1];
+                } else {
+                    acc = sacc[0][v];
+                }
+                z[v] = (tok0 + v < t_end) ? acc * score_scale : -INFINITY;
+            }
+            // ---- online softmax
+            float mt = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
+            mt = fmaxf(mt, __shfl_xor(mt, 16));
+            mt = fmaxf(mt, __shfl_xor(mt, 32));
+            if (__builtin_amdgcn_ballot_w64(mt > m)) {
+                const float mn = fmaxf(m, mt);
+                const float alpha = __builtin_amdgcn_exp2f(m - mn);
+                l *= alpha;
+#pragma unroll
+                for (int i = 0; i < DT; ++i)
+                    o[i] *= alpha;
+                m = mn;
+            }
+            float pr[4];
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                pr[v] = __builtin_amdgcn_exp2f(z[v] - m);
+                l += pr[v];
+            }
+            // ---- P^T operands (V group scales folded in for INT8)
+            f16x4 pop[NG];
+            if constexpr (FMT == FMT_INT8) {
+#pragma unroll
+                for (int j = 0; j < NG; ++j) {
 #pragma unroll
                     for (int v = 0; v < 4; ++v)
-                        if (tok0 + v >= t_end)
-                            a[v] = (f16)0.0f;
+                        pop[j][v] = (f16)((tok0 + v < t_end) ? pr[v] * sv[v][j] : 0.0f);
                 }
+            } else {
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    pop[0][v] = (f16)pr[v];
             }
-            const int gi = (FMT == FMT_INT8 && NG == 2) ? (64 * g4) / G : 0;
-            o[tau] = __builtin_amdgcn_mfma_f32_16x16x16f16(a, pop[gi], o[tau], 0, 0, 0);
+            // ---- O^T += V^T P^T; d-tile tau covers dims 64 (tau/4) + 4 m + tau%4
+            const bool partial = ts + 16 > t_end;
+#pragma unroll
+            for (int tau = 0; tau < DT; ++tau) {
+                const int g4 = tau >> 2, i = tau & 3;
+                f16x4 a;
+                if constexpr (FMT == FMT_INT8) {
+                    a = int8x4_to_f16x4(cur.v[4 * g4 + i]);
+                } else if constexpr (FMT == FMT_FP8) {
+                    a = fp8x4_to_f16x4_scaled(cur.v[4 * g4 + i]);
+                } else {
+                    // fp16 micro-tiles hold 2 dims x 4 tokens: part i/2 of quad g4
+                    const int x = 2 * g4 + (i >> 1), wd = 2 * (i & 1);
+                    a = f16x4_from_u2(cur.v[4 * x + wd], cur.v[4 * x + wd + 1]);
+                    if (partial) {  // stale fp16 slots may hold non-finite values
+#pragma unroll
+                        for (int v = 0; v < 4; ++v)
+                            if (tok0 + v >= t_end)
+                                a[v] = (f16)0.0f;
+                    }
+                }
+                const int gi = (FMT == FMT_INT8 && NG == 2) ? (64 * g4) / G : 0;
+                o[tau] = __builtin_amdgcn_mfma_f32_16x16x16f16(a, pop[gi], o[tau], 0, 0, 0);
+            }
+        };
+
+        // ---- walk the run in windows of up to 64 blocks (block ids one per
+        // lane); inside a window, ping-pong over two tile buffers: tile i+1's
+        // loads are in flight while tile i is computed.  Loads are issued
+        // unconditionally (past the end they repeat the last tile) so the
+        // wait counts stay static.
+        const int32_t *bt = p.block_tables + (int64_t)b * p.max_blocks;
+        for (int c0 = t0; c0 < t1; c0 += WIN) {
+            const int c1 = min(t1, c0 + WIN);
+            const int blk0 = (16 * c0) / BS;
+            const int blk_last = (16 * c1 - 1) / BS;
+            const int win = (blk0 + lane <= blk_last) ? bt[blk0 + lane] : 0;
+            const int ntiles = c1 - c0;
+            auto ld = [&](TileData<FMT, D> &buf, int i) {
+                i = c0 + min(i, ntiles - 1);
+                int id = __builtin_amdgcn_readlane(win, (16 * i) / BS - blk0);
+                id = min(max(id, 0), p.num_blocks - 1);  // never leave the pool
+                load_tile<FMT, D, BS, NG>(p, buf, id, h, (16 * i) % BS, col, grp);
+            };
+            TileData<FMT, D> buf0, buf1;
+            ld(buf0, 0);
+            for (int it = 0; it < ntiles; it += 2) {
+                ld(buf1, it + 1);
+                process(buf0, 16 * (c0 + it));
+                ld(buf0, it + 2);
+                if (it + 1 < ntiles)
+                    process(buf1, 16 * (c0 + it + 1));
+            }
         }
+
+        // ---- epilogue: lane holds dims 64 g4 + 16 grp + (0..15) of head col
+        float lt = l + __shfl_xor(l, 16);
+        lt += __shfl_xor(lt, 32);
+        if (!head_ok)
+            return;
+        if (t0 == 0 && t1 == n) {  // the whole unit: final output
+            const float inv = out_scale / lt;
+            f16 *orow = p.out + ((int64_t)b * p.Hq + qhead) * D + 16 * grp;
+#pragma unroll
+            for (int g4 = 0; g4 < D / 64; ++g4) {
+                f16x4 hv[4];
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    hv[v] = f16x4{(f16)(o[4 * g4 + 0][v] * inv), (f16)(o[4 * g4 + 1][v] * inv),
+                                  (f16)(o[4 * g4 + 2][v] * inv), (f16)(o[4 * g4 + 3][v] * inv)};
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    *reinterpret_cast<f16x4 *>(orow + 64 * g4 + 4 * v) = hv[v];
+            }
+            return;
+        }
+        // a piece of a unit: slot 0 if it continues a unit, slot 1 if it starts one
+        const int slot = t0 > 0 ? 0 : 1;
+        const int64_t idx = ((int64_t)w * 2 + slot) * p.r + col;
+        float *wacc = p.ws_acc + idx * D + 16 * grp;
+#pragma unroll
+        for (int g4 = 0; g4 < D / 64; ++g4)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const f32x4 wv = {o[4 * g4 + 0][v] * out_scale, o[4 * g4 + 1][v] * out_scale,
+                                  o[4 * g4 + 2][v] * out_scale, o[4 * g4 + 3][v] * out_scale};
+                *reinterpret_cast<f32x4 *>(wacc + 64 * g4 + 4 * v) = wv;
+            }
+        if (grp == 0)
+            *reinterpret_cast<float2 *>(p.ws_ml + 2 * idx) = make_float2(m, lt);
     };
 
-    // Ping-pong over two tile buffers: the loads of tile i+1 are in flight
-    // while tile i is computed.  Loads are issued unconditionally (past the
-    // end they repeat the last tile) so the wait counts stay static.
-    TileData<FMT, D> buf0, buf1;
-    load_tile<FMT, D, BS, NG>(p, buf0, tile_phys(0), h, tile_off(0), col, grp);
-    for (int it = 0; it < ntiles; it += 2) {
-        const int i1 = min(it + 1, ntiles - 1);
-        load_tile<FMT, D, BS, NG>(p, buf1, tile_phys(i1), h, tile_off(i1), col, grp);
-        process(buf0, t_begin + 16 * it);
-        const int i2 = min(it + 2, ntiles - 1);
-        load_tile<FMT, D, BS, NG>(p, buf0, tile_phys(i2), h, tile_off(i2), col, grp);
-        if (it + 1 < ntiles)
-            process(buf1, t_begin + 16 * (it + 1));
-    }
-
-    // ---- epilogue: lane holds dims 64 g4 + 16 grp + (0..15) of head col
-    float lt = l + __shfl_xor(l, 16);
-    lt += __shfl_xor(lt, 32);
-    if (!head_ok)
-        return;
-    if (nsplit == 1) {
-        const float inv = out_scale / lt;
-        f16 *orow = p.out + ((int64_t)b * p.Hq + qhead) * D + 16 * grp;
-#pragma unroll
-        for (int g4 = 0; g4 < D / 64; ++g4) {
-            f16x4 hv[4];
-#pragma unroll
-            for (int v = 0; v < 4; ++v)
-                hv[v] = f16x4{(f16)(o[4 * g4 + 0][v] * inv), (f16)(o[4 * g4 + 1][v] * inv),
-                              (f16)(o[4 * g4 + 2][v] * inv), (f16)(o[4 * g4 + 3][v] * inv)};
-#pragma unroll
-            for (int v = 0; v < 4; ++v)
-                *reinterpret_cast<f16x4 *>(orow + 64 * g4 + 4 * v) = hv[v];
+    // ---- walk the run [g0, g1) unit by unit (all values wave-uniform)
+    int b = rec.b;
+    int g = rec.g0;
+    int n = ctx_tiles(p.context_lens, b, p.max_ctx);
+    int base = p.Hkv * p.plan_S[b];
+    while (g < rec.g1) {
+        if (g >= base + p.Hkv * n) {
+            base += p.Hkv * n;
+            ++b;
+            n = ctx_tiles(p.context_lens, b, p.max_ctx);
+            continue;
         }
-        return;
+        const int h = (g - base) / n;
+        const int t0 = g - base - h * n;
+        const int t1 = min(n, t0 + (rec.g1 - g));
+        const int ctx = min(p.context_lens[b], p.max_ctx);
+        attend(b, h, ctx, n, t0, t1);
+        g += t1 - t0;
     }
-    const int64_t idx = ((int64_t)b * p.Hq + qhead) * p.max_splits + split;
-    float *wacc = p.ws_acc + idx * D + 16 * grp;
-#pragma unroll
-    for (int g4 = 0; g4 < D / 64; ++g4)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            const f32x4 w = {o[4 * g4 + 0][v] * out_scale, o[4 * g4 + 1][v] * out_scale,
-                             o[4 * g4 + 2][v] * out_scale, o[4 * g4 + 3][v] * out_scale};
-            *reinterpret_cast<f32x4 *>(wacc + 64 * g4 + 4 * v) = w;
-        }
-    if (grp == 0)
-        *reinterpret_cast<float2 *>(p.ws_ml + 2 * idx) = make_float2(m, lt);
 }
 
-// Log-sum-exp merge of the split partials of one (sequence, query head):
+// Log-sum-exp merge of the pieces of a unit cut by run boundaries:
 //   M = max_i m_i,  L = sum_i l_i 2^(m_i - M),  out = sum_i acc_i 2^(m_i - M) / L.
-// Runs as its own launch after the split kernel, so the partials written by
-// wavefronts on any XCD are visible without device-wide fences inside the
-// split kernel.  Sequences that were not split were finished by that kernel.
+// Workgroup (k, head) looks at the boundary between runs k-1 and k; it merges
+// that query head of the unit holding tile g0(k) when that boundary is the
+// unit's first one.  The pieces are run k-1's slot 1 (the unit's start) and
+// slot 0 of runs k, k+1, ... up to the unit's end.  It runs as its own
+// launch, so the partials written by wavefronts on any XCD are visible
+// without device-wide fences.
 template <int D>
-__global__ __launch_bounds__(64) void merge_splits_kernel(DecodeParams p)
+__global__ __launch_bounds__(64) void merge_runs_kernel(DecodeParams p)
 {
-    const int g = blockIdx.x;
-    const int b = blockIdx.y;
-    const int lane = threadIdx.x;
-    const int ctx = min(p.context_lens[b], p.max_ctx);
-    const int nsplit = (ctx + p.span - 1) / p.span;
-    if (nsplit <= 1)
+    const int k = blockIdx.x + 1;
+    const int col = blockIdx.y;
+    const int nrec = p.plan_meta[0];
+    if (k >= nrec)
         return;
-    const int64_t base = ((int64_t)b * p.Hq + g) * p.max_splits;
+    const PlanRecord rk = p.plan_rec[k];
+    const int b = rk.b;
+    const int n = ctx_tiles(p.context_lens, b, p.max_ctx);
+    if (n == 0)
+        return;
+    const int base = p.Hkv * p.plan_S[b];
+    const int h = (rk.g0 - base) / n;
+    const int us = base + h * n, ue = us + n;
+    if (us == rk.g0)
+        return;                           // the boundary is a unit start
+    if (p.plan_rec[k - 1].g0 > us)
+        return;                           // an earlier boundary cuts this unit
+    const int lane = threadIdx.x;
+    // pieces: j = 0 is run k-1 (slot 1), j >= 1 is run k-1+j (slot 0)
+    auto piece = [&](int j) -> int64_t {
+        return ((int64_t)(k - 1 + j) * 2 + (j == 0 ? 1 : 0)) * p.r + col;
+    };
+    // number of pieces: runs k-1 .. kl with g0 < ue
+    int np = 1;
+    for (int j0 = 0;; j0 += 64) {
+        const int rj = k + j0 + lane;
+        const bool in = rj < nrec && p.plan_rec[rj].g0 < ue;
+        const uint64_t mask = __builtin_amdgcn_ballot_w64(in);
+        np += __builtin_popcountll(mask);
+        if (mask != ~0ull)
+            break;
+    }
     float mx = -INFINITY;
-    for (int i = lane; i < nsplit; i += 64)
-        mx = fmaxf(mx, p.ws_ml[2 * (base + i)]);
+    for (int j = lane; j < np; j += 64)
+        mx = fmaxf(mx, p.ws_ml[2 * piece(j)]);
     mx = wave_max(mx);
     float ls = 0.0f;
-    for (int i = lane; i < nsplit; i += 64)
-        ls += p.ws_ml[2 * (base + i) + 1] * __builtin_amdgcn_exp2f(p.ws_ml[2 * (base + i)] - mx);
+    for (int j = lane; j < np; j += 64)
+        ls += p.ws_ml[2 * piece(j) + 1] * __builtin_amdgcn_exp2f(p.ws_ml[2 * piece(j)] - mx);
     ls = wave_sum(ls);
-    const float inv = 1.0f / ls;
     constexpr int PER = D / 64;
     float acc[PER];
 #pragma unroll
-    for (int j = 0; j < PER; ++j)
-        acc[j] = 0.0f;
-    for (int i = 0; i < nsplit; ++i) {
-        const float w = __builtin_amdgcn_exp2f(p.ws_ml[2 * (base + i)] - mx);
-        const float *a = p.ws_acc + (base + i) * D + PER * lane;
+    for (int i = 0; i < PER; ++i)
+        acc[i] = 0.0f;
+#pragma unroll 4
+    for (int j = 0; j < np; ++j) {
+        const int64_t ix = piece(j);
+        const float wgt = __builtin_amdgcn_exp2f(p.ws_ml[2 * ix] - mx);
+        const float *a = p.ws_acc + ix * D + PER * lane;
 #pragma unroll
-        for (int j = 0; j < PER; ++j)
-            acc[j] += a[j] * w;
+        for (int i = 0; i < PER; ++i)
+            acc[i] += a[i] * wgt;
     }
-    f16 *orow = p.out + ((int64_t)b * p.Hq + g) * D + PER * lane;
+    const float inv = 1.0f / ls;
+    f16 *orow = p.out + ((int64_t)b * p.Hq + h * p.r + col) * D + PER * lane;
 #pragma unroll
-    for (int j = 0; j < PER; ++j)
-        orow[j] = (f16)(acc[j] * inv);
+    for (int i = 0; i < PER; ++i)
+        orow[i] = (f16)(acc[i] * inv);
 }
 
 }  // namespace kvq

@@ -29,8 +29,7 @@ POOL_DTYPES = {"fp16": torch.float16, "int8": torch.int8, "fp8": torch.uint8}
 STATUS = {0: "KVQ_OK", -1: "KVQ_ERR_INVALID_ARG", -2: "KVQ_ERR_UNSUPPORTED",
           -3: "KVQ_ERR_WORKSPACE", -4: "KVQ_ERR_HIP"}
 EXPORTS = ("kvq_status_string", "kvq_version", "kvq_cache_write",
-           "kvq_paged_decode", "kvq_decode_split_tokens",
-           "kvq_decode_workspace_size", "kvq_copy_blocks")
+           "kvq_paged_decode", "kvq_decode_workspace_size", "kvq_copy_blocks")
 
 
 class KvqError(RuntimeError):
@@ -67,8 +66,6 @@ def lib() -> ctypes.CDLL:
                                            i32, i32, i32, i32, i32, i32, i32,
                                            ctypes.c_float, i32, P, P,
                                            ctypes.c_size_t, P]
-            L.kvq_decode_split_tokens.restype = i32
-            L.kvq_decode_split_tokens.argtypes = [i32] * 5
             L.kvq_decode_workspace_size.restype = ctypes.c_size_t
             L.kvq_decode_workspace_size.argtypes = [i32] * 7
             L.kvq_copy_blocks.restype = i32
@@ -157,12 +154,6 @@ def kvq_cache_write(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor
     _check(st, "kvq_cache_write")
 
 
-def kvq_decode_split_tokens(num_seqs: int, num_kv_heads: int, block_size: int,
-                            max_context_len: int, split_tokens: int = 0) -> int:
-    return int(lib().kvq_decode_split_tokens(num_seqs, num_kv_heads, block_size,
-                                             max_context_len, split_tokens))
-
-
 def kvq_decode_workspace_size(num_seqs: int, num_q_heads: int, num_kv_heads: int,
                               head_dim: int, block_size: int, max_context_len: int,
                               split_tokens: int = 0) -> int:
@@ -178,7 +169,7 @@ def alloc_workspace(nbytes: int, device="cuda") -> Optional[torch.Tensor]:
     """Decode workspace (contents on entry do not matter)."""
     if nbytes == 0:
         return None
-    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+    return torch.empty((nbytes + 15) // 16 * 16, dtype=torch.uint8, device=device)
 
 
 def kvq_paged_decode(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
@@ -203,8 +194,8 @@ def kvq_paged_decode(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor
     for t in (q, k_pool, v_pool, block_tables, context_lens, out):
         if not t.is_contiguous():
             raise ValueError("tensors must be contiguous")
-    ws_need = kvq_decode_workspace_size(B, hq, hkv, d, bs, max_context_len, split_tokens) \
-        if B > 0 else 0
+    ws_need = kvq_decode_workspace_size(B, hq, hkv, d, bs, max(max_context_len, 1),
+                                        split_tokens) if B > 0 else 0
     if workspace is None and ws_need:
         workspace = alloc_workspace(ws_need, q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()

@@ -142,23 +142,23 @@ def test_status_strings_and_version(lib):
         assert lib.kvq_status_string(code)
 
 
-def test_split_planner_and_workspace(lib):
+def test_workspace_size(lib):
     from paged_quantized_kv_cache_amd import kvq
-    # short contexts: one split, no workspace
-    assert kvq.kvq_decode_split_tokens(4, 1, 16, 33) >= 33
-    assert kvq.kvq_decode_workspace_size(4, 4, 1, 64, 16, 33) == 0
-    # long contexts are split into spans of at most 1024 tokens
-    span = kvq.kvq_decode_split_tokens(16, 8, 16, 32768)
-    assert span % 16 == 0 and span <= 1024
-    ws = kvq.kvq_decode_workspace_size(16, 32, 8, 128, 16, 32768)
-    nsplit = -(-32768 // span)
-    assert ws >= 16 * 32 * nsplit * (128 + 2) * 4
-    # explicit spans
-    assert kvq.kvq_decode_split_tokens(2, 2, 16, 100, 32) == 32
-    assert kvq.kvq_decode_workspace_size(2, 4, 2, 64, 16, 100, 32) > 0
-    assert lib.kvq_decode_split_tokens(2, 2, 16, 100, 17) == -1
+    # always holds the run plan; grows with the partial slots of the runs
+    small = kvq.kvq_decode_workspace_size(4, 4, 1, 64, 16, 33)
+    assert small > 0
+    big = kvq.kvq_decode_workspace_size(16, 32, 8, 128, 16, 32768)
+    assert big > small
+    # fixed spans: one run per span of every (sequence, KV head) unit
+    fixed = kvq.kvq_decode_workspace_size(16, 32, 8, 128, 16, 32768, 1024)
+    runs = 16 * 8 * 32
+    assert fixed >= runs * 2 * 4 * (128 + 2) * 4
     with pytest.raises(ValueError):
         kvq.kvq_decode_workspace_size(2, 4, 2, 64, 16, 0)
+    with pytest.raises(ValueError):
+        kvq.kvq_decode_workspace_size(2, 4, 2, 64, 16, 100, 24)
+    with pytest.raises(ValueError):
+        kvq.kvq_decode_workspace_size(2, 6, 4, 64, 16, 100)
 
 
 def test_bad_arguments_rejected_before_any_device_work(lib):
@@ -196,6 +196,7 @@ def test_bad_arguments_rejected_before_any_device_work(lib):
     assert dec(sm=-1.0) == -1
     assert dec(q=None) == -1
     assert dec(split=16) == -3                    # needs a workspace
+    assert dec() == -3
     assert dec(D=96) == -2
     assert dec(B=0) == 0
     assert dec(dt=1, ks=None) == -1
