@@ -126,7 +126,11 @@ KVQ_API kvq_status kvq_cache_write(const void *k, const void *v,
  *
  *   q             fp16 [num_seqs][num_q_heads][head_dim].
  *   block_tables  int32 [num_seqs][max_blocks_per_seq]; entries past
- *                 ceil(ctx / block_size) are never read.
+ *                 ceil(ctx / block_size) are never read.  Bits 0..29 of an
+ *                 entry are the physical block id; bit 30 may be set on
+ *                 blocks that several sequences share (a prefix): it only
+ *                 changes the cache policy of their loads, never the result.
+ *                 Bit 31 must be 0.
  *   context_lens  int32 [num_seqs] on the device, each in
  *                 [1, max_context_len]; max_context_len is the host-side bound
  *                 (used to plan the split) and must not exceed

@@ -19,6 +19,7 @@ from typing import Dict, List, Optional, Tuple
 import numpy as np
 
 TABLE_PAD = -1  # value of table entries past a sequence's last block
+SHARED_HINT = 1 << 30  # table-entry bit: block read by several sequences
 
 
 class PoolExhausted(RuntimeError):
@@ -92,7 +93,11 @@ class BlockManager:
         return blocks[-1] * self.block_size + off, copy
 
     # ------------------------------------------------------------ tables
-    def tables(self, num_seqs: int, max_blocks: Optional[int] = None) -> np.ndarray:
+    def tables(self, num_seqs: int, max_blocks: Optional[int] = None,
+               mark_shared: bool = False) -> np.ndarray:
+        """Block tables ``int32 [num_seqs][width]``.  With ``mark_shared``,
+        entries of blocks held by more than one sequence carry SHARED_HINT
+        (bit 30), the decode kernel's cache-policy hint."""
         width = max((len(self._blocks.get(s, [])) for s in range(num_seqs)),
                     default=0)
         width = max(width, 1) if max_blocks is None else max_blocks
@@ -101,7 +106,10 @@ class BlockManager:
             bl = self._blocks.get(s, [])
             if len(bl) > width:
                 raise ValueError("table width too small")
-            t[s, :len(bl)] = bl
+            ids = np.asarray(bl, np.int64)
+            if mark_shared and ids.size:
+                ids = np.where(self.refcount[ids] > 1, ids | SHARED_HINT, ids)
+            t[s, :len(bl)] = ids
         return t
 
     def used_blocks(self) -> List[int]:

@@ -346,7 +346,7 @@ kvq_status kvq_paged_decode(const void *q, const void *k_pool, const void *v_poo
     if (st != KVQ_OK)
         return st;
     if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_blocks <= 0 ||
-        max_blocks_per_seq <= 0)
+        max_blocks_per_seq <= 0 || num_blocks > kBlockIdMask + 1)
         return KVQ_ERR_INVALID_ARG;
     if (num_q_heads % num_kv_heads != 0)
         return KVQ_ERR_INVALID_ARG;

@@ -53,6 +53,13 @@ namespace kvq {
 // cut by run boundaries leaves (m, l, acc) partials that the boundary merge
 // kernel combines.  The partition depends only on the lengths, never on
 // where blocks sit in the pool.
+// Block-table entries: bits 0..29 hold the physical block id; bit 30 is a
+// caching hint set by the caller for blocks shared by several sequences.
+constexpr int kBlockIdMask = 0x3fffffff;
+// Buffer descriptor word 3 for raw (untyped) buffer loads on gfx9-class GPUs.
+constexpr int kBufferConfig = 0x00020000;
+constexpr int kSharedBlock = 0x40000000;
+
 struct PlanRecord {
     int32_t b;   // sequence holding tile g0
     int32_t g0;  // first tile of the run
@@ -206,21 +213,26 @@ __device__ __forceinline__ float row_bcast(float x)
     return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x10 | (idx << 5)));
 }
 
-template <int FMT, int D, int BS, int NG>
-__device__ __forceinline__ void load_tile(const DecodeParams &p, TileData<FMT, D> &t,
-                                          int phys, int h, int toff, int col, int grp)
+template <int FMT, int D, int BS, int NG, bool kNT>
+__device__ __forceinline__ void load_codes(const DecodeParams &p, TileData<FMT, D> &t,
+                                           const uint8_t *kb, const uint8_t *vb, int toff,
+                                           int col, int grp)
 {
     constexpr int EB = TileData<FMT, D>::EB;
     constexpr int NL = TileData<FMT, D>::NL;
-    const int64_t tile = (int64_t)phys * p.Hkv + h;
-    const uint8_t *kb = p.k_pool + tile * (BS * D * EB);
-    const uint8_t *vb = p.v_pool + tile * (BS * D * EB);
-    // K/V codes are read once per step: nontemporal loads keep them from
-    // displacing reusable lines (block tables, scales, q) in the caches.
+    // Buffer loads on a descriptor spanning one tile: the cache policy is an
+    // immediate of each load (nt = bit 1 of the aux field on gfx950), and
+    // offsets past the tile read zeros instead of faulting.
+    constexpr int kAux = kNT ? 2 : 0;
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t *>(kb), 0, BS * D * EB, kBufferConfig);
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t *>(vb), 0, BS * D * EB, kBufferConfig);
 #pragma unroll
     for (int x = 0; x < NL; ++x) {
         // K chunk x of token toff + col: bytes [16 grp, 16 grp + 16) of its row
-        const u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(kb + (x * BS + toff + col) * 64 + 16 * grp));
+        const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(
+            rk, (x * BS + toff + col) * 64 + 16 * grp, 0, kAux);
         t.k[4 * x + 0] = w.x;
         t.k[4 * x + 1] = w.y;
         t.k[4 * x + 2] = w.z;
@@ -230,13 +242,33 @@ __device__ __forceinline__ void load_tile(const DecodeParams &p, TileData<FMT, D
     for (int x = 0; x < NL; ++x) {
         // V micro-tile: part e, dim quad col + 16 * g4, token quad toff/4 + grp
         const int e = x % EB, g4 = x / EB;
-        const u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(
-            vb + ((((toff / 16) * EB + e) * (D / 4) + col + 16 * g4) * 4 + grp) * 16));
+        const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(
+            rv, ((((toff / 16) * EB + e) * (D / 4) + col + 16 * g4) * 4 + grp) * 16, 0, kAux);
         t.v[4 * x + 0] = w.x;
         t.v[4 * x + 1] = w.y;
         t.v[4 * x + 2] = w.z;
         t.v[4 * x + 3] = w.w;
     }
+}
+
+// Loads one 16-token tile.  Codes of private blocks are read once per step,
+// so they use nontemporal loads that do not displace reusable lines; blocks
+// the caller marks as shared (several sequences read them in the same step)
+// use ordinary loads so that later readers can hit in L2 / the last-level
+// cache.
+template <int FMT, int D, int BS, int NG>
+__device__ __forceinline__ void load_tile(const DecodeParams &p, TileData<FMT, D> &t,
+                                          int phys, bool shared, int h, int toff, int col,
+                                          int grp)
+{
+    constexpr int EB = TileData<FMT, D>::EB;
+    const int64_t tile = (int64_t)phys * p.Hkv + h;
+    const uint8_t *kb = p.k_pool + tile * (BS * D * EB);
+    const uint8_t *vb = p.v_pool + tile * (BS * D * EB);
+    if (shared)
+        load_codes<FMT, D, BS, NG, false>(p, t, kb, vb, toff, col, grp);
+    else
+        load_codes<FMT, D, BS, NG, true>(p, t, kb, vb, toff, col, grp);
     if constexpr (FMT == FMT_INT8) {
         const int e = col % (8 * NG);
         const float *arr = e < 4 * NG ? p.k_scale : p.v_scale;
@@ -435,9 +467,10 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
             const int ntiles = c1 - c0;
             auto ld = [&](TileData<FMT, D> &buf, int i) {
                 i = c0 + min(i, ntiles - 1);
-                int id = __builtin_amdgcn_readlane(win, (16 * i) / BS - blk0);
-                id = min(max(id, 0), p.num_blocks - 1);  // never leave the pool
-                load_tile<FMT, D, BS, NG>(p, buf, id, h, (16 * i) % BS, col, grp);
+                const int e = __builtin_amdgcn_readlane(win, (16 * i) / BS - blk0);
+                const int id = min(max(e & kBlockIdMask, 0), p.num_blocks - 1);  // stay in the pool
+                load_tile<FMT, D, BS, NG>(p, buf, id, (e & kSharedBlock) != 0, h, (16 * i) % BS,
+                                          col, grp);
             };
             TileData<FMT, D> buf0, buf1;
             ld(buf0, 0);

@@ -64,7 +64,8 @@ class DecodeCase:
         # holds no data, never at an address outside the pool.
         unused = sorted(set(range(L.num_blocks)) - set(int(x) for x in L.used_blocks))
         self.pad_block = unused[0] if unused else 0
-        bt = L.block_tables.copy()
+        # decode reads the tables with the shared-block cache hints
+        bt = L.block_tables_hinted.copy()
         bt[bt < 0] = self.pad_block
         dev = self.device
         self.block_tables = torch.from_numpy(bt).to(dev)

@@ -165,6 +165,7 @@ class Layout:
     """
     context_lens: np.ndarray          # [B] int64
     block_tables: np.ndarray          # [B][max_blocks] int32 (after append)
+    block_tables_hinted: np.ndarray   # same, shared blocks carry the hint bit
     num_blocks: int
     seq_tokens: List[np.ndarray]      # per sequence, unique token ids
     n_unique: int
@@ -265,9 +266,11 @@ def build_layout(s: Spec, lens: np.ndarray, rng: np.random.Generator) -> Layout:
         seq_tokens[b] = np.concatenate([seq_tokens[b], append_ids[b:b + 1]])
 
     tables = bm.tables(B)
+    hinted = bm.tables(B, mark_shared=True)
     return Layout(
         context_lens=lens.copy(),
         block_tables=tables,
+        block_tables_hinted=hinted,
         num_blocks=nblocks,
         seq_tokens=seq_tokens,
         n_unique=uid,

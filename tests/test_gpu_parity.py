@@ -189,6 +189,13 @@ def test_shared_prefix_and_cow(fmt, gpu):
     got_priv = _host(priv.decode(0))
     got_shared = _host(case.decode(0))
     assert np.array_equal(got_priv.view(np.uint16), got_shared.view(np.uint16))
+    # the shared-block hint bit changes only the cache policy of the loads
+    assert (case.layout.block_tables_hinted >> 30 == 1).any()
+    plain = case.block_tables & 0x3FFFFFFF
+    case.block_tables, hinted = plain, case.block_tables
+    got_plain = _host(case.decode(0))
+    case.block_tables = hinted
+    assert np.array_equal(got_plain.view(np.uint16), got_shared.view(np.uint16))
 
 
 def test_cow_leaves_other_sharer_untouched(gpu):
