@@ -200,9 +200,9 @@ kvq_status launch_decode(DecodeParams p, const LaunchPlan &lp, hipStream_t s)
     int32_t *S = reinterpret_cast<int32_t *>(lp.ws + w.s_off);
     int32_t *meta = reinterpret_cast<int32_t *>(lp.ws + w.meta_off);
     PlanRecord *rec = reinterpret_cast<PlanRecord *>(lp.ws + w.rec_off);
-    p.plan_S = S;
     p.plan_meta = meta;
     p.plan_rec = rec;
+    p.inline_plan = (lp.split_tokens == 0 && p.B <= 64 * kInlineSeqs) ? 1 : 0;
     p.ws_ml = reinterpret_cast<float *>(lp.ws + w.ml_off);
     p.ws_acc = reinterpret_cast<float *>(lp.ws + w.acc_off);
     p.W = (int32_t)runs;
@@ -217,7 +217,8 @@ kvq_status launch_decode(DecodeParams p, const LaunchPlan &lp, hipStream_t s)
     pp.max_ctx = lp.max_ctx;
     pp.W = (int32_t)runs;
     pp.span_tiles = lp.split_tokens / 16;
-    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, pp);
+    if (!p.inline_plan)
+        hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, pp);
     hipLaunchKernelGGL((paged_decode_kernel<FMT, D, BS, NG>), dim3((unsigned)runs), dim3(64), 0,
                        s, p);
     if (runs > 1)

@@ -61,11 +61,16 @@ constexpr int kBufferConfig = 0x00020000;
 constexpr int kSharedBlock = 0x40000000;
 
 struct PlanRecord {
-    int32_t b;   // sequence holding tile g0
-    int32_t g0;  // first tile of the run
-    int32_t g1;  // one past the last tile
-    int32_t pad;
+    int32_t b;     // sequence holding tile g0
+    int32_t g0;    // first tile of the run
+    int32_t g1;    // one past the last tile
+    int32_t base;  // first tile of sequence b (Hkv * tiles before b)
 };
+
+// Batches of at most 64 * kInlineSeqs sequences are planned inside the
+// decode kernel (each wavefront scans the lengths itself); larger ones by
+// plan_kernel.
+constexpr int kInlineSeqs = 16;
 
 struct DecodeParams {
     const f16 *q;
@@ -76,9 +81,9 @@ struct DecodeParams {
     const int32_t *block_tables;
     const int32_t *context_lens;
     f16 *out;
-    const int32_t *plan_S;       // [B + 1] tiles before each sequence (per KV head)
-    const PlanRecord *plan_rec;  // [W]
-    const int32_t *plan_meta;    // [0] = runs in use
+    PlanRecord *plan_rec;        // [W] (written here when planned inline)
+    int32_t *plan_meta;          // [0] = runs in use
+    int32_t inline_plan;         // 1: plan inside the decode kernel
     float *ws_acc;               // [W][2 slots][r][D]
     float *ws_ml;                // [W][2 slots][r][2]
     int32_t B;
@@ -158,7 +163,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanParams p)
                 for (int k = 0; k < m; ++k) {
                     const int g0 = lo + h * n + k * p.span_tiles;
                     p.rec[p.Hkv * off_i + h * m + k] =
-                        PlanRecord{b, g0, min(lo + (h + 1) * n, g0 + p.span_tiles), 0};
+                        PlanRecord{b, g0, min(lo + (h + 1) * n, g0 + p.span_tiles), lo};
                 }
             off_i += m;
         }
@@ -188,7 +193,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanParams p)
             else
                 hi = mid - 1;
         }
-        p.rec[w] = PlanRecord{lo, g0, g1, 0};
+        p.rec[w] = PlanRecord{lo, g0, g1, p.Hkv * S[lo]};
     }
 }
 
@@ -288,12 +293,55 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
     static_assert(FMT != FMT_INT8 || G >= 64, "groups must cover a 64-dim chunk");
 
     const int w = blockIdx.x;
-    if (w >= p.plan_meta[0])
-        return;
-    const PlanRecord rec = p.plan_rec[w];
     const int lane = threadIdx.x;
     const int col = lane & 15;
     const int grp = lane >> 4;
+    PlanRecord rec;
+    if (p.inline_plan) {
+        // every wavefront scans the lengths: lane i holds sequences
+        // per*i .. per*i + per - 1
+        const int per = (p.B + 63) >> 6;
+        int tl[kInlineSeqs];
+        int sum = 0;
+#pragma unroll
+        for (int j = 0; j < kInlineSeqs; ++j) {
+            const int bb = lane * per + j;
+            tl[j] = (j < per && bb < p.B) ? ctx_tiles(p.context_lens, bb, p.max_ctx) : 0;
+            sum += tl[j];
+        }
+        int incl = sum;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int y = __shfl_up(incl, o);
+            if (lane >= o)
+                incl += y;
+        }
+        const int T = p.Hkv * __shfl(incl, 63);
+        const int W = min(p.W, T);
+        if (w == 0 && lane == 0)
+            p.plan_meta[0] = W;  // runs in use, for the merge launch
+        if (w >= W)
+            return;
+        const int g0 = (int)((int64_t)w * T / W);
+        const int g1 = (int)((int64_t)(w + 1) * T / W);
+        int s0 = incl - sum, found = -1, fbase = 0;
+#pragma unroll
+        for (int j = 0; j < kInlineSeqs; ++j) {
+            if (p.Hkv * s0 <= g0 && g0 < p.Hkv * (s0 + tl[j])) {
+                found = lane * per + j;
+                fbase = p.Hkv * s0;
+            }
+            s0 += tl[j];
+        }
+        const int src = __builtin_ctzll(__builtin_amdgcn_ballot_w64(found >= 0));
+        rec = PlanRecord{__shfl(found, src), g0, g1, __shfl(fbase, src)};
+        if (lane == 0)
+            p.plan_rec[w] = rec;  // for the merge launch
+    } else {
+        if (w >= p.plan_meta[0])
+            return;
+        rec = p.plan_rec[w];
+    }
     const bool head_ok = col < p.r;
 
     float score_scale0 = p.score_scale;
@@ -524,7 +572,7 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
     int b = rec.b;
     int g = rec.g0;
     int n = ctx_tiles(p.context_lens, b, p.max_ctx);
-    int base = p.Hkv * p.plan_S[b];
+    int base = rec.base;
     while (g < rec.g1) {
         if (g >= base + p.Hkv * n) {
             base += p.Hkv * n;
@@ -562,7 +610,7 @@ __global__ __launch_bounds__(64) void merge_runs_kernel(DecodeParams p)
     const int n = ctx_tiles(p.context_lens, b, p.max_ctx);
     if (n == 0)
         return;
-    const int base = p.Hkv * p.plan_S[b];
+    const int base = rk.base;
     const int h = (rk.g0 - base) / n;
     const int us = base + h * n, ue = us + n;
     if (us == rk.g0)
