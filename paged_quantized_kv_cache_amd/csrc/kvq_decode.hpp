@@ -316,7 +316,8 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
             if (lane >= o)
                 incl += y;
         }
-        const int T = p.Hkv * __shfl(incl, 63);
+        // (readfirstlane: the values are wave-uniform; keep them scalar)
+        const int T = p.Hkv * __builtin_amdgcn_readfirstlane(__shfl(incl, 63));
         const int W = min(p.W, T);
         if (w == 0 && lane == 0)
             p.plan_meta[0] = W;  // runs in use, for the merge launch
@@ -334,7 +335,8 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
             s0 += tl[j];
         }
         const int src = __builtin_ctzll(__builtin_amdgcn_ballot_w64(found >= 0));
-        rec = PlanRecord{__shfl(found, src), g0, g1, __shfl(fbase, src)};
+        rec = PlanRecord{__builtin_amdgcn_readlane(found, src), g0, g1,
+                         __builtin_amdgcn_readlane(fbase, src)};
         if (lane == 0)
             p.plan_rec[w] = rec;  // for the merge launch
     } else {
