@@ -263,7 +263,7 @@ def main(argv=None) -> int:
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "traffic": traffic,
-            "kernel": "kvq_paged_decode call: paged_decode_kernel + merge_splits_kernel (%s)"
+            "kernel": "kvq_paged_decode call: paged_decode_kernel + merge_runs_kernel (%s)"
                       % ("int8" if "int8" in fmts else fmts[0]),
             "algorithmic_bytes_per_launch": int(dom_bytes),
             "avg_launch_ms": round(dom_ms, 5),

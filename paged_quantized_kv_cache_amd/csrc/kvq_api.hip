@@ -83,10 +83,15 @@ kvq_status launch_status()
 
 // ---------------------------------------------------------------- run plan
 // split_tokens == 0: balanced runs, one per wavefront the GPU holds at once
-// (compute units x resident wavefronts per CU for the kernel instance), at
-// most one run per 4 tiles of the largest possible batch.  split_tokens > 0:
-// one run per span; the launch covers the largest possible count.
+// (compute units x resident wavefronts per CU for the kernel instance, at
+// most three per SIMD), at most one run per 4 tiles of the largest possible
+// batch.  Past three waves per SIMD the loop is already fed from HBM; more
+// runs only add partial results to merge and per-run set-up (measured: a
+// fourth wave per SIMD was 1-5% slower on long-context batches).
+// split_tokens > 0: one run per span; the launch covers the largest
+// possible count.
 constexpr int kMaxWavesPerCU = 32;  // hardware bound used for workspace sizing
+constexpr int kRunWavesPerCU = 12;  // 3 per SIMD
 
 bool valid_split(int32_t split_tokens)
 {
@@ -173,7 +178,7 @@ int waves_per_cu()
                 &n, reinterpret_cast<const void *>(&paged_decode_kernel<FMT, D, BS, NG>), 64,
                 0) != hipSuccess || n <= 0)
             n = 4;
-        v = std::min(n, kMaxWavesPerCU);
+        v = std::min(n, kRunWavesPerCU);
         cache[dev].store(v, std::memory_order_relaxed);
     }
     return v;

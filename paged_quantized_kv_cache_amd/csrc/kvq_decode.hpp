@@ -385,6 +385,21 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
                     qop[s] = f16x4{0, 0, 0, 0};
             }
         }
+        // INT8 K enters the MFMA as c + 1152 (no subtraction per code); the
+        // score of group j is corrected by 1152 * sum of q over the group.
+        float qbias[NG];
+        if constexpr (FMT == FMT_INT8) {
+#pragma unroll
+            for (int j = 0; j < NG; ++j) {
+                float sum = 0.0f;
+#pragma unroll
+                for (int s = j * (KS / NG); s < (j + 1) * (KS / NG); ++s)
+                    sum += ((float)qop[s][0] + (float)qop[s][1]) + ((float)qop[s][2] + (float)qop[s][3]);
+                sum += __shfl_xor(sum, 16);
+                sum += __shfl_xor(sum, 32);
+                qbias[j] = 1152.0f * sum;
+            }
+        }
         float score_scale = score_scale0;
         float out_scale = 1.0f;
         if constexpr (FMT == FMT_FP8) {
@@ -420,7 +435,7 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
             for (int s = 0; s < KS; ++s) {
                 f16x4 a;
                 if constexpr (FMT == FMT_INT8) {
-                    a = int8x4_to_f16x4(cur.k[s]);
+                    a = int8x4_to_f16x4_biased(cur.k[s]);
                 } else if constexpr (FMT == FMT_FP8) {
                     a = fp8x4_to_f16x4_scaled(cur.k[s]);
                 } else {
@@ -436,9 +451,9 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
             for (int v = 0; v < 4; ++v) {
                 float acc;
                 if constexpr (FMT == FMT_INT8) {
-                    acc = sacc[0][v] * sk[v][0];
+                    acc = (sacc[0][v] - qbias[0]) * sk[v][0];
                     if constexpr (NG == 2)
-                        acc += sacc[1][v] * sk[v][1];
+                        acc += (sacc[1][v] - qbias[1]) * sk[v][1];
                 } else {
                     acc = sacc[0][v];
                 }

@@ -62,6 +62,18 @@ __device__ __forceinline__ f16x4 int8x4_to_f16x4(uint32_t w)
     return f16x4{a.x, a.y, b.x, b.y};
 }
 
+// Four INT8 codes -> 4 exact fp16 holding c + 1152 (the bias is removed
+// after the dot product, where it costs one fused multiply-add per token).
+__device__ __forceinline__ f16x4 int8x4_to_f16x4_biased(uint32_t w)
+{
+    const uint32_t u = w ^ 0x80808080u;
+    const uint32_t lo = byte_perm(0x64646464u, u, 0x04010400u);
+    const uint32_t hi = byte_perm(0x64646464u, u, 0x04030402u);
+    const f16x2 a = bit_cast<f16x2>(lo);
+    const f16x2 b = bit_cast<f16x2>(hi);
+    return f16x4{a.x, a.y, b.x, b.y};
+}
+
 // Four E4M3 bytes -> 4 fp16 holding value * 2^-8 exactly.
 __device__ __forceinline__ f16x4 fp8x4_to_f16x4_scaled(uint32_t w)
 {
