@@ -33,8 +33,9 @@
  *
  * Pool layout (one layer; the caller keeps one set of pools per layer):
  *   k_pool, v_pool  [num_blocks][Hkv][tile], one tile of block_size * head_dim
- *   elements (EB bytes each: INT8 = int8 codes and FP8 = E4M3 bytes, EB = 1;
- *   FP16 = IEEE half, EB = 2) per (block, KV head).  Inside a tile, element
+ *   elements (EB bytes each: INT8 = codes in excess-128 form, byte = code +
+ *   128, and FP8 = E4M3 bytes, EB = 1; FP16 = IEEE half, EB = 2) per (block,
+ *   KV head).  Inside a tile, element
  *   (token t, dim d) sits at byte
  *     K:  ((d*EB/64) * block_size + t) * 64 + (d*EB) % 64
  *         (rows of 64 bytes: 64 one-byte dims or 32 fp16 dims of one token)
@@ -96,7 +97,8 @@ KVQ_API int32_t kvq_version(void);
  *                   elements): a = max |x|; s = fl32(a / 127);
  *                   code = clamp(round_half_even(fl32(x / s)), -127, 127);
  *                   a == 0 stores s = 0 and zero codes.  Codes go to the
- *                   pools, s to k_scale / v_scale (written).
+ *                   pools as bytes code + 128, s to k_scale / v_scale
+ *                   (written).
  *                 KVQ_FP8_E4M3: code = E4M3(fl32(x / S[h])) rounding to
  *                   nearest-even and saturating to +-448; S = k_scale /
  *                   v_scale [num_kv_heads] (read only).

@@ -256,24 +256,17 @@ __device__ __forceinline__ void load_codes(const DecodeParams &p, TileData<FMT, 
     }
 }
 
-// Loads one 16-token tile.  Codes of private blocks are read once per step,
-// so they use nontemporal loads that do not displace reusable lines; blocks
-// the caller marks as shared (several sequences read them in the same step)
-// use ordinary loads so that later readers can hit in L2 / the last-level
-// cache.
-template <int FMT, int D, int BS, int NG>
+// Loads one 16-token tile.  kNT selects nontemporal loads (see the window
+// walk in the decode kernel for when).
+template <int FMT, int D, int BS, int NG, bool kNT>
 __device__ __forceinline__ void load_tile(const DecodeParams &p, TileData<FMT, D> &t,
-                                          int phys, bool shared, int h, int toff, int col,
-                                          int grp)
+                                          int phys, int h, int toff, int col, int grp)
 {
     constexpr int EB = TileData<FMT, D>::EB;
     const int64_t tile = (int64_t)phys * p.Hkv + h;
     const uint8_t *kb = p.k_pool + tile * (BS * D * EB);
     const uint8_t *vb = p.v_pool + tile * (BS * D * EB);
-    if (shared)
-        load_codes<FMT, D, BS, NG, false>(p, t, kb, vb, toff, col, grp);
-    else
-        load_codes<FMT, D, BS, NG, true>(p, t, kb, vb, toff, col, grp);
+    load_codes<FMT, D, BS, NG, kNT>(p, t, kb, vb, toff, col, grp);
     if constexpr (FMT == FMT_INT8) {
         const int e = col % (8 * NG);
         const float *arr = e < 4 * NG ? p.k_scale : p.v_scale;
@@ -385,8 +378,10 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
                     qop[s] = f16x4{0, 0, 0, 0};
             }
         }
-        // INT8 K enters the MFMA as c + 1152 (no subtraction per code); the
-        // score of group j is corrected by 1152 * sum of q over the group.
+        // INT8 codes enter both MFMAs as c + 1152 (no subtraction per code).
+        // The score of group j is corrected by 1152 * (sum of q over the
+        // group); the output by 1152 * (sum of the P^T operand entries of the
+        // group), accumulated in csum with the same rescales as o.
         float qbias[NG];
         if constexpr (FMT == FMT_INT8) {
 #pragma unroll
@@ -397,7 +392,7 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
                     sum += ((float)qop[s][0] + (float)qop[s][1]) + ((float)qop[s][2] + (float)qop[s][3]);
                 sum += __shfl_xor(sum, 16);
                 sum += __shfl_xor(sum, 32);
-                qbias[j] = 1152.0f * sum;
+                qbias[j] = kInt8Bias * sum;
             }
         }
         float score_scale = score_scale0;
@@ -405,6 +400,16 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
         if constexpr (FMT == FMT_FP8) {
             score_scale *= 256.0f * p.k_scale[h];
             out_scale = 256.0f * p.v_scale[h];
+        }
+        // INT8: this lane's scale entry (see TileData) is token lane_tok of
+        // the tile; K entries carry the score scale, so the scores need no
+        // further multiply.  Entries of tokens past t_end become 0.
+        float lane_fac = 1.0f;
+        int lane_tok = 0;
+        if constexpr (FMT == FMT_INT8) {
+            const int e = col % (8 * NG);
+            lane_fac = e < 4 * NG ? score_scale : 1.0f;
+            lane_tok = 4 * grp + (e % (4 * NG)) / NG;
         }
 
         // o[tau][v]: output dim 64 (tau / 4) + 16 grp + 4 v + tau % 4, head col
@@ -414,16 +419,21 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
             o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
         float m = -INFINITY;
         float l = 0.0f;
+        float csum[NG];
+#pragma unroll
+        for (int j = 0; j < NG; ++j)
+            csum[j] = 0.0f;
 
         // One tile of 16 tokens starting at logical token ts, data in `cur`.
         auto process = [&](const TileData<FMT, D> &cur, const int ts) {
             // ---- this lane's scales: sk[v][j], sv[v][j] of tokens 4 grp + v
             float sk[4][NG], sv[4][NG];
             if constexpr (FMT == FMT_INT8) {
+                const float sc = (ts + lane_tok < t_end) ? cur.sc * lane_fac : 0.0f;
                 static_for<0, 4 * NG>([&](auto I) {
                     constexpr int i = decltype(I)::value;
-                    sk[i / NG][i % NG] = row_bcast<i>(cur.sc);
-                    sv[i / NG][i % NG] = row_bcast<4 * NG + i>(cur.sc);
+                    sk[i / NG][i % NG] = row_bcast<i>(sc);
+                    sv[i / NG][i % NG] = row_bcast<4 * NG + i>(sc);
                 });
             }
             // ---- S^T = K Q^T, one accumulator per INT8 group
@@ -455,9 +465,9 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
                     if constexpr (NG == 2)
                         acc += (sacc[1][v] - qbias[1]) * sk[v][1];
                 } else {
-                    acc = sacc[0][v];
+                    acc = sacc[0][v] * score_scale;
                 }
-                z[v] = (tok0 + v < t_end) ? acc * score_scale : -INFINITY;
+                z[v] = (tok0 + v < t_end) ? acc : -INFINITY;
             }
             // ---- online softmax
             float mt = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
@@ -470,6 +480,9 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
 #pragma unroll
                 for (int i = 0; i < DT; ++i)
                     o[i] *= alpha;
+#pragma unroll
+                for (int j = 0; j < NG; ++j)
+                    csum[j] *= alpha;
                 m = mn;
             }
             float pr[4];
@@ -478,14 +491,18 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
                 pr[v] = __builtin_amdgcn_exp2f(z[v] - m);
                 l += pr[v];
             }
-            // ---- P^T operands (V group scales folded in for INT8)
+            // ---- P^T operands (V group scales folded in for INT8; masked
+            // tokens have pr = 0 and a zeroed scale)
             f16x4 pop[NG];
             if constexpr (FMT == FMT_INT8) {
+                const f16x2 ones = {(f16)1.0f, (f16)1.0f};
 #pragma unroll
                 for (int j = 0; j < NG; ++j) {
 #pragma unroll
                     for (int v = 0; v < 4; ++v)
-                        pop[j][v] = (f16)((tok0 + v < t_end) ? pr[v] * sv[v][j] : 0.0f);
+                        pop[j][v] = (f16)(pr[v] * sv[v][j]);
+                    csum[j] = __builtin_amdgcn_fdot2(f16x2{pop[j][0], pop[j][1]}, ones, csum[j], false);
+                    csum[j] = __builtin_amdgcn_fdot2(f16x2{pop[j][2], pop[j][3]}, ones, csum[j], false);
                 }
             } else {
 #pragma unroll
@@ -493,64 +510,123 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
                     pop[0][v] = (f16)pr[v];
             }
             // ---- O^T += V^T P^T; d-tile tau covers dims 64 (tau/4) + 4 m + tau%4
-            const bool partial = ts + 16 > t_end;
+            // fp16: stale slots past t_end may hold non-finite values, which
+            // a zero P entry does not cancel; the lane's V dwords hold tokens
+            // (0, 1) or (2, 3) of its quad and are masked per token.
+            uint32_t vmask01 = ~0u, vmask23 = ~0u;
+            if constexpr (FMT == FMT_FP16) {
+                const int nv = t_end - tok0;  // valid tokens of this lane's quad (if < 4)
+                vmask01 = nv >= 2 ? ~0u : (nv == 1 ? 0xffffu : 0u);
+                vmask23 = nv >= 4 ? ~0u : (nv == 3 ? 0xffffu : 0u);
+            }
 #pragma unroll
             for (int tau = 0; tau < DT; ++tau) {
                 const int g4 = tau >> 2, i = tau & 3;
                 f16x4 a;
                 if constexpr (FMT == FMT_INT8) {
-                    a = int8x4_to_f16x4(cur.v[4 * g4 + i]);
+                    a = int8x4_to_f16x4_biased(cur.v[4 * g4 + i]);
                 } else if constexpr (FMT == FMT_FP8) {
                     a = fp8x4_to_f16x4_scaled(cur.v[4 * g4 + i]);
                 } else {
                     // fp16 micro-tiles hold 2 dims x 4 tokens: part i/2 of quad g4
                     const int x = 2 * g4 + (i >> 1), wd = 2 * (i & 1);
-                    a = f16x4_from_u2(cur.v[4 * x + wd], cur.v[4 * x + wd + 1]);
-                    if (partial) {  // stale fp16 slots may hold non-finite values
-#pragma unroll
-                        for (int v = 0; v < 4; ++v)
-                            if (tok0 + v >= t_end)
-                                a[v] = (f16)0.0f;
-                    }
+                    a = f16x4_from_u2(cur.v[4 * x + wd] & vmask01, cur.v[4 * x + wd + 1] & vmask23);
                 }
                 const int gi = (FMT == FMT_INT8 && NG == 2) ? (64 * g4) / G : 0;
                 o[tau] = __builtin_amdgcn_mfma_f32_16x16x16f16(a, pop[gi], o[tau], 0, 0, 0);
             }
         };
 
-        // ---- walk the run in windows of up to 64 blocks (block ids one per
-        // lane); inside a window, ping-pong over two tile buffers: tile i+1's
-        // loads are in flight while tile i is computed.  Loads are issued
-        // unconditionally (past the end they repeat the last tile) so the
-        // wait counts stay static.
+        // ---- walk tiles [t0, t1) with two tile buffers: tile i+1's loads
+        // are in flight while tile i is computed.  Loads are issued
+        // unconditionally (past t1 they repeat the last tile), so the wait
+        // before a tile's compute leaves the next tile's loads in flight.
+        //
+        // Block ids come from 64-entry windows of the table row (one entry
+        // per lane, read with readlane), aligned to 64-block boundaries of
+        // the sequence.  Three window registers rotate: the current window,
+        // the next one (read by the loads that run ahead), and the one after,
+        // whose load is issued a whole window before it is needed, so the
+        // walk never waits on the table.
+        //
+        // Cache policy, one per piece (a per-tile choice would put the loads
+        // under a branch, and the wait would then have to cover every load
+        // issued): codes of private blocks are read once per step, so they
+        // use nontemporal loads, which do not displace reusable lines; blocks
+        // the caller marks as shared are read by several sequences in the
+        // same step and use ordinary loads, so that later readers hit in L2 /
+        // the last-level cache.  Shared blocks are normally a prefix of the
+        // sequence: the leading windows (among the three first loaded) that
+        // hold a shared block are walked with ordinary loads, the rest with
+        // nontemporal ones.
         const int32_t *bt = p.block_tables + (int64_t)b * p.max_blocks;
-        for (int c0 = t0; c0 < t1; c0 += WIN) {
-            const int c1 = min(t1, c0 + WIN);
-            const int blk0 = (16 * c0) / BS;
-            const int blk_last = (16 * c1 - 1) / BS;
-            const int win = (blk0 + lane <= blk_last) ? bt[blk0 + lane] : 0;
-            const int ntiles = c1 - c0;
-            auto ld = [&](TileData<FMT, D> &buf, int i) {
-                i = c0 + min(i, ntiles - 1);
-                const int e = __builtin_amdgcn_readlane(win, (16 * i) / BS - blk0);
-                const int id = min(max(e & kBlockIdMask, 0), p.num_blocks - 1);  // stay in the pool
-                load_tile<FMT, D, BS, NG>(p, buf, id, (e & kSharedBlock) != 0, h, (16 * i) % BS,
-                                          col, grp);
-            };
+        constexpr int TPB = BS / 16;                // tiles per block
+        const int blk_last = (16 * t1 - 1) / BS;    // last block of the piece
+        // (entries past the piece repeat its last block: never used, and the
+        // load stays unconditional so no wait is needed until a use)
+        auto load_win = [&](int wi) -> int { return bt[min(64 * wi + lane, blk_last)]; };
+        int wi = t0 / (64 * TPB);   // window of the tile being processed
+        int win_a = load_win(wi), win_b = load_win(wi + 1), win_c = load_win(wi + 2);
+        auto ld = [&](TileData<FMT, D> &buf, int i, auto nt_tag) {
+            const int blk = i / TPB;
+            const int ea = __builtin_amdgcn_readlane(win_a, blk % 64);
+            const int eb = __builtin_amdgcn_readlane(win_b, blk % 64);
+            const int e = blk / 64 == wi ? ea : eb;
+            const int id = min(max(e & kBlockIdMask, 0), p.num_blocks - 1);  // stay in the pool
+            load_tile<FMT, D, BS, NG, decltype(nt_tag)::value>(p, buf, id, h, (16 * i) % BS, col,
+                                                              grp);
+        };
+        // walk tiles [tb, te) with one cache policy; tile tb lies in window
+        // wi or wi + 1
+        auto walk = [&](const int tb, const int te, auto nt_tag) {
+            auto ldw = [&](TileData<FMT, D> &buf, int i) { ld(buf, min(i, te - 1), nt_tag); };
             TileData<FMT, D> buf0, buf1;
-            ld(buf0, 0);
-            for (int it = 0; it < ntiles; it += 2) {
-                ld(buf1, it + 1);
-                process(buf0, 16 * (c0 + it));
-                ld(buf0, it + 2);
-                if (it + 1 < ntiles)
-                    process(buf1, 16 * (c0 + it + 1));
+            ldw(buf0, tb);
+            // loop invariant: tile i lies in window wi and its data is in buf0
+            for (int i = tb; i < te; i += 2) {
+                if (i / (64 * TPB) != wi) {  // entering the next window
+                    ++wi;
+                    win_a = win_b;
+                    win_b = win_c;
+                    win_c = load_win(wi + 2);
+                }
+                ldw(buf1, i + 1);
+                process(buf0, 16 * i);
+                ldw(buf0, i + 2);
+                if (i + 1 < te)
+                    process(buf1, 16 * (i + 1));
             }
+        };
+        auto has_shared = [&](int win) {
+            return __builtin_amdgcn_ballot_w64((win & kSharedBlock) != 0) != 0;
+        };
+        int ts = t0;  // end of the leading windows that hold shared blocks
+        if (has_shared(win_a)) {
+            ts = (wi + 1) * 64 * TPB;
+            if (has_shared(win_b))
+                ts = has_shared(win_c) ? t1 : (wi + 2) * 64 * TPB;
         }
+        ts = min(ts, t1);
+        if (ts > t0)
+            walk(t0, ts, std::false_type{});
+        if (ts < t1)
+            walk(ts, t1, std::true_type{});
 
         // ---- epilogue: lane holds dims 64 g4 + 16 grp + (0..15) of head col
         float lt = l + __shfl_xor(l, 16);
         lt += __shfl_xor(lt, 32);
+        if constexpr (FMT == FMT_INT8) {
+            // remove the code bias: o -= 1152 * (sum of P^T entries of the group)
+#pragma unroll
+            for (int j = 0; j < NG; ++j) {
+                float c = csum[j] + __shfl_xor(csum[j], 16);
+                c += __shfl_xor(c, 32);
+                csum[j] = kInt8Bias * c;
+            }
+#pragma unroll
+            for (int tau = 0; tau < DT; ++tau)
+                o[tau] -= csum[(64 * (tau >> 2)) / G];
+        }
         if (!head_ok)
             return;
         if (t0 == 0 && t1 == n) {  // the whole unit: final output

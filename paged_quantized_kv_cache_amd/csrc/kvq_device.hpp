@@ -2,9 +2,11 @@
 //
 // Element conversions used inside the attention loops.  They turn stored
 // codes into exact fp16 values for the MFMA operands:
-//   INT8 code c (|c| <= 127) -> fp16 c exactly, via the 1024 + byte trick
-//     (an fp16 with exponent field 25 has a unit step, so the bit pattern
-//     0x6400 | u is the number 1024 + u for a byte u).
+//   INT8 code c (|c| <= 127), stored as the excess-128 byte u = c + 128 ->
+//     fp16 holding c + 1152 exactly, via the 1024 + byte trick (an fp16 with
+//     exponent field 25 has a unit step, so the bit pattern 0x6400 | u is the
+//     number 1024 + u).  The constant 1152 is removed after the dot products,
+//     where it costs one term per row instead of one subtraction per code.
 //   E4M3 code -> fp16 equal to value * 2^-8 exactly: moving the 4 exponent
 //     and 3 mantissa bits into the fp16 fields keeps the mantissa and
 //     re-biases the exponent from 7 to 15 (subnormals land on fp16
@@ -50,25 +52,12 @@ __device__ __forceinline__ uint32_t byte_perm(uint32_t hi, uint32_t lo,
     return __builtin_amdgcn_perm(hi, lo, sel);
 }
 
-// Four INT8 codes (two's complement bytes of one dword) -> 4 exact fp16.
-__device__ __forceinline__ f16x4 int8x4_to_f16x4(uint32_t w)
-{
-    const uint32_t u = w ^ 0x80808080u;  // offset-binary: c + 128
-    const uint32_t lo = byte_perm(0x64646464u, u, 0x04010400u);
-    const uint32_t hi = byte_perm(0x64646464u, u, 0x04030402u);
-    const f16x2 bias = {(f16)1152.0f, (f16)1152.0f};
-    const f16x2 a = bit_cast<f16x2>(lo) - bias;  // (1024 + c + 128) - 1152
-    const f16x2 b = bit_cast<f16x2>(hi) - bias;
-    return f16x4{a.x, a.y, b.x, b.y};
-}
-
-// Four INT8 codes -> 4 exact fp16 holding c + 1152 (the bias is removed
-// after the dot product, where it costs one fused multiply-add per token).
+// Four excess-128 INT8 bytes (one dword) -> 4 exact fp16 holding c + 1152.
+constexpr float kInt8Bias = 1152.0f;
 __device__ __forceinline__ f16x4 int8x4_to_f16x4_biased(uint32_t w)
 {
-    const uint32_t u = w ^ 0x80808080u;
-    const uint32_t lo = byte_perm(0x64646464u, u, 0x04010400u);
-    const uint32_t hi = byte_perm(0x64646464u, u, 0x04030402u);
+    const uint32_t lo = byte_perm(0x64646464u, w, 0x04010400u);  // 0x64 | byte 0, 0x64 | byte 1
+    const uint32_t hi = byte_perm(0x64646464u, w, 0x04030402u);
     const f16x2 a = bit_cast<f16x2>(lo);
     const f16x2 b = bit_cast<f16x2>(hi);
     return f16x4{a.x, a.y, b.x, b.y};

@@ -7,7 +7,9 @@
 // One wavefront per (token, KV head): lanes 0..31 take K, lanes 32..63 take V,
 // each lane D/32 consecutive elements of the head.  A group of G elements is
 // spread over G/(D/32) neighbouring lanes; its absmax is reduced across them
-// with xor shuffles, so the scale and the codes come out in one pass.  K codes
+// with xor shuffles, so the scale and the codes come out in one pass.  INT8
+// codes are stored as excess-128 bytes (c + 128), which the decode kernel
+// turns into fp16 with two byte permutes per four codes.  K codes
 // go to 64-byte token rows (one dword per lane), V codes to 4x4 micro-tiles
 // (the layouts the decode kernel reads, see k_offset / v_offset), scales to
 // the slot's entry of the scale arrays.
@@ -90,7 +92,7 @@ __global__ __launch_bounds__(64 * kWriteWaves) void cache_write_kernel(WritePara
                 q = __builtin_rintf(x[i] / s);  // round half to even
                 q = fminf(fmaxf(q, -127.0f), 127.0f);
             }
-            code[i] = (uint32_t)(int32_t)q & 0xffu;
+            code[i] = (uint32_t)((int32_t)q + 128);  // stored in excess-128 form
         }
         if ((lane & (LPG - 1)) == 0) {
             float *sc = is_v ? p.v_scale : p.k_scale;

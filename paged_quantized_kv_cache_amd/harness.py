@@ -27,17 +27,16 @@ class LayerPools:
     v_scale: Optional[torch.Tensor]
 
 
-def poison_(pools: LayerPools, seed: int = 1234) -> None:
+def poison_(pools: LayerPools) -> None:
     """Fill pools with values that would corrupt any result that read them:
-    NaN fp16 / NaN scales; INT8 codes at the extremes; E4M3 NaN bytes."""
-    g = torch.Generator(device=pools.k_pool.device)
-    g.manual_seed(seed)
+    NaN fp16 / NaN scales; INT8 bytes at the extremes (excess-128 bytes 0x00
+    and 0xFF, codes -128 and +127); E4M3 NaN bytes."""
     if pools.fmt == "fp16":
         pools.k_pool.fill_(float("nan"))
         pools.v_pool.fill_(float("nan"))
     elif pools.fmt == "int8":
-        pools.k_pool.fill_(-128)
-        pools.v_pool.fill_(127)
+        pools.k_pool.fill_(0x00)
+        pools.v_pool.fill_(0xFF)
         pools.k_scale.fill_(float("nan"))
         pools.v_scale.fill_(float("inf"))
     else:
@@ -179,9 +178,10 @@ class DecodeCase:
                 g = g.reshape(n, s.Hkv, s.D, eb).contiguous().cpu().numpy()
                 if eb == 2:
                     g = g.view(np.float16).reshape(n, s.Hkv, s.D)
+                elif p.fmt == "int8":   # excess-128 bytes -> signed codes
+                    g = (g.reshape(n, s.Hkv, s.D) ^ np.uint8(0x80)).view(np.int8)
                 else:
-                    g = g.reshape(n, s.Hkv, s.D).view(
-                        np.int8 if p.fmt == "int8" else np.uint8)
+                    g = g.reshape(n, s.Hkv, s.D).view(np.uint8)
                 item[name] = g
             if p.fmt == "int8":
                 item["k_scale"] = p.k_scale[blk, :, off, :].cpu().numpy()

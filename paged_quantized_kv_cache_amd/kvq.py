@@ -25,7 +25,8 @@ LIB_PATH = os.path.join(_HERE, "libkvq.so")
 
 KVQ_FP16, KVQ_INT8, KVQ_FP8_E4M3 = 0, 1, 2
 FORMATS = {"fp16": KVQ_FP16, "int8": KVQ_INT8, "fp8": KVQ_FP8_E4M3}
-POOL_DTYPES = {"fp16": torch.float16, "int8": torch.int8, "fp8": torch.uint8}
+# INT8 pools hold excess-128 bytes (code + 128), FP8 pools E4M3 bytes.
+POOL_DTYPES = {"fp16": torch.float16, "int8": torch.uint8, "fp8": torch.uint8}
 STATUS = {0: "KVQ_OK", -1: "KVQ_ERR_INVALID_ARG", -2: "KVQ_ERR_UNSUPPORTED",
           -3: "KVQ_ERR_WORKSPACE", -4: "KVQ_ERR_HIP"}
 EXPORTS = ("kvq_status_string", "kvq_version", "kvq_cache_write",
