@@ -15,7 +15,6 @@ once, plus q, out, table entries and lengths) over its event-timed duration.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -28,20 +27,17 @@ if ROOT not in sys.path:
 METRIC = "paged INT8 GQA decode-attn seq-steps/s + achieved HBM GB/s (% of MI355X peak)"
 HBM_PEAK_GBPS = 8000.0
 DEFAULT_WORKLOAD = "c3_gqa"
-KERNEL_SOURCES = ("kvq_decode.hpp", "kvq_device.hpp", "kvq_api.hip")
 
 
 def kernel_hash() -> str:
-    h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "paged_quantized_kv_cache_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
-    return h.hexdigest()[:16]
+    """Identity of the device code the counters were taken on."""
+    from paged_quantized_kv_cache_amd import build as B
+    return B.device_code_hash()
 
 
 def load_traffic(workload: str):
-    """HBM bytes per decode launch from committed rocprofv3 counter runs, if
-    they were taken on the current kernel source; else None."""
+    """HBM bytes per decode call from committed rocprofv3 counter runs, if
+    they were taken on the device code now built; else None."""
     path = os.path.join(ROOT, "profiles", "traffic_%s.json" % workload)
     if not os.path.exists(path):
         return None

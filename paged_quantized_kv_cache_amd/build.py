@@ -1,7 +1,9 @@
 """Build libkvq.so (hand-written HIP for gfx950) in-tree with hipcc."""
 from __future__ import annotations
 
+import hashlib
 import os
+import struct
 import subprocess
 import sys
 
@@ -39,6 +41,42 @@ def build(verbose: bool = False, extra=()) -> str:
     subprocess.run(cmd, check=True)
     os.replace(tmp, LIB)
     return LIB
+
+
+def _elf_sections(b: bytes, base: int = 0) -> dict:
+    """name -> (offset, size) of the sections of the 64-bit ELF at b[base:]."""
+    shoff, = struct.unpack_from("<Q", b, base + 0x28)
+    shentsize, shnum, shstrndx = struct.unpack_from("<HHH", b, base + 0x3A)
+    hdrs = [struct.unpack_from("<IIQQQQIIQQ", b, base + shoff + i * shentsize)
+            for i in range(shnum)]
+    names = base + hdrs[shstrndx][4]
+    out = {}
+    for h in hdrs:
+        end = b.index(b"\0", names + h[0])
+        out[b[names + h[0]:end].decode()] = (base + h[4], h[5])
+    return out
+
+
+def device_code_hash(path: str = LIB) -> str:
+    """Hash of the gfx950 machine code (.text of the device code object in
+    the library's offload bundle).  Comments or host-side edits leave it
+    unchanged; any change to a kernel's instructions changes it."""
+    with open(path, "rb") as f:
+        b = f.read()
+    off, size = _elf_sections(b)[".hip_fatbin"]
+    fb = b[off:off + size]
+    if not fb.startswith(b"__CLANG_OFFLOAD_BUNDLE__"):
+        raise ValueError("no offload bundle in %s" % path)
+    n, = struct.unpack_from("<Q", fb, 24)
+    pos, h = 32, hashlib.sha256()
+    for _ in range(n):
+        eo, _es, tl = struct.unpack_from("<QQQ", fb, pos)
+        triple = fb[pos + 24:pos + 24 + tl].decode()
+        pos += 24 + tl
+        if "gfx950" in triple:
+            to, ts = _elf_sections(fb, eo)[".text"]
+            h.update(fb[to:to + ts])
+    return h.hexdigest()[:16]
 
 
 def stale() -> bool:

@@ -6,10 +6,11 @@
 // dequantization fused into attention):
 //     out[b][g] = sum_t softmax_t(sm * q[b][g] . Khat[t]) Vhat[t]
 //
-// Work decomposition.  One wavefront owns one (sequence b, KV head h, split)
-// item: a span of `span` logical tokens (all of them when the sequence is not
-// split).  It walks the span in tiles of 16 tokens (a 16-token block, or half
-// of a 32-token block), gathering each tile through the block table.
+// Work decomposition (details at PlanRecord).  The batch's 16-token tiles,
+// unit by unit ((sequence b, KV head h) units), are dealt in contiguous runs,
+// one per wavefront.  A wavefront walks its run's tiles, gathering each
+// through the block table (a 16-token block, or half of a 32-token block),
+// with the next tile's loads in flight while the current one is computed.
 //
 // Both contractions run on 16x16x16 fp16 MFMA with the head_dim / token axes
 // laid out so that no data moves between lanes except for softmax maxima.
@@ -24,16 +25,16 @@
 //       micro-tile layout stores next to each other.
 // The head_dim order inside an MFMA k-step is a permutation chosen so that
 // each lane's K bytes are contiguous; q is loaded with the same permutation.
-// Codes are converted to exact fp16 (INT8 c, or E4M3 value * 2^-8) right
-// before the MFMA; K group scales multiply the per-group partial dot products
-// (one accumulator per group); V group scales are folded into P (rounded to
-// fp16 once) so the token sum stays a single MFMA chain.
+// Codes are converted to exact fp16 (INT8 c + 1152, or E4M3 value * 2^-8)
+// right before the MFMA; K group scales multiply the per-group partial dot
+// products (one accumulator per group); V group scales are folded into P
+// (rounded to fp16 once) so the token sum stays a single MFMA chain.
 //
 // Online softmax in base 2 (the log2(e) factor rides on the score scale), with
 // a rescale of the running output only when some head's maximum grows.
-// Splits of one (b, h) write (m, l, acc) partials that a second, small launch
-// merges with a log-sum-exp; a sequence that fits one split is finished by
-// the split kernel itself.
+// Pieces of a unit cut by run boundaries write (m, l, acc) partials that a
+// second, small launch merges with a log-sum-exp; a unit that lies inside one
+// run is finished by the decode kernel itself.
 #pragma once
 
 #include "kvq_device.hpp"
