@@ -11,8 +11,10 @@ shares no code with the HIP library.
 Sources (web pages, cited by title and section):
   * "KV Cache优化实战：大模型推理显存占用与加速方案详解" (0539edu.com):
     s1.1 decode with a KV cache, s1.2 byte formula, s2.1 GQA, s2.3 INT8
-    absmax / per-group / FP8 quantization, s3.1 memory estimator, s3.3
-    per_group granularity with group 128 or 64.
+    absmax / per-channel / per-group / FP8 quantization, s3.1 memory
+    estimator, s3.3 per_channel / per_group / per_token granularity with
+    group 128 or 64.
+  * xpshop.cn article 312, s3: FP8 KV cache as ``fp8_e5m2``.
 """
 from __future__ import annotations
 
@@ -66,6 +68,19 @@ def _L():
             lib.orc_fp8_quantize_rows.restype = i32
             lib.orc_fp8_quantize_rows.argtypes = [P, i64, i32, i32, P, P]
             lib.orc_fp8_dequantize_rows.argtypes = [P, i64, i32, i32, P, P]
+            lib.orc_e5m2_decode.restype = ctypes.c_double
+            lib.orc_e5m2_decode.argtypes = [ctypes.c_uint8]
+            lib.orc_e5m2_encode.restype = ctypes.c_uint8
+            lib.orc_e5m2_encode.argtypes = [ctypes.c_float]
+            lib.orc_fp8_quantize_rows_fmt.restype = i32
+            lib.orc_fp8_quantize_rows_fmt.argtypes = [P, i64, i32, i32, P, i32, P]
+            lib.orc_fp8_dequantize_rows_fmt.argtypes = [P, i64, i32, i32, P, i32, P]
+            lib.orc_fp8_quantize_groups.restype = i32
+            lib.orc_fp8_quantize_groups.argtypes = [P, i64, i32, i32, i32, P, P]
+            lib.orc_fp8_dequantize_groups.argtypes = [P, P, i64, i32, i32, i32, P]
+            lib.orc_int8_quantize_channels.restype = i32
+            lib.orc_int8_quantize_channels.argtypes = [P, i64, i32, i32, P, P]
+            lib.orc_int8_dequantize_channels.argtypes = [P, i64, i32, i32, P, P]
             lib.orc_decode_attention.restype = i32
             lib.orc_decode_attention.argtypes = [P, P, P, P, i32, i32, i32,
                                                  i32, ctypes.c_double, P]
@@ -152,25 +167,97 @@ def e4m3_encode(y) -> np.ndarray:
                     np.uint8).reshape(y.shape)
 
 
-def fp8_quantize(x, scale) -> np.ndarray:
-    """x: [T][Hkv][d] fp16; scale: [Hkv] fp32.  code = e4m3(fl32(x / S[h]))."""
+FP8_FORMATS = {"e4m3": 0, "e5m2": 1}
+
+
+def e5m2_decode(codes) -> np.ndarray:
+    codes = np.ascontiguousarray(codes, np.uint8)
+    lib = _L()
+    return np.array([lib.orc_e5m2_decode(int(c)) for c in codes.ravel()],
+                    np.float64).reshape(codes.shape)
+
+
+def e5m2_encode(y) -> np.ndarray:
+    y = np.ascontiguousarray(y, np.float32)
+    lib = _L()
+    return np.array([lib.orc_e5m2_encode(float(v)) for v in y.ravel()],
+                    np.uint8).reshape(y.shape)
+
+
+def fp8_quantize(x, scale, fmt: str = "e4m3") -> np.ndarray:
+    """x: [T][Hkv][d] fp16; scale: [Hkv] fp32 (static per head).
+    code = fp8(fl32(x / S[h]))."""
     bits = _f16_bits(x)
     T, Hkv, d = bits.shape
     S = np.ascontiguousarray(scale, np.float32)
     assert S.shape == (Hkv,)
     codes = np.empty(bits.shape, np.uint8)
-    rc = _L().orc_fp8_quantize_rows(_ptr(bits), T, Hkv, d, _ptr(S), _ptr(codes))
+    rc = _L().orc_fp8_quantize_rows_fmt(_ptr(bits), T, Hkv, d, _ptr(S),
+                                        FP8_FORMATS[fmt], _ptr(codes))
     if rc != 0:
         raise ValueError("oracle: non-finite input")
     return codes
 
 
-def fp8_dequantize(codes: np.ndarray, scale) -> np.ndarray:
+def fp8_dequantize(codes: np.ndarray, scale, fmt: str = "e4m3") -> np.ndarray:
     codes = np.ascontiguousarray(codes, np.uint8)
     T, Hkv, d = codes.shape
     S = np.ascontiguousarray(scale, np.float32)
     out = np.empty(codes.shape, np.float64)
-    _L().orc_fp8_dequantize_rows(_ptr(codes), T, Hkv, d, _ptr(S), _ptr(out))
+    _L().orc_fp8_dequantize_rows_fmt(_ptr(codes), T, Hkv, d, _ptr(S),
+                                     FP8_FORMATS[fmt], _ptr(out))
+    return out
+
+
+def fp8_quantize_groups(x, group_size: int, fmt: str = "e4m3"):
+    """Dynamic per-group FP8 along the last axis.
+
+    Returns ``(codes uint8 same shape, scales float32 [..., d/G])``."""
+    bits = _f16_bits(x)
+    d = bits.shape[-1]
+    if group_size <= 0 or d % group_size:
+        raise ValueError("group_size must divide the last dimension")
+    rows = bits.size // d
+    codes = np.empty(bits.shape, np.uint8)
+    scales = np.empty(bits.shape[:-1] + (d // group_size,), np.float32)
+    rc = _L().orc_fp8_quantize_groups(_ptr(bits), rows, d, group_size,
+                                      FP8_FORMATS[fmt], _ptr(codes), _ptr(scales))
+    if rc != 0:
+        raise ValueError("oracle: non-finite input or bad group size (%d)" % rc)
+    return codes, scales
+
+
+def fp8_dequantize_groups(codes: np.ndarray, scales: np.ndarray,
+                          fmt: str = "e4m3") -> np.ndarray:
+    codes = np.ascontiguousarray(codes, np.uint8)
+    scales = np.ascontiguousarray(scales, np.float32)
+    d = codes.shape[-1]
+    G = d // scales.shape[-1]
+    out = np.empty(codes.shape, np.float64)
+    _L().orc_fp8_dequantize_groups(_ptr(codes), _ptr(scales), codes.size // d,
+                                   d, G, FP8_FORMATS[fmt], _ptr(out))
+    return out
+
+
+def int8_quantize_channels(x, scale) -> np.ndarray:
+    """x: [T][Hkv][d] fp16; scale: [Hkv][d] fp32 (static per channel)."""
+    bits = _f16_bits(x)
+    T, Hkv, d = bits.shape
+    S = np.ascontiguousarray(scale, np.float32)
+    assert S.shape == (Hkv, d)
+    codes = np.empty(bits.shape, np.int8)
+    rc = _L().orc_int8_quantize_channels(_ptr(bits), T, Hkv, d, _ptr(S), _ptr(codes))
+    if rc != 0:
+        raise ValueError("oracle: non-finite input")
+    return codes
+
+
+def int8_dequantize_channels(codes: np.ndarray, scale) -> np.ndarray:
+    codes = np.ascontiguousarray(codes, np.int8)
+    T, Hkv, d = codes.shape
+    S = np.ascontiguousarray(scale, np.float32)
+    out = np.empty(codes.shape, np.float64)
+    _L().orc_int8_dequantize_channels(_ptr(codes), T, Hkv, d, _ptr(S), _ptr(out))
     return out
 
 
@@ -219,9 +306,10 @@ def quantize_kv(x, fmt: str, group_size: int = 0, scale=None):
     if fmt == "int8":
         codes, sc = int8_quantize(x, group_size)
         return codes, sc, int8_dequantize(codes, sc)
-    if fmt == "fp8":
-        codes = fp8_quantize(x, scale)
-        return codes, None, fp8_dequantize(codes, scale)
+    if fmt in ("fp8", "e5m2"):
+        f = "e5m2" if fmt == "e5m2" else "e4m3"
+        codes = fp8_quantize(x, scale, f)
+        return codes, None, fp8_dequantize(codes, scale, f)
     if fmt == "fp16":
         bits = _f16_bits(x)
         return bits.copy(), None, f16_to_f64(bits)

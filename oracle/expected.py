@@ -14,26 +14,39 @@ from typing import List, Optional, Sequence
 
 import numpy as np
 
-from . import (decode_attention, fp8_dequantize, fp8_quantize, f16_to_f64,
-               int8_dequantize, int8_quantize)
+from . import (decode_attention, fp8_dequantize, fp8_dequantize_groups,
+               fp8_quantize, fp8_quantize_groups, f16_to_f64,
+               int8_dequantize, int8_dequantize_channels, int8_quantize,
+               int8_quantize_channels)
 
 
 @dataclass
 class Quantized:
     codes: np.ndarray            # [N][Hkv][D] int8 / uint8 / uint16 (fp16 bits)
-    scales: Optional[np.ndarray]  # INT8: [N][Hkv][D/G] fp32
+    scales: Optional[np.ndarray]  # per-group formats: [N][Hkv][D/G] fp32
     deq: np.ndarray              # [N][Hkv][D] fp64
 
 
 def quantize(x: np.ndarray, fmt: str, group_size: int = 0,
              static_scale: Optional[np.ndarray] = None) -> Quantized:
-    """x: fp16 ``[N][Hkv][D]`` (numpy float16)."""
+    """x: fp16 ``[N][Hkv][D]`` (numpy float16).
+
+    fmt "int8": group_size > 0 per-group absmax; 0 per-channel with
+    static_scale [Hkv][D].  fmt "fp8" (E4M3) / "e5m2": group_size 0 static
+    per-head static_scale [Hkv]; > 0 dynamic per-group scales."""
     if fmt == "int8":
+        if group_size == 0:
+            c = int8_quantize_channels(x, static_scale)
+            return Quantized(c, None, int8_dequantize_channels(c, static_scale))
         c, s = int8_quantize(x, group_size)
         return Quantized(c, s, int8_dequantize(c, s))
-    if fmt == "fp8":
-        c = fp8_quantize(x, static_scale)
-        return Quantized(c, None, fp8_dequantize(c, static_scale))
+    if fmt in ("fp8", "e5m2"):
+        f = "e5m2" if fmt == "e5m2" else "e4m3"
+        if group_size:
+            c, s = fp8_quantize_groups(x, group_size, f)
+            return Quantized(c, s, fp8_dequantize_groups(c, s, f))
+        c = fp8_quantize(x, static_scale, f)
+        return Quantized(c, None, fp8_dequantize(c, static_scale, f))
     if fmt == "fp16":
         bits = np.ascontiguousarray(x).view(np.uint16)
         return Quantized(bits.copy(), None, f16_to_f64(bits))

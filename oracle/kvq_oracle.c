@@ -32,6 +32,17 @@
  *    nearest, ties to even, and saturates to +-448; a negative value that
  *    rounds to zero keeps its sign (code 0x80).  The scale is a static fp32
  *    per KV head, applied as fl32(x / S).
+ *  - FP8 E5M2 (the kv_cache_dtype "fp8_e5m2" of xpshop.cn article 312 s3) is
+ *    the OCP E5M2 format (bias 15, 2 mantissa bits, infinities and NaNs);
+ *    encode rounds to nearest, ties to even, and saturates to +-57344.
+ *  - FP8 with dynamic scales (either format): per (token, head, group of G
+ *    consecutive elements), s = fl32(absmax / FP8_MAX), code =
+ *    fp8(fl32(x / s)); an all-zero group stores s = 0 and codes 0.  G =
+ *    head_dim is the per-token case.
+ *  - INT8 per-channel ("per_channel" granularity, [P3] s2.3, s3.3, s4.2):
+ *    one static fp32 scale per (KV head, channel), given as an input like the
+ *    FP8 static scale; code = clamp(rne(fl32(x / s_c)), -127, 127); a zero
+ *    scale gives code 0.
  *  - softmax scale defaults to 1/sqrt(head_dim); query head g reads KV head
  *    g / (Hq / Hkv) (contiguous grouping).
  *
@@ -194,10 +205,88 @@ ORC_API uint8_t orc_e4m3_encode(float yf)
     return (uint8_t)(sign | (efield << 3) | mfield);
 }
 
-/* x: [rows][Hkv][d] fp16 bits; S: [Hkv] static scales; codes same shape.
- * code = e4m3(fl32(x / S[h])). */
-ORC_API int orc_fp8_quantize_rows(const uint16_t *x, int64_t rows, int Hkv,
-                                  int d, const float *S, uint8_t *codes)
+/* ------------------------------------------------------------------ */
+/* FP8 E5M2 (OCP)                                                       */
+/* value(code) for exponent field e and mantissa m:                      */
+/*   e == 0  : m/4 * 2^-14  (subnormal)                                  */
+/*   e == 31 : infinity (m == 0) or NaN                                  */
+/*   else    : (1 + m/4) * 2^(e-15)                                      */
+/* ------------------------------------------------------------------ */
+ORC_API double orc_e5m2_decode(uint8_t c)
+{
+    int sign = c >> 7;
+    int e = (c >> 2) & 0x1f;
+    int m = c & 3;
+    double v;
+    if (e == 31) {
+        if (m)
+            return NAN;
+        v = INFINITY;
+    } else if (e == 0) {
+        v = ldexp((double)m, -16);
+    } else {
+        v = ldexp((double)(4 + m), e - 17);
+    }
+    return sign ? -v : v;
+}
+
+/* Round a finite fp32 value to E5M2: nearest representable, ties to the
+ * even mantissa, magnitudes beyond the largest finite value (57344)
+ * saturate. */
+ORC_API uint8_t orc_e5m2_encode(float yf)
+{
+    double y = (double)yf;
+    uint8_t sign = signbit(y) ? 0x80 : 0x00;
+    double a = fabs(y);
+    if (!(a < 57344.0))                 /* 1.75 * 2^15, largest finite */
+        return (uint8_t)(sign | 0x7b);
+    if (a == 0.0)
+        return sign;
+    int ex;
+    frexp(a, &ex);
+    int E = ex - 1;                     /* a in [2^E, 2^(E+1))          */
+    if (E < -14)
+        E = -14;                        /* below 2^-14: subnormal spacing */
+    double quantum = ldexp(1.0, E - 2); /* 2 fraction bits               */
+    double n = nearbyint(a / quantum);
+    double v = n * quantum;
+    if (v == 0.0)
+        return sign;
+    int e2;
+    frexp(v, &e2);
+    int E2 = e2 - 1;
+    int efield, mfield;
+    if (E2 < -14) {                     /* subnormal: v = m * 2^-16      */
+        efield = 0;
+        mfield = (int)(v / ldexp(1.0, -16));
+    } else {
+        efield = E2 + 15;
+        mfield = (int)(v / ldexp(1.0, E2 - 2)) - 4;
+    }
+    return (uint8_t)(sign | (efield << 2) | mfield);
+}
+
+/* fmt: 0 = E4M3, 1 = E5M2 */
+static double fp8_decode(uint8_t c, int fmt)
+{
+    return fmt ? orc_e5m2_decode(c) : orc_e4m3_decode(c);
+}
+
+static uint8_t fp8_encode(float y, int fmt)
+{
+    return fmt ? orc_e5m2_encode(y) : orc_e4m3_encode(y);
+}
+
+static float fp8_max(int fmt)
+{
+    return fmt ? 57344.0f : 448.0f;
+}
+
+/* Static per-head scale.  x: [rows][Hkv][d] fp16 bits; S: [Hkv]; codes same
+ * shape as x.  code = fp8(fl32(x / S[h])). */
+ORC_API int orc_fp8_quantize_rows_fmt(const uint16_t *x, int64_t rows, int Hkv,
+                                      int d, const float *S, int fmt,
+                                      uint8_t *codes)
 {
     int bad = 0;
 #pragma omp parallel for schedule(static) reduction(| : bad)
@@ -211,21 +300,130 @@ ORC_API int orc_fp8_quantize_rows(const uint16_t *x, int64_t rows, int Hkv,
                     continue;
                 }
                 float y = (float)xd / S[h];
-                codes[k] = orc_e4m3_encode(y);
+                codes[k] = fp8_encode(y, fmt);
             }
     return bad ? -1 : 0;
 }
 
-ORC_API void orc_fp8_dequantize_rows(const uint8_t *codes, int64_t rows,
-                                     int Hkv, int d, const float *S,
-                                     double *out)
+ORC_API int orc_fp8_quantize_rows(const uint16_t *x, int64_t rows, int Hkv,
+                                  int d, const float *S, uint8_t *codes)
+{
+    return orc_fp8_quantize_rows_fmt(x, rows, Hkv, d, S, 0, codes);
+}
+
+ORC_API void orc_fp8_dequantize_rows_fmt(const uint8_t *codes, int64_t rows,
+                                         int Hkv, int d, const float *S,
+                                         int fmt, double *out)
 {
 #pragma omp parallel for schedule(static)
     for (int64_t r = 0; r < rows; ++r)
         for (int h = 0; h < Hkv; ++h)
             for (int i = 0; i < d; ++i) {
                 int64_t k = (r * Hkv + h) * d + i;
-                out[k] = orc_e4m3_decode(codes[k]) * (double)S[h];
+                out[k] = fp8_decode(codes[k], fmt) * (double)S[h];
+            }
+}
+
+ORC_API void orc_fp8_dequantize_rows(const uint8_t *codes, int64_t rows,
+                                     int Hkv, int d, const float *S,
+                                     double *out)
+{
+    orc_fp8_dequantize_rows_fmt(codes, rows, Hkv, d, S, 0, out);
+}
+
+/* Dynamic per-group scale: rows of d elements, groups of G consecutive
+ * elements; s = fl32(absmax / FP8_MAX), code = fp8(fl32(x / s)); an
+ * all-zero group stores s = 0 and codes 0.  codes: [rows][d]; scales:
+ * [rows][d/G]. */
+ORC_API int orc_fp8_quantize_groups(const uint16_t *x, int64_t rows, int d,
+                                    int G, int fmt, uint8_t *codes,
+                                    float *scales)
+{
+    if (G <= 0 || d % G != 0)
+        return -2;
+    int ng = d / G;
+    int bad = 0;
+#pragma omp parallel for schedule(static) reduction(| : bad)
+    for (int64_t r = 0; r < rows; ++r)
+        for (int j = 0; j < ng; ++j) {
+            const uint16_t *xg = x + r * d + j * G;
+            float absmax = 0.0f;
+            for (int i = 0; i < G; ++i) {
+                double xd = orc_f16_to_f64(xg[i]);
+                if (!isfinite(xd))
+                    bad = 1;
+                else if (fabsf((float)xd) > absmax)
+                    absmax = fabsf((float)xd);
+            }
+            float s = absmax / fp8_max(fmt);          /* IEEE fp32 division */
+            scales[r * ng + j] = s;
+            for (int i = 0; i < G; ++i) {
+                if (s == 0.0f) {
+                    codes[r * d + j * G + i] = 0;
+                    continue;
+                }
+                float y = (float)orc_f16_to_f64(xg[i]) / s;
+                codes[r * d + j * G + i] = fp8_encode(y, fmt);
+            }
+        }
+    return bad ? -1 : 0;
+}
+
+ORC_API void orc_fp8_dequantize_groups(const uint8_t *codes,
+                                       const float *scales, int64_t rows,
+                                       int d, int G, int fmt, double *out)
+{
+    int ng = d / G;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r)
+        for (int i = 0; i < d; ++i)
+            out[r * d + i] = fp8_decode(codes[r * d + i], fmt) *
+                             (double)scales[r * ng + i / G];
+}
+
+/* ------------------------------------------------------------------ */
+/* INT8 per-channel, static scales ([P3] s2.3 per_channel)              */
+/* x: [rows][Hkv][d] fp16 bits; S: [Hkv][d]; codes same shape as x.      */
+/* ------------------------------------------------------------------ */
+ORC_API int orc_int8_quantize_channels(const uint16_t *x, int64_t rows,
+                                       int Hkv, int d, const float *S,
+                                       int8_t *codes)
+{
+    int bad = 0;
+#pragma omp parallel for schedule(static) reduction(| : bad)
+    for (int64_t r = 0; r < rows; ++r)
+        for (int h = 0; h < Hkv; ++h)
+            for (int i = 0; i < d; ++i) {
+                int64_t k = (r * Hkv + h) * d + i;
+                double xd = orc_f16_to_f64(x[k]);
+                float s = S[h * d + i];
+                if (!isfinite(xd)) {
+                    bad = 1;
+                    continue;
+                }
+                if (s == 0.0f) {
+                    codes[k] = 0;
+                    continue;
+                }
+                float y = (float)xd / s;              /* fp32, correctly rounded */
+                float q = rintf(y);                   /* nearest, ties to even   */
+                if (q > 127.0f) q = 127.0f;
+                if (q < -127.0f) q = -127.0f;
+                codes[k] = (int8_t)q;
+            }
+    return bad ? -1 : 0;
+}
+
+ORC_API void orc_int8_dequantize_channels(const int8_t *codes, int64_t rows,
+                                          int Hkv, int d, const float *S,
+                                          double *out)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r)
+        for (int h = 0; h < Hkv; ++h)
+            for (int i = 0; i < d; ++i) {
+                int64_t k = (r * Hkv + h) * d + i;
+                out[k] = (double)codes[k] * (double)S[h * d + i];
             }
 }
 
