@@ -57,6 +57,7 @@ def cpu_baseline(case, layer_inputs, spec, max_seqs: int, min_seconds: float = 1
 
     import oracle
     from oracle import expected as E
+    from paged_quantized_kv_cache_amd import kvq
 
     layers = [0] if spec.layers == 1 else list(range(spec.layers))
     nseq = min(max_seqs, spec.B)
@@ -74,7 +75,7 @@ def cpu_baseline(case, layer_inputs, spec, max_seqs: int, min_seconds: float = 1
         q = d.q[:nseq].cpu().numpy()
         fmt = spec.fmt_of_layer(layer)
         sk = sv = None
-        if fmt == "fp8":
+        if kvq.scale_mode(fmt, spec.G) in ("head", "channel"):   # static scales
             sk = case.pools[layer].k_scale.cpu().numpy()
             sv = case.pools[layer].v_scale.cpu().numpy()
         toks = [remap[case.layout.seq_tokens[b]] for b in seqs]

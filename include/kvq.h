@@ -12,11 +12,14 @@
  *     s2.2  paged cache: fixed-size physical blocks, a per-sequence block table
  *           mapping logical blocks to physical ones anywhere in the pool.
  *     s2.3  INT8 absmax symmetric quantization storing a scale, dequantized at
- *           run time; per-group scales (e.g. 128 elements per group); FP8.
- *     s3.3  per_group granularity, group size 128 or 64.
+ *           run time; per-channel scales; per-group scales (e.g. 128
+ *           elements per group); FP8.
+ *     s3.3  per_channel / per_group / per_token granularity, group size 128
+ *           or 64.
  *     s4.3  dequantization fused into the attention kernel instead of separate
  *           small kernels.
- *   xpshop.cn article 312, s3: 16- or 32-token blocks; FP8 KV cache.
+ *   xpshop.cn article 312, s3: 16- or 32-token blocks; FP8 KV cache
+ *     (kv_cache_dtype "fp8_e5m2").
  *
  * Conventions shared by every call
  *  - All buffers are device memory owned by the caller; the library never
@@ -27,15 +30,22 @@
  *  - The synchronous return value covers host-side argument checks and launch
  *    errors.  Device contents (block ids, slots, lengths) are trusted, except
  *    that cache writes skip slots outside the pool.
- *  - Supported: head_dim 64 or 128; block_size 16 or 32; INT8 group_size 64 or
- *    128 dividing head_dim; Hq / Hkv between 1 and 16; gfx950 only.
+ *  - Supported: head_dim 64 or 128; block_size 16 or 32; Hq / Hkv between 1
+ *    and 16; gfx950 only.  Scale granularity by dtype and group_size:
+ *      KVQ_INT8      group_size 64 / 128 (<= head_dim): per-group scales
+ *                    computed by the cache write (per token when group_size
+ *                    = head_dim); group_size 0: static per-channel scales.
+ *      KVQ_FP8_E4M3  group_size 0: static per-KV-head scales; 64 / 128:
+ *                    per-group scales computed by the cache write.
+ *      KVQ_FP8_E5M2  group_size 0 only: static per-KV-head scales.
+ *      KVQ_FP16      group_size ignored, no scales.
  *  - Pointers to q, out, pools, scales and workspace must be 16-byte aligned.
  *
  * Pool layout (one layer; the caller keeps one set of pools per layer):
  *   k_pool, v_pool  [num_blocks][Hkv][tile], one tile of block_size * head_dim
  *   elements (EB bytes each: INT8 = codes in excess-128 form, byte = code +
- *   128, and FP8 = E4M3 bytes, EB = 1; FP16 = IEEE half, EB = 2) per (block,
- *   KV head).  Inside a tile, element
+ *   128, and FP8 = E4M3 / E5M2 bytes, EB = 1; FP16 = IEEE half, EB = 2) per
+ *   (block, KV head).  Inside a tile, element
  *   (token t, dim d) sits at byte
  *     K:  ((d*EB/64) * block_size + t) * 64 + (d*EB) % 64
  *         (rows of 64 bytes: 64 one-byte dims or 32 fp16 dims of one token)
@@ -45,9 +55,13 @@
  *         half of a block).
  *   These orders let every 16-byte load of the decode kernel cover, across a
  *   wavefront, one contiguous KiB of whole cache lines.
- *   INT8 scales: k_scale, v_scale [num_blocks][Hkv][block_size][head_dim/G]
- *   fp32, one per (token slot, group of G consecutive head_dim elements).
- *   FP8 scales:  k_scale, v_scale [Hkv] fp32, static, read only.
+ *   Per-group scales (INT8 or E4M3, group_size G > 0): k_scale, v_scale
+ *   [num_blocks][Hkv][block_size][head_dim/G] fp32, one per (token slot,
+ *   group of G consecutive head_dim elements), written by the cache write.
+ *   Static per-channel scales (INT8, group_size 0): k_scale, v_scale
+ *   [Hkv][head_dim] fp32, read only.
+ *   Static per-head scales (FP8, group_size 0): k_scale, v_scale [Hkv] fp32,
+ *   read only.
  *   FP16: no scales (pass NULL).
  *   A slot is block * block_size + offset.
  */
@@ -66,8 +80,9 @@ extern "C" {
 /* KV element formats (per layer). */
 enum {
     KVQ_FP16 = 0,
-    KVQ_INT8 = 1,     /* per-group absmax, one fp32 scale per group   */
-    KVQ_FP8_E4M3 = 2  /* OCP E4M3FN, one static fp32 scale per KV head */
+    KVQ_INT8 = 1,      /* symmetric, |code| <= 127, per-group or per-channel */
+    KVQ_FP8_E4M3 = 2,  /* OCP E4M3FN (max 448), per-head or per-group       */
+    KVQ_FP8_E5M2 = 3   /* OCP E5M2 (max 57344), per-head                    */
 };
 
 typedef int32_t kvq_status;
@@ -93,17 +108,26 @@ KVQ_API int32_t kvq_version(void);
  *   k, v          fp16 [num_tokens][num_kv_heads][head_dim], contiguous.
  *   slot_mapping  int64 [num_tokens]: slot of each token; a negative slot, or
  *                 one >= num_blocks * block_size, skips the token.
- *   dtype         KVQ_INT8: for each (token, head, group of group_size
- *                   elements): a = max |x|; s = fl32(a / 127);
+ *   dtype, group_size (see "Scale granularity" above):
+ *                 KVQ_INT8, group_size G > 0: for each (token, head, group of
+ *                   G elements): a = max |x|; s = fl32(a / 127);
  *                   code = clamp(round_half_even(fl32(x / s)), -127, 127);
  *                   a == 0 stores s = 0 and zero codes.  Codes go to the
  *                   pools as bytes code + 128, s to k_scale / v_scale
  *                   (written).
- *                 KVQ_FP8_E4M3: code = E4M3(fl32(x / S[h])) rounding to
- *                   nearest-even and saturating to +-448; S = k_scale /
- *                   v_scale [num_kv_heads] (read only).
+ *                 KVQ_INT8, group_size 0: code = clamp(round_half_even(
+ *                   fl32(x / S[h][d])), -127, 127) with the static channel
+ *                   scales S = k_scale / v_scale [num_kv_heads][head_dim]
+ *                   (read only); S == 0 gives code 0.
+ *                 KVQ_FP8_E4M3 / KVQ_FP8_E5M2, group_size 0: code =
+ *                   FP8(fl32(x / S[h])) rounding to nearest-even and
+ *                   saturating to the largest finite value (448 / 57344);
+ *                   S = k_scale / v_scale [num_kv_heads] (read only);
+ *                   S == 0 gives code 0.
+ *                 KVQ_FP8_E4M3, group_size G > 0: per group, s = fl32(a /
+ *                   448), code = E4M3(fl32(x / s)) (a == 0: s = 0, codes 0);
+ *                   s written to k_scale / v_scale like INT8.
  *                 KVQ_FP16: the values are copied.
- *   group_size    INT8 only (64 or 128, divides head_dim); ignored otherwise.
  * Tokens are independent; two tokens mapped to the same slot race.
  */
 KVQ_API kvq_status kvq_cache_write(const void *k, const void *v,

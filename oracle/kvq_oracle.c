@@ -31,7 +31,8 @@
  *  - FP8 is OCP E4M3FN (bias 7, max 448, no infinities); encode rounds to
  *    nearest, ties to even, and saturates to +-448; a negative value that
  *    rounds to zero keeps its sign (code 0x80).  The scale is a static fp32
- *    per KV head, applied as fl32(x / S).
+ *    per KV head, applied as fl32(x / S); a zero scale (a head whose
+ *    calibration data are all zero) gives code 0.
  *  - FP8 E5M2 (the kv_cache_dtype "fp8_e5m2" of xpshop.cn article 312 s3) is
  *    the OCP E5M2 format (bias 15, 2 mantissa bits, infinities and NaNs);
  *    encode rounds to nearest, ties to even, and saturates to +-57344.
@@ -297,6 +298,10 @@ ORC_API int orc_fp8_quantize_rows_fmt(const uint16_t *x, int64_t rows, int Hkv,
                 double xd = orc_f16_to_f64(x[k]);
                 if (!isfinite(xd)) {
                     bad = 1;
+                    continue;
+                }
+                if (S[h] == 0.0f) {           /* no scale: code 0 */
+                    codes[k] = 0;
                     continue;
                 }
                 float y = (float)xd / S[h];

@@ -61,18 +61,22 @@ bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 kvq_status check_format(int32_t dtype, int32_t head_dim, int32_t block_size,
                         int32_t group_size)
 {
-    if (dtype != KVQ_FP16 && dtype != KVQ_INT8 && dtype != KVQ_FP8_E4M3)
+    if (dtype != KVQ_FP16 && dtype != KVQ_INT8 && dtype != KVQ_FP8_E4M3 &&
+        dtype != KVQ_FP8_E5M2)
         return KVQ_ERR_UNSUPPORTED;
     if (head_dim != 64 && head_dim != 128)
         return KVQ_ERR_UNSUPPORTED;
     if (block_size != 16 && block_size != 32)
         return KVQ_ERR_UNSUPPORTED;
-    if (dtype == KVQ_INT8) {
-        if (group_size != 64 && group_size != 128)
+    if (dtype == KVQ_INT8 || dtype == KVQ_FP8_E4M3) {
+        // 0: static scales; 64 / 128: per-group scales
+        if (group_size != 0 && group_size != 64 && group_size != 128)
             return KVQ_ERR_UNSUPPORTED;
-        if (group_size > head_dim || head_dim % group_size != 0)
+        if (group_size > head_dim)
             return KVQ_ERR_UNSUPPORTED;
     }
+    if (dtype == KVQ_FP8_E5M2 && group_size != 0)
+        return KVQ_ERR_UNSUPPORTED;
     return KVQ_OK;
 }
 
@@ -144,15 +148,17 @@ void launch_write(const WriteParams &p, hipStream_t s)
 template <int FMT, int D>
 kvq_status dispatch_write_g(const WriteParams &p, int G, hipStream_t s)
 {
-    if constexpr (FMT == FMT_INT8) {
-        if (G == 64)
+    if constexpr (FMT == FMT_INT8 || FMT == FMT_FP8) {
+        if (G == 0)
+            launch_write<FMT, D, 0>(p, s);
+        else if (G == 64)
             launch_write<FMT, D, 64>(p, s);
         else if constexpr (D >= 128)
             launch_write<FMT, D, 128>(p, s);
         else
             return KVQ_ERR_UNSUPPORTED;
     } else {
-        launch_write<FMT, D, D>(p, s);
+        launch_write<FMT, D, 0>(p, s);
     }
     return launch_status();
 }
@@ -232,10 +238,14 @@ kvq_status launch_decode(DecodeParams p, const LaunchPlan &lp, hipStream_t s)
     return launch_status();
 }
 
+// Kernel instances: NG = head_dim / group_size for per-group scales, 0 for
+// static scales (FP8 per head, INT8 per channel) and fp16.
 template <int FMT, int D, int BS>
 kvq_status dispatch_decode_ng(const DecodeParams &p, const LaunchPlan &lp, int G, hipStream_t s)
 {
-    if constexpr (FMT == FMT_INT8) {
+    if constexpr (FMT == FMT_INT8 || FMT == FMT_FP8) {
+        if (G == 0)
+            return launch_decode<FMT, D, BS, 0>(p, lp, s);
         const int NG = D / G;
         if (NG == 1)
             return launch_decode<FMT, D, BS, 1>(p, lp, s);
@@ -243,7 +253,7 @@ kvq_status dispatch_decode_ng(const DecodeParams &p, const LaunchPlan &lp, int G
             return launch_decode<FMT, D, BS, 2>(p, lp, s);
         return KVQ_ERR_UNSUPPORTED;
     } else {
-        return launch_decode<FMT, D, BS, 1>(p, lp, s);
+        return launch_decode<FMT, D, BS, 0>(p, lp, s);
     }
 }
 
@@ -316,7 +326,8 @@ kvq_status kvq_cache_write(const void *k, const void *v, const int64_t *slot_map
     switch (dtype) {
     case KVQ_INT8: return dispatch_write_d<FMT_INT8>(p, head_dim, group_size, s);
     case KVQ_FP8_E4M3: return dispatch_write_d<FMT_FP8>(p, head_dim, group_size, s);
-    default: return dispatch_write_d<FMT_FP16>(p, head_dim, group_size, s);
+    case KVQ_FP8_E5M2: return dispatch_write_d<FMT_E5M2>(p, head_dim, 0, s);
+    default: return dispatch_write_d<FMT_FP16>(p, head_dim, 0, s);
     }
 }
 
@@ -374,7 +385,8 @@ kvq_status kvq_paged_decode(const void *q, const void *k_pool, const void *v_poo
     if (dtype != KVQ_FP16 && (!k_scale || !v_scale))
         return KVQ_ERR_INVALID_ARG;
     if (!aligned16(q) || !aligned16(out) || !aligned16(k_pool) || !aligned16(v_pool) ||
-        (workspace && !aligned16(workspace)))
+        (workspace && !aligned16(workspace)) || (k_scale && !aligned16(k_scale)) ||
+        (v_scale && !aligned16(v_scale)))
         return KVQ_ERR_INVALID_ARG;
     if (!workspace)
         return KVQ_ERR_WORKSPACE;
@@ -411,8 +423,10 @@ kvq_status kvq_paged_decode(const void *q, const void *k_pool, const void *v_poo
         return dispatch_decode<FMT_INT8>(p, lp, head_dim, block_size, group_size, s);
     case KVQ_FP8_E4M3:
         return dispatch_decode<FMT_FP8>(p, lp, head_dim, block_size, group_size, s);
+    case KVQ_FP8_E5M2:
+        return dispatch_decode<FMT_E5M2>(p, lp, head_dim, block_size, 0, s);
     default:
-        return dispatch_decode<FMT_FP16>(p, lp, head_dim, block_size, group_size, s);
+        return dispatch_decode<FMT_FP16>(p, lp, head_dim, block_size, 0, s);
     }
 }
 
@@ -430,7 +444,8 @@ kvq_status kvq_copy_blocks(const int32_t *block_pairs, int32_t num_pairs, int32_
         return KVQ_OK;
     if (!block_pairs || !k_pool || !v_pool || !aligned16(k_pool) || !aligned16(v_pool))
         return KVQ_ERR_INVALID_ARG;
-    if (dtype == KVQ_INT8 && (!k_scale || !v_scale))
+    const bool group_scales = (dtype == KVQ_INT8 || dtype == KVQ_FP8_E4M3) && group_size > 0;
+    if (group_scales && (!k_scale || !v_scale))
         return KVQ_ERR_INVALID_ARG;
     st = check_device();
     if (st != KVQ_OK)
@@ -444,7 +459,7 @@ kvq_status kvq_copy_blocks(const int32_t *block_pairs, int32_t num_pairs, int32_
     const int eb = dtype == KVQ_FP16 ? 2 : 1;
     p.block_bytes = (int64_t)num_kv_heads * block_size * head_dim * eb;
     p.scale_block_floats =
-        dtype == KVQ_INT8 ? (int64_t)num_kv_heads * block_size * (head_dim / group_size) : 0;
+        group_scales ? (int64_t)num_kv_heads * block_size * (head_dim / group_size) : 0;
     p.num_blocks = num_blocks;
     const unsigned chunks = (unsigned)((p.block_bytes / 16 + 255) / 256);
     hipLaunchKernelGGL(copy_blocks_kernel, dim3((unsigned)num_pairs, chunks), dim3(256), 0,

@@ -268,7 +268,7 @@ __device__ __forceinline__ void load_tile(const DecodeParams &p, TileData<FMT, D
     const uint8_t *kb = p.k_pool + tile * (BS * D * EB);
     const uint8_t *vb = p.v_pool + tile * (BS * D * EB);
     load_codes<FMT, D, BS, NG, kNT>(p, t, kb, vb, toff, col, grp);
-    if constexpr (FMT == FMT_INT8) {
+    if constexpr (NG > 0) {  // per-group scales
         const int e = col % (8 * NG);
         const float *arr = e < 4 * NG ? p.k_scale : p.v_scale;
         const int w = e % (4 * NG);
@@ -282,9 +282,16 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
     constexpr int KS = D / 16;   // MFMA k-steps over head_dim
     constexpr int DT = D / 16;   // 16-dim output tiles
     constexpr int EB = TileData<FMT, D>::EB;
-    constexpr int G = D / NG;    // INT8 group size
-    constexpr int WIN = 64 * BS / 16;  // tiles covered by one 64-block window
-    static_assert(FMT != FMT_INT8 || G >= 64, "groups must cover a 64-dim chunk");
+    // Scales: NG > 0 -- one per (token, group of G dims) in arrays beside
+    // the pools (INT8 or E4M3); NG == 0 -- static: one per KV head (FP8),
+    // one per (KV head, channel) (INT8), none (fp16).
+    constexpr bool kGroup = NG > 0;
+    constexpr int NA = kGroup ? NG : 1;        // score accumulators per tile
+    constexpr int G = kGroup ? D / NG : D;     // group size
+    constexpr bool kInt8 = FMT == FMT_INT8;
+    constexpr bool kChannel = kInt8 && !kGroup;
+    constexpr float kCodeScale = FMT == FMT_FP8 ? 256.0f : 1.0f;  // E4M3 enters as value * 2^-8
+    static_assert(!kGroup || G >= 64, "groups must cover a 64-dim chunk");
 
     const int w = blockIdx.x;
     const int lane = threadIdx.x;
@@ -379,18 +386,44 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
                     qop[s] = f16x4{0, 0, 0, 0};
             }
         }
+        // INT8 per channel: K's channel scales ride on q, q' = q * s_d, as an
+        // fp16 pair hi + lo (hi = fp16(q'), lo = fp16(q' - hi)) so the dot
+        // products keep ~22 bits of q'; both halves go through the MFMA.
+        f16x4 qlo[kChannel ? KS : 1];
+        if constexpr (kChannel) {
+            const float *srow = p.k_scale + (int64_t)h * D;
+#pragma unroll
+            for (int c = 0; c < D / 64; ++c) {
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {  // dims 64 c + 16 grp + 4 u + (0..3)
+                    const float4 sc4 = *reinterpret_cast<const float4 *>(srow + 64 * c + 16 * grp + 4 * u);
+                    const float scv[4] = {sc4.x, sc4.y, sc4.z, sc4.w};
+                    f16x4 &hi = qop[4 * c + u];
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) {
+                        const float qs = (float)hi[v] * scv[v];
+                        const f16 h16 = (f16)qs;
+                        hi[v] = h16;
+                        qlo[4 * c + u][v] = (f16)(qs - (float)h16);
+                    }
+                }
+            }
+        }
         // INT8 codes enter both MFMAs as c + 1152 (no subtraction per code).
         // The score of group j is corrected by 1152 * (sum of q over the
         // group); the output by 1152 * (sum of the P^T operand entries of the
         // group), accumulated in csum with the same rescales as o.
-        float qbias[NG];
-        if constexpr (FMT == FMT_INT8) {
+        float qbias[NA];
+        if constexpr (kInt8) {
 #pragma unroll
-            for (int j = 0; j < NG; ++j) {
+            for (int j = 0; j < NA; ++j) {
                 float sum = 0.0f;
 #pragma unroll
-                for (int s = j * (KS / NG); s < (j + 1) * (KS / NG); ++s)
+                for (int s = j * (KS / NA); s < (j + 1) * (KS / NA); ++s) {
                     sum += ((float)qop[s][0] + (float)qop[s][1]) + ((float)qop[s][2] + (float)qop[s][3]);
+                    if constexpr (kChannel)
+                        sum += ((float)qlo[s][0] + (float)qlo[s][1]) + ((float)qlo[s][2] + (float)qlo[s][3]);
+                }
                 sum += __shfl_xor(sum, 16);
                 sum += __shfl_xor(sum, 32);
                 qbias[j] = kInt8Bias * sum;
@@ -398,18 +431,19 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
         }
         float score_scale = score_scale0;
         float out_scale = 1.0f;
-        if constexpr (FMT == FMT_FP8) {
-            score_scale *= 256.0f * p.k_scale[h];
-            out_scale = 256.0f * p.v_scale[h];
+        if constexpr ((FMT == FMT_FP8 || FMT == FMT_E5M2) && !kGroup) {
+            score_scale *= kCodeScale * p.k_scale[h];
+            out_scale = kCodeScale * p.v_scale[h];
         }
-        // INT8: this lane's scale entry (see TileData) is token lane_tok of
-        // the tile; K entries carry the score scale, so the scores need no
-        // further multiply.  Entries of tokens past t_end become 0.
+        // Per-group scales: this lane's scale entry (see TileData) is token
+        // lane_tok of the tile; K entries carry the score scale, so the
+        // scores need no further multiply.  Entries of tokens past t_end
+        // become 0.
         float lane_fac = 1.0f;
         int lane_tok = 0;
-        if constexpr (FMT == FMT_INT8) {
+        if constexpr (kGroup) {
             const int e = col % (8 * NG);
-            lane_fac = e < 4 * NG ? score_scale : 1.0f;
+            lane_fac = e < 4 * NG ? score_scale * kCodeScale : kCodeScale;
             lane_tok = 4 * grp + (e % (4 * NG)) / NG;
         }
 
@@ -420,16 +454,16 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
             o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
         float m = -INFINITY;
         float l = 0.0f;
-        float csum[NG];
+        float csum[NA];
 #pragma unroll
-        for (int j = 0; j < NG; ++j)
+        for (int j = 0; j < NA; ++j)
             csum[j] = 0.0f;
 
         // One tile of 16 tokens starting at logical token ts, data in `cur`.
         auto process = [&](const TileData<FMT, D> &cur, const int ts) {
             // ---- this lane's scales: sk[v][j], sv[v][j] of tokens 4 grp + v
-            float sk[4][NG], sv[4][NG];
-            if constexpr (FMT == FMT_INT8) {
+            float sk[4][NA], sv[4][NA];
+            if constexpr (kGroup) {
                 const float sc = (ts + lane_tok < t_end) ? cur.sc * lane_fac : 0.0f;
                 static_for<0, 4 * NG>([&](auto I) {
                     constexpr int i = decltype(I)::value;
@@ -437,10 +471,10 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
                     sv[i / NG][i % NG] = row_bcast<4 * NG + i>(sc);
                 });
             }
-            // ---- S^T = K Q^T, one accumulator per INT8 group
-            f32x4 sacc[NG];
+            // ---- S^T = K Q^T, one accumulator per scale group
+            f32x4 sacc[NA];
 #pragma unroll
-            for (int i = 0; i < NG; ++i)
+            for (int i = 0; i < NA; ++i)
                 sacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int s = 0; s < KS; ++s) {
@@ -449,11 +483,15 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
                     a = int8x4_to_f16x4_biased(cur.k[s]);
                 } else if constexpr (FMT == FMT_FP8) {
                     a = fp8x4_to_f16x4_scaled(cur.k[s]);
+                } else if constexpr (FMT == FMT_E5M2) {
+                    a = e5m2x4_to_f16x4(cur.k[s]);
                 } else {
                     a = f16x4_from_u2(cur.k[2 * s], cur.k[2 * s + 1]);
                 }
-                const int gi = (FMT == FMT_INT8 && NG == 2) ? (s >> 2) : 0;
+                const int gi = NA == 2 ? (s >> 2) : 0;
                 sacc[gi] = __builtin_amdgcn_mfma_f32_16x16x16f16(a, qop[s], sacc[gi], 0, 0, 0);
+                if constexpr (kChannel)
+                    sacc[0] = __builtin_amdgcn_mfma_f32_16x16x16f16(a, qlo[s], sacc[0], 0, 0, 0);
             }
             // ---- scores of tokens ts + 4 grp + v for query head col (base 2)
             const int tok0 = ts + 4 * grp;
@@ -461,10 +499,12 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 float acc;
-                if constexpr (FMT == FMT_INT8) {
-                    acc = (sacc[0][v] - qbias[0]) * sk[v][0];
-                    if constexpr (NG == 2)
-                        acc += (sacc[1][v] - qbias[1]) * sk[v][1];
+                if constexpr (kGroup) {
+                    acc = (kInt8 ? sacc[0][v] - qbias[0] : sacc[0][v]) * sk[v][0];
+                    if constexpr (NA == 2)
+                        acc += (kInt8 ? sacc[1][v] - qbias[1] : sacc[1][v]) * sk[v][1];
+                } else if constexpr (kInt8) {
+                    acc = (sacc[0][v] - qbias[0]) * score_scale;
                 } else {
                     acc = sacc[0][v] * score_scale;
                 }
@@ -482,7 +522,7 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
                 for (int i = 0; i < DT; ++i)
                     o[i] *= alpha;
 #pragma unroll
-                for (int j = 0; j < NG; ++j)
+                for (int j = 0; j < NA; ++j)
                     csum[j] *= alpha;
                 m = mn;
             }
@@ -492,33 +532,35 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
                 pr[v] = __builtin_amdgcn_exp2f(z[v] - m);
                 l += pr[v];
             }
-            // ---- P^T operands (V group scales folded in for INT8; masked
-            // tokens have pr = 0 and a zeroed scale)
-            f16x4 pop[NG];
-            if constexpr (FMT == FMT_INT8) {
-                const f16x2 ones = {(f16)1.0f, (f16)1.0f};
+            // ---- P^T operands (V group scales folded in; masked tokens have
+            // pr = 0 and a zeroed scale)
+            f16x4 pop[NA];
 #pragma unroll
-                for (int j = 0; j < NG; ++j) {
+            for (int j = 0; j < NA; ++j) {
 #pragma unroll
-                    for (int v = 0; v < 4; ++v)
-                        pop[j][v] = (f16)(pr[v] * sv[v][j]);
+                for (int v = 0; v < 4; ++v)
+                    pop[j][v] = kGroup ? (f16)(pr[v] * sv[v][j]) : (f16)pr[v];
+                if constexpr (kInt8) {
+                    const f16x2 ones = {(f16)1.0f, (f16)1.0f};
                     csum[j] = __builtin_amdgcn_fdot2(f16x2{pop[j][0], pop[j][1]}, ones, csum[j], false);
                     csum[j] = __builtin_amdgcn_fdot2(f16x2{pop[j][2], pop[j][3]}, ones, csum[j], false);
                 }
-            } else {
-#pragma unroll
-                for (int v = 0; v < 4; ++v)
-                    pop[0][v] = (f16)pr[v];
             }
             // ---- O^T += V^T P^T; d-tile tau covers dims 64 (tau/4) + 4 m + tau%4
             // fp16: stale slots past t_end may hold non-finite values, which
             // a zero P entry does not cancel; the lane's V dwords hold tokens
             // (0, 1) or (2, 3) of its quad and are masked per token.
-            uint32_t vmask01 = ~0u, vmask23 = ~0u;
+            // E5M2 likewise: its conversion is exact, so stale NaN / inf
+            // codes survive it; a V dword holds tokens 0..3 of the quad, one
+            // byte each.
+            uint32_t vmask01 = ~0u, vmask23 = ~0u, vmask8 = ~0u;
             if constexpr (FMT == FMT_FP16) {
                 const int nv = t_end - tok0;  // valid tokens of this lane's quad (if < 4)
                 vmask01 = nv >= 2 ? ~0u : (nv == 1 ? 0xffffu : 0u);
                 vmask23 = nv >= 4 ? ~0u : (nv == 3 ? 0xffffu : 0u);
+            } else if constexpr (FMT == FMT_E5M2) {
+                const int nv = t_end - tok0;
+                vmask8 = nv >= 4 ? ~0u : (nv <= 0 ? 0u : (1u << (8 * nv)) - 1u);
             }
 #pragma unroll
             for (int tau = 0; tau < DT; ++tau) {
@@ -528,12 +570,14 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
                     a = int8x4_to_f16x4_biased(cur.v[4 * g4 + i]);
                 } else if constexpr (FMT == FMT_FP8) {
                     a = fp8x4_to_f16x4_scaled(cur.v[4 * g4 + i]);
+                } else if constexpr (FMT == FMT_E5M2) {
+                    a = e5m2x4_to_f16x4(cur.v[4 * g4 + i] & vmask8);
                 } else {
                     // fp16 micro-tiles hold 2 dims x 4 tokens: part i/2 of quad g4
                     const int x = 2 * g4 + (i >> 1), wd = 2 * (i & 1);
                     a = f16x4_from_u2(cur.v[4 * x + wd] & vmask01, cur.v[4 * x + wd + 1] & vmask23);
                 }
-                const int gi = (FMT == FMT_INT8 && NG == 2) ? (64 * g4) / G : 0;
+                const int gi = NA == 2 ? (64 * g4) / G : 0;
                 o[tau] = __builtin_amdgcn_mfma_f32_16x16x16f16(a, pop[gi], o[tau], 0, 0, 0);
             }
         };
@@ -616,10 +660,10 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
         // ---- epilogue: lane holds dims 64 g4 + 16 grp + (0..15) of head col
         float lt = l + __shfl_xor(l, 16);
         lt += __shfl_xor(lt, 32);
-        if constexpr (FMT == FMT_INT8) {
+        if constexpr (kInt8) {
             // remove the code bias: o -= 1152 * (sum of P^T entries of the group)
 #pragma unroll
-            for (int j = 0; j < NG; ++j) {
+            for (int j = 0; j < NA; ++j) {
                 float c = csum[j] + __shfl_xor(csum[j], 16);
                 c += __shfl_xor(c, 32);
                 csum[j] = kInt8Bias * c;
@@ -630,6 +674,20 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
         }
         if (!head_ok)
             return;
+        if constexpr (kChannel) {
+            // V channel scales: o[4 g4 + i][v] is dim 64 g4 + 16 grp + 4 v + i
+            const float *srow = p.v_scale + (int64_t)h * D + 16 * grp;
+#pragma unroll
+            for (int g4 = 0; g4 < D / 64; ++g4)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const float4 sc4 = *reinterpret_cast<const float4 *>(srow + 64 * g4 + 4 * v);
+                    o[4 * g4 + 0][v] *= sc4.x;
+                    o[4 * g4 + 1][v] *= sc4.y;
+                    o[4 * g4 + 2][v] *= sc4.z;
+                    o[4 * g4 + 3][v] *= sc4.w;
+                }
+        }
         if (t0 == 0 && t1 == n) {  // the whole unit: final output
             const float inv = out_scale / lt;
             f16 *orow = p.out + ((int64_t)b * p.Hq + qhead) * D + 16 * grp;

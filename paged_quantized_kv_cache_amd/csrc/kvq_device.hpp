@@ -11,6 +11,9 @@
 //     and 3 mantissa bits into the fp16 fields keeps the mantissa and
 //     re-biases the exponent from 7 to 15 (subnormals land on fp16
 //     subnormals with the same factor); the 2^8 goes into the scale.
+//   E5M2 code -> fp16 of the same value: E5M2 has fp16's sign and exponent
+//     fields and its two top fraction bits, so the code is the fp16's high
+//     byte.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -20,7 +23,15 @@
 
 namespace kvq {
 
-enum { FMT_FP16 = 0, FMT_INT8 = 1, FMT_FP8 = 2 };
+// FMT_FP8 is E4M3; FMT_E5M2 is the other OCP FP8 format.
+enum { FMT_FP16 = 0, FMT_INT8 = 1, FMT_FP8 = 2, FMT_E5M2 = 3 };
+
+// Largest finite value of each FP8 format.
+template <int FMT>
+constexpr float fp8_max()
+{
+    return FMT == FMT_E5M2 ? 57344.0f : 448.0f;
+}
 
 typedef _Float16 f16;
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
@@ -76,6 +87,17 @@ __device__ __forceinline__ f16x4 fp8x4_to_f16x4_scaled(uint32_t w)
     return f16x4{a.x, a.y, b.x, b.y};
 }
 
+// Four E5M2 bytes -> 4 fp16 of the same values (each byte becomes the high
+// byte of an fp16 whose low byte is zero).
+__device__ __forceinline__ f16x4 e5m2x4_to_f16x4(uint32_t w)
+{
+    const uint32_t h0 = byte_perm(0u, w, 0x010c000cu);  // b0 << 8, b1 << 24
+    const uint32_t h1 = byte_perm(0u, w, 0x030c020cu);
+    const f16x2 a = bit_cast<f16x2>(h0);
+    const f16x2 b = bit_cast<f16x2>(h1);
+    return f16x4{a.x, a.y, b.x, b.y};
+}
+
 __device__ __forceinline__ f16x4 f16x4_from_u2(uint32_t lo, uint32_t hi)
 {
     const f16x2 a = bit_cast<f16x2>(lo);
@@ -101,6 +123,35 @@ __device__ __forceinline__ uint32_t e4m3_rne_sat(float y)
     const uint32_t ab = __float_as_uint(a);
     const uint32_t r = (ab + 0x7ffffu + ((ab >> 20) & 1u)) >> 20;  // 3 fraction bits, RNE
     return sign | (r - (120u << 3));  // exponent bias 127 -> 7
+}
+
+// Round to the nearest E5M2 value (ties to even), saturating to +-57344;
+// the sign of a zero result is kept.  Bit-level, from the format definition.
+__device__ __forceinline__ uint32_t e5m2_rne_sat(float y)
+{
+    const uint32_t bits = __float_as_uint(y);
+    const uint32_t sign = (bits >> 24) & 0x80u;
+    const float a = __builtin_fabsf(y);
+    if (a != a)
+        return sign | 0x7fu;
+    if (!(a < 57344.0f))
+        return sign | 0x7bu;
+    if (a < 6.103515625e-05f) {  // below 2^-14: fixed spacing 2^-16
+        const float q = __builtin_rintf(a * 65536.0f);
+        return sign | (uint32_t)q;  // 0..4, 4 is the smallest normal
+    }
+    const uint32_t ab = __float_as_uint(a);
+    const uint32_t r = (ab + 0xfffffu + ((ab >> 21) & 1u)) >> 21;  // 2 fraction bits, RNE
+    return sign | (r - (112u << 2));  // exponent bias 127 -> 15
+}
+
+template <int FMT>
+__device__ __forceinline__ uint32_t fp8_rne_sat(float y)
+{
+    if constexpr (FMT == FMT_E5M2)
+        return e5m2_rne_sat(y);
+    else
+        return e4m3_rne_sat(y);
 }
 
 // ---------------------------------------------------------------- layouts

@@ -2,7 +2,12 @@
 //
 // Cache write ("KV Cache优化实战" s1.1: the new token's K/V is appended to the
 // cache; s2.3 / s3.3: INT8 absmax symmetric per group of 64 or 128 elements,
-// with a stored scale; xpshop.cn article 312 s3: FP8 KV).
+// with a stored scale, or per channel; xpshop.cn article 312 s3: FP8 KV, as
+// E4M3 or E5M2).
+//
+// G > 0: a scale per (token, head, group of G elements) computed here (INT8
+// or FP8); G == 0: static scales given by the caller (FP8: one per KV head;
+// INT8: one per (KV head, channel)); fp16 is copied.
 //
 // One wavefront per (token, KV head): lanes 0..31 take K, lanes 32..63 take V,
 // each lane D/32 consecutive elements of the head.  A group of G elements is
@@ -74,7 +79,9 @@ __global__ __launch_bounds__(64 * kWriteWaves) void cache_write_kernel(WritePara
     const int64_t head_base = blk * p.Hkv + h;  // (block, head) tile index
     uint32_t code[EPL];
 
-    if constexpr (FMT == FMT_INT8) {
+    if constexpr (G > 0) {
+        // dynamic per-group scale (INT8, or either FP8 format): s = absmax /
+        // (largest code value), one fp32 scale per (slot, group)
         constexpr int LPG = G / EPL;            // lanes per group
         constexpr int NG = D / G;
         float a = 0.0f;
@@ -84,25 +91,43 @@ __global__ __launch_bounds__(64 * kWriteWaves) void cache_write_kernel(WritePara
 #pragma unroll
         for (int o = 1; o < LPG; o <<= 1)
             a = fmaxf(a, __shfl_xor(a, o));
-        const float s = a / 127.0f;             // IEEE division (correctly rounded)
+        constexpr float kMaxCode = FMT == FMT_INT8 ? 127.0f : fp8_max<FMT>();
+        const float s = a / kMaxCode;           // IEEE division (correctly rounded)
 #pragma unroll
         for (int i = 0; i < EPL; ++i) {
-            float q = 0.0f;
-            if (s != 0.0f) {
-                q = __builtin_rintf(x[i] / s);  // round half to even
-                q = fminf(fmaxf(q, -127.0f), 127.0f);
+            if constexpr (FMT == FMT_INT8) {
+                float q = 0.0f;
+                if (s != 0.0f) {
+                    q = __builtin_rintf(x[i] / s);  // round half to even
+                    q = fminf(fmaxf(q, -127.0f), 127.0f);
+                }
+                code[i] = (uint32_t)((int32_t)q + 128);  // stored in excess-128 form
+            } else {
+                code[i] = s != 0.0f ? fp8_rne_sat<FMT>(x[i] / s) : 0u;
             }
-            code[i] = (uint32_t)((int32_t)q + 128);  // stored in excess-128 form
         }
         if ((lane & (LPG - 1)) == 0) {
             float *sc = is_v ? p.v_scale : p.k_scale;
             sc[(head_base * BS + off) * NG + (e0 / G)] = s;
         }
-    } else if constexpr (FMT == FMT_FP8) {
+    } else if constexpr (FMT == FMT_INT8) {
+        // static per-channel scales [Hkv][D]; a zero scale gives code 0
+        const float *S = (is_v ? p.v_scale : p.k_scale) + (int64_t)h * D + e0;
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) {
+            float q = 0.0f;
+            if (S[i] != 0.0f) {
+                q = __builtin_rintf(x[i] / S[i]);
+                q = fminf(fmaxf(q, -127.0f), 127.0f);
+            }
+            code[i] = (uint32_t)((int32_t)q + 128);
+        }
+    } else if constexpr (FMT == FMT_FP8 || FMT == FMT_E5M2) {
+        // static per-head scale
         const float S = (is_v ? p.v_scale : p.k_scale)[h];
 #pragma unroll
         for (int i = 0; i < EPL; ++i)
-            code[i] = e4m3_rne_sat(x[i] / S);
+            code[i] = S != 0.0f ? fp8_rne_sat<FMT>(x[i] / S) : 0u;  // zero scale: code 0
     }
 
     // Tile layouts: see k_offset / v_offset (kvq_device.hpp).

@@ -29,19 +29,20 @@ class LayerPools:
 
 def poison_(pools: LayerPools) -> None:
     """Fill pools with values that would corrupt any result that read them:
-    NaN fp16 / NaN scales; INT8 bytes at the extremes (excess-128 bytes 0x00
-    and 0xFF, codes -128 and +127); E4M3 NaN bytes."""
+    NaN fp16 / NaN and inf per-group scales; INT8 bytes at the extremes
+    (excess-128 bytes 0x00 and 0xFF, codes -128 and +127); FP8 NaN bytes."""
     if pools.fmt == "fp16":
         pools.k_pool.fill_(float("nan"))
         pools.v_pool.fill_(float("nan"))
     elif pools.fmt == "int8":
         pools.k_pool.fill_(0x00)
         pools.v_pool.fill_(0xFF)
-        pools.k_scale.fill_(float("nan"))
-        pools.v_scale.fill_(float("inf"))
     else:
         pools.k_pool.fill_(0x7F)
         pools.v_pool.fill_(0xFF)
+    if pools.k_scale is not None and pools.k_scale.dim() == 4:  # per-group scales
+        pools.k_scale.fill_(float("nan"))
+        pools.v_scale.fill_(float("inf"))
 
 
 class DecodeCase:
@@ -95,10 +96,11 @@ class DecodeCase:
         pools = LayerPools(fmt, kp, vp, ks, vs)
         if self.poison:
             poison_(pools)
-        if fmt == "fp8":
-            d = self.data[layer]
-            pools.k_scale.copy_(W.fp8_static_scales(d.k))
-            pools.v_scale.copy_(W.fp8_static_scales(d.v))
+        d = self.data[layer]
+        for scale, x in ((pools.k_scale, d.k), (pools.v_scale, d.v)):
+            st = W.static_scales(fmt, s.G, x)
+            if st is not None:
+                scale.copy_(st)
         self.pools[layer] = pools
         return pools
 
@@ -183,7 +185,7 @@ class DecodeCase:
                 else:
                     g = g.reshape(n, s.Hkv, s.D).view(np.uint8)
                 item[name] = g
-            if p.fmt == "int8":
+            if kvq.scale_mode(p.fmt, s.G) == "group":
                 item["k_scale"] = p.k_scale[blk, :, off, :].cpu().numpy()
                 item["v_scale"] = p.v_scale[blk, :, off, :].cpu().numpy()
             out.append(item)

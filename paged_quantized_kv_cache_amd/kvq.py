@@ -23,10 +23,22 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libkvq.so")
 
-KVQ_FP16, KVQ_INT8, KVQ_FP8_E4M3 = 0, 1, 2
-FORMATS = {"fp16": KVQ_FP16, "int8": KVQ_INT8, "fp8": KVQ_FP8_E4M3}
-# INT8 pools hold excess-128 bytes (code + 128), FP8 pools E4M3 bytes.
-POOL_DTYPES = {"fp16": torch.float16, "int8": torch.uint8, "fp8": torch.uint8}
+KVQ_FP16, KVQ_INT8, KVQ_FP8_E4M3, KVQ_FP8_E5M2 = 0, 1, 2, 3
+FORMATS = {"fp16": KVQ_FP16, "int8": KVQ_INT8, "fp8": KVQ_FP8_E4M3, "e5m2": KVQ_FP8_E5M2}
+# INT8 pools hold excess-128 bytes (code + 128), FP8 pools E4M3 / E5M2 bytes.
+POOL_DTYPES = {"fp16": torch.float16, "int8": torch.uint8, "fp8": torch.uint8,
+               "e5m2": torch.uint8}
+
+
+def scale_mode(fmt: str, group_size: int) -> str:
+    """'group' (per token-group scales written by the cache write),
+    'head' (static per KV head), 'channel' (static per KV head and channel)
+    or 'none'."""
+    if fmt == "fp16":
+        return "none"
+    if group_size > 0:
+        return "group"
+    return "channel" if fmt == "int8" else "head"
 STATUS = {0: "KVQ_OK", -1: "KVQ_ERR_INVALID_ARG", -2: "KVQ_ERR_UNSUPPORTED",
           -3: "KVQ_ERR_WORKSPACE", -4: "KVQ_ERR_HIP"}
 EXPORTS = ("kvq_status_string", "kvq_version", "kvq_cache_write",
@@ -107,17 +119,23 @@ def alloc_pools(num_blocks: int, num_kv_heads: int, block_size: int,
                 head_dim: int, fmt: str, group_size: int = 0, device="cuda"):
     """Allocate one layer's (k_pool, v_pool, k_scale, v_scale) with torch.
 
-    FP8 scales are returned as ones (the caller fills in its static scales);
-    FP16 has no scales (None)."""
+    Per-group scales: [num_blocks][Hkv][block_size][head_dim/G] (written by
+    the cache write).  Static scales are returned as ones, for the caller to
+    fill: [Hkv] per head (FP8), [Hkv][head_dim] per channel (INT8).  FP16 has
+    no scales (None)."""
     dt = POOL_DTYPES[fmt]
     kp = torch.empty((num_blocks, num_kv_heads, block_size, head_dim), dtype=dt, device=device)
     vp = torch.empty((num_blocks, num_kv_heads, block_size, head_dim), dtype=dt, device=device)
-    if fmt == "int8":
+    mode = scale_mode(fmt, group_size)
+    if mode == "group":
         ng = head_dim // group_size
         ks = torch.empty((num_blocks, num_kv_heads, block_size, ng), dtype=torch.float32, device=device)
         vs = torch.empty_like(ks)
-    elif fmt == "fp8":
+    elif mode == "head":
         ks = torch.ones(num_kv_heads, dtype=torch.float32, device=device)
+        vs = torch.ones_like(ks)
+    elif mode == "channel":
+        ks = torch.ones((num_kv_heads, head_dim), dtype=torch.float32, device=device)
         vs = torch.ones_like(ks)
     else:
         ks = vs = None
@@ -218,7 +236,7 @@ def kvq_copy_blocks(block_pairs: torch.Tensor, k_pool: torch.Tensor, v_pool: tor
     if block_pairs.dtype != torch.int32 or (block_pairs.numel() and block_pairs.shape[-1] != 2):
         raise ValueError("block_pairs must be int32 [n][2]")
     n = block_pairs.numel() // 2
-    scale_ok = fmt == "int8"
+    scale_ok = scale_mode(fmt, group_size) == "group"
     st = lib().kvq_copy_blocks(_ptr(block_pairs), n, hkv, d, bs, num_blocks, _fmt(fmt),
                                group_size, _ptr(k_pool), _ptr(v_pool),
                                _ptr(k_scale) if scale_ok else None,

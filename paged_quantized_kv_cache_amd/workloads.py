@@ -25,7 +25,7 @@ import torch
 
 from .block_manager import BlockManager
 
-FORMATS = ("fp16", "int8", "fp8")
+FORMATS = ("fp16", "int8", "fp8", "e5m2")   # fp8 = E4M3
 
 
 @dataclass
@@ -44,7 +44,7 @@ class Spec:
     D: int
     BS: int
     fmt: str                      # format of single-layer workloads
-    G: int = 0                    # INT8 group size
+    G: int = 0                    # scale group size (0: static / none)
     lens: str = "fixed"           # fixed | uniform | lognormal
     lens_args: tuple = ()
     pool_blocks: int = 0          # 0: ceil(slack * needed)
@@ -105,6 +105,21 @@ SPECS: Dict[str, Spec] = {
         "c4_long_bs32", B=16, Hq=32, Hkv=8, D=128, BS=32, fmt="fp8",
         lens="fixed", lens_args=(32768,) * 16, seed=0,
         description="16 x 32768 tokens, FP8 e4m3, 32-token blocks"),
+    "c4_long_e5m2": Spec(
+        "c4_long_e5m2", B=16, Hq=32, Hkv=8, D=128, BS=16, fmt="e5m2",
+        lens="fixed", lens_args=(32768,) * 16, seed=0,
+        description="16 x 32768 tokens, FP8 e5m2 (static per-head scales)"),
+    "c3_fp8_token": Spec(
+        "c3_fp8_token", B=256, Hq=32, Hkv=8, D=128, BS=16, fmt="fp8", G=128,
+        lens="lognormal", lens_args=(2048, 16, 8192), seed=0,
+        k_out=Outliers(5, 10.0),
+        description="the GQA layer, FP8 e4m3 with a dynamic scale per "
+                    "(token, head)"),
+    "c3_int8_channel": Spec(
+        "c3_int8_channel", B=256, Hq=32, Hkv=8, D=128, BS=16, fmt="int8", G=0,
+        lens="lognormal", lens_args=(2048, 16, 8192), seed=0,
+        k_out=Outliers(5, 10.0),
+        description="the GQA layer, INT8 with static per-channel scales"),
     "c5_prefix_mixed": Spec(
         "c5_prefix_mixed", B=128, Hq=32, Hkv=8, D=128, BS=16, fmt="int8",
         G=128, lens="prefix_tails", lens_args=(64, 4096), seed=0, layers=32,
@@ -334,12 +349,29 @@ def gen_layer(s: Spec, n_unique: int, layer: int = 0, device="cpu",
     return LayerData(k=out[0], v=out[1], q=out[2])
 
 
-def fp8_static_scales(x: torch.Tensor) -> torch.Tensor:
+FP8_MAX = {"fp8": 448.0, "e5m2": 57344.0}
+
+
+def fp8_static_scales(x: torch.Tensor, fmt: str = "fp8") -> torch.Tensor:
     """Calibrated static FP8 scale per KV head: absmax over all tokens and
-    dims of that head, divided by the largest E4M3 value (448), in fp32, so
-    that no calibrated value saturates."""
+    dims of that head, divided by the format's largest value (E4M3 448,
+    E5M2 57344), in fp32, so that no calibrated value saturates."""
     a = x.float().abs().amax(dim=(0, 2))
-    return (a / 448.0).to(torch.float32)
+    return (a / FP8_MAX[fmt]).to(torch.float32)
+
+
+def int8_channel_scales(x: torch.Tensor) -> torch.Tensor:
+    """Calibrated static INT8 scale per (KV head, channel): absmax over all
+    tokens of that channel / 127, in fp32.  ``x``: [N][Hkv][D]."""
+    a = x.float().abs().amax(dim=0)
+    return (a / 127.0).to(torch.float32)
+
+
+def static_scales(fmt: str, group_size: int, x: torch.Tensor) -> Optional[torch.Tensor]:
+    """The static scale array a format needs (None if it has none)."""
+    if group_size > 0 or fmt == "fp16":
+        return None
+    return int8_channel_scales(x) if fmt == "int8" else fp8_static_scales(x, fmt)
 
 
 # ----------------------------------------------------------------- bytes
@@ -348,14 +380,17 @@ def algorithmic_bytes(s: Spec, lens: np.ndarray, fmt: str,
     """Bytes a decode step must move at least once: every valid cached token's
     K and V codes (+ their scales), Q in, O out, the block-table entries read
     and the context lengths.  ``unique_tokens`` counts shared blocks once."""
-    elem = {"fp16": 2, "int8": 1, "fp8": 1}[fmt]
+    elem = 2 if fmt == "fp16" else 1
     ntok = int(unique_tokens if unique_tokens is not None else lens.sum())
     per_tok = s.Hkv * 2 * s.D * elem
-    if fmt == "int8":
-        per_tok += s.Hkv * 2 * (s.D // s.G) * 4
+    G = s.G if fmt != "fp16" else 0
+    if G > 0:                                              # per token-group scales
+        per_tok += s.Hkv * 2 * (s.D // G) * 4
     total = ntok * per_tok
-    if fmt == "fp8":
+    if fmt in ("fp8", "e5m2") and G == 0:                  # static per-head scales
         total += 2 * s.Hkv * 4
+    if fmt == "int8" and G == 0:                           # static per-channel scales
+        total += 2 * s.Hkv * s.D * 4
     total += 2 * s.B * s.Hq * s.D * 2                     # q in, out
     total += int(sum(-(-int(n) // s.BS) for n in lens)) * 4   # table entries
     total += 4 * s.B                                       # context_lens

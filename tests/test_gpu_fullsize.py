@@ -15,6 +15,7 @@ import pytest
 import torch
 
 from oracle import expected as E
+from paged_quantized_kv_cache_amd import kvq
 from paged_quantized_kv_cache_amd import workloads as W
 from paged_quantized_kv_cache_amd.harness import DecodeCase
 
@@ -44,7 +45,7 @@ def _check_layer(case, layer, seqs):
     k16 = d.k.index_select(0, idx).cpu().numpy()
     v16 = d.v.index_select(0, idx).cpu().numpy()
     sk = sv = None
-    if fmt == "fp8":
+    if kvq.scale_mode(fmt, s.G) in ("head", "channel"):   # static scales
         sk = case.pools[layer].k_scale.cpu().numpy()
         sv = case.pools[layer].v_scale.cpu().numpy()
     kq = E.quantize(k16, fmt, s.G, sk)
@@ -58,7 +59,7 @@ def _check_layer(case, layer, seqs):
             gk, gv = gk.view(np.uint16), gv.view(np.uint16)
         assert np.array_equal(gk, kq.codes[t]), "K codes (seq %d)" % b
         assert np.array_equal(gv, vq.codes[t]), "V codes (seq %d)" % b
-        if fmt == "int8":
+        if kq.scales is not None:
             assert np.array_equal(codes[i]["k_scale"], kq.scales[t]), "K scales (seq %d)" % b
             assert np.array_equal(codes[i]["v_scale"], vq.scales[t]), "V scales (seq %d)" % b
     q = d.q.cpu().numpy()[seqs]
@@ -87,7 +88,8 @@ def _run(name, layers=(0,)):
 
 
 @pytest.mark.parametrize("name", ["c1_tiny", "c2_mha", "c3_gqa", "c3_gqa_fp16",
-                                  "c4_long_bs16", "c4_long_bs32"])
+                                  "c4_long_bs16", "c4_long_bs32", "c4_long_e5m2",
+                                  "c3_fp8_token", "c3_int8_channel"])
 def test_full_size_single_layer(name, gpu):
     _run(name)
 

@@ -15,6 +15,7 @@ import torch
 
 import oracle
 from oracle import expected as E
+from paged_quantized_kv_cache_amd import kvq
 from paged_quantized_kv_cache_amd import workloads as W
 from paged_quantized_kv_cache_amd.harness import DecodeCase, tile_offsets
 
@@ -45,6 +46,22 @@ SMALL_CASES = {
                                lens="fixed", lens_args=(2, 40, 97)),
     "fp16_d64_mqa": small("c1_tiny", fmt="fp16", G=0, B=3, pool_blocks=0,
                           lens="fixed", lens_args=(7, 64, 90)),
+    # format variants: E5M2, FP8 with dynamic per-token / per-group scales,
+    # INT8 with static per-channel scales
+    "e5m2_bs16": small("c4_long_bs16", fmt="e5m2", B=3, Hq=8, Hkv=2, lens="fixed",
+                       lens_args=(1, 150, 1100)),
+    "e5m2_d64_bs32": small("c1_tiny", fmt="e5m2", G=0, B=3, Hq=16, Hkv=1, BS=32,
+                           pool_blocks=0, lens="fixed", lens_args=(2, 40, 97)),
+    "fp8_token_g128": small("c3_gqa", fmt="fp8", G=128, B=5, Hq=8, Hkv=2, lens="fixed",
+                            lens_args=(1, 17, 100, 257, 700)),
+    "fp8_g64_bs32": small("c3_gqa", fmt="fp8", G=64, BS=32, B=4, Hq=16, Hkv=2,
+                          lens="fixed", lens_args=(31, 32, 65, 400)),
+    "fp8_d64_token": small("c1_tiny", fmt="fp8", G=64, B=3, pool_blocks=0,
+                           lens="fixed", lens_args=(7, 64, 90)),
+    "int8_channel": small("c3_gqa", fmt="int8", G=0, B=5, Hq=8, Hkv=2, lens="fixed",
+                          lens_args=(1, 17, 100, 257, 700)),
+    "int8_channel_d64_bs32": small("c1_tiny", fmt="int8", G=0, B=3, Hq=16, Hkv=1, BS=32,
+                                   pool_blocks=0, lens="fixed", lens_args=(2, 40, 97)),
 }
 
 
@@ -58,7 +75,7 @@ def _expected(case: DecodeCase, layer: int, seqs=None):
     d = case.data[layer]
     k16, v16 = _host(d.k), _host(d.v)
     sk = sv = None
-    if fmt == "fp8":
+    if kvq.scale_mode(fmt, s.G) in ("head", "channel"):   # static scales
         sk = _host(case.pools[layer].k_scale)
         sv = _host(case.pools[layer].v_scale)
     seqs = list(range(s.B)) if seqs is None else list(seqs)
@@ -84,7 +101,7 @@ def _check_codes(case, layer, kq, vq, toks, seqs):
             gk, gv = gk.view(np.uint16), gv.view(np.uint16)
         assert np.array_equal(gk, ek), "K codes differ (seq %d)" % b
         assert np.array_equal(gv, ev), "V codes differ (seq %d)" % b
-        if fmt == "int8":
+        if kq.scales is not None:
             assert np.array_equal(got[i]["k_scale"], kq.scales[t]), "K scales (seq %d)" % b
             assert np.array_equal(got[i]["v_scale"], vq.scales[t]), "V scales (seq %d)" % b
 

@@ -173,6 +173,13 @@ def test_bad_arguments_rejected_before_any_device_work(lib):
                                dummy, dummy, dummy, dummy, None) == -2
     assert lib.kvq_cache_write(dummy, dummy, dummy, 1, 1, 64, 16, 4, 7, 64,
                                dummy, dummy, dummy, dummy, None) == -2
+    # E5M2 has static per-head scales only; group sizes are 0, 64 or 128
+    assert lib.kvq_cache_write(dummy, dummy, dummy, 1, 1, 128, 16, 4, 3, 64,
+                               dummy, dummy, dummy, dummy, None) == -2
+    assert lib.kvq_cache_write(dummy, dummy, dummy, 1, 1, 128, 16, 4, 1, 32,
+                               dummy, dummy, dummy, dummy, None) == -2
+    assert lib.kvq_cache_write(dummy, dummy, dummy, 1, 1, 128, 16, 4, 2, 96,
+                               dummy, dummy, dummy, dummy, None) == -2
     # null pointers
     assert lib.kvq_cache_write(None, dummy, dummy, 1, 1, 64, 16, 4, 1, 64,
                                dummy, dummy, dummy, dummy, None) == -1
@@ -198,6 +205,10 @@ def test_bad_arguments_rejected_before_any_device_work(lib):
     assert dec(split=16) == -3                    # needs a workspace
     assert dec() == -3
     assert dec(D=96) == -2
+    assert dec(dt=3, G=64) == -2                  # E5M2: static scales only
+    assert dec(dt=3, G=0) == -3                   # E5M2 per head: valid, needs a workspace
+    assert dec(dt=1, G=0) == -3                   # INT8 per channel: valid
+    assert dec(dt=2, G=64) == -3                  # E4M3 per group: valid
     assert dec(B=0) == 0
     assert dec(dt=1, ks=None) == -1
     assert lib.kvq_copy_blocks(dummy, 1, 1, 64, 16, 4, 1, 64, dummy, dummy, None, None,

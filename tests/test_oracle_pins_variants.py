@@ -167,3 +167,13 @@ def test_expected_quantize_modes():
     assert q.scales.shape == (20, 2, 2)
     q = E.quantize(x16, "int8", 0, cs)
     assert q.scales is None and np.array_equal(q.deq, q.codes * np.float64(np.float32(0.03)))
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+def test_fp8_static_zero_scale_gives_code_zero(fmt):
+    x16 = np.random.default_rng(14).standard_normal((5, 2, 64)).astype(np.float16)
+    x16[:, 1] = 0                                   # an all-zero head: scale 0
+    S = np.array([0.01, 0.0], np.float32)
+    codes = oracle.fp8_quantize(x16, S, fmt)
+    assert np.all(codes[:, 1] == 0)
+    assert np.all(oracle.fp8_dequantize(codes, S, fmt)[:, 1] == 0)
