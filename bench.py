@@ -125,6 +125,38 @@ def copy_bandwidth(nbytes: int = 2 << 30, reps: int = 5) -> float:
     return 2 * nbytes / dt / 1e9
 
 
+def swap_bandwidth(case, spec, reps: int = 3) -> dict:
+    """Swap every block layer 0 uses out to a pinned host buffer and back in
+    place; bytes of the swap slots over event time, best of ``reps``."""
+    import torch
+    from paged_quantized_kv_cache_amd import kvq
+    p = case.pools[0]
+    blocks = sorted(int(b) for b in case.layout.used_blocks)
+    slot = kvq.kvq_swap_block_bytes(spec.Hkv, spec.D, spec.BS, p.fmt, spec.G)
+    buf = torch.empty(len(blocks) * slot, dtype=torch.uint8, pin_memory=True)
+    pairs = torch.tensor([[b, i] for i, b in enumerate(blocks)], dtype=torch.int32,
+                         device=p.k_pool.device)
+    best = {}
+    for name in ("out", "in"):
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            if name == "out":
+                kvq.kvq_swap_out(pairs, p.k_pool, p.v_pool, p.k_scale, p.v_scale, p.fmt,
+                                 spec.G, buf)
+            else:
+                kvq.kvq_swap_in(pairs, buf, p.k_pool, p.v_pool, p.k_scale, p.v_scale,
+                                p.fmt, spec.G)
+            e1.record()
+            torch.cuda.synchronize()
+            best[name] = min(best.get(name, 1e30), e0.elapsed_time(e1))
+    nbytes = len(blocks) * slot
+    return {"blocks": len(blocks), "bytes": nbytes, "staging": "pinned host",
+            "out_ms": round(best["out"], 3), "in_ms": round(best["in"], 3),
+            "out_GBps": round(nbytes / (best["out"] * 1e-3) / 1e9, 1),
+            "in_GBps": round(nbytes / (best["in"] * 1e-3) / 1e9, 1)}
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -136,6 +168,10 @@ def main(argv=None) -> int:
     ap.add_argument("--cpu-min-seconds", type=float, default=10.0)
     ap.add_argument("--copy-calib-bytes", type=int, default=0,
                     help="also run one plain copy of this many bytes (counter calibration)")
+    ap.add_argument("--swap", action="store_true",
+                    help="also time swapping layer 0's blocks out to pinned host "
+                         "memory and back (kvq_swap_out / kvq_swap_in), outside the "
+                         "timed steps")
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -220,6 +256,7 @@ def main(argv=None) -> int:
     achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
     traffic = load_traffic(spec.name)
 
+    swap = swap_bandwidth(case, spec) if args.swap else None
     copy_gbps = copy_bandwidth()
     if args.copy_calib_bytes:
         a = torch.zeros(args.copy_calib_bytes, dtype=torch.uint8, device=dev)
@@ -267,6 +304,7 @@ def main(argv=None) -> int:
         },
         "decode_ms_per_layer": [round(float(x), 5) for x in per_layer_ms] if nl > 1 else None,
         "measured_copy_gbps": round(copy_gbps, 1),
+        "swap": swap,
         "setup_s": round(setup_s, 1),
     }
     if args.cpu_seqs > 0:

@@ -214,6 +214,49 @@ KVQ_API kvq_status kvq_copy_blocks(const int32_t *block_pairs, int32_t num_pairs
                            void *v_pool, float *k_scale, float *v_scale,
                            void *stream);
 
+/*
+ * Swap of whole blocks between one layer's pools and a staging buffer, for
+ * preemption: under memory pressure a low-priority request's KV is swapped
+ * out and brought back later (xpshop.cn article 312, s3 and s6), possibly
+ * into other physical blocks (the caller rewrites the block table).
+ *
+ * A swap slot holds one block: [K codes][V codes][K scales][V scales] (the
+ * scales only for per-group formats; static scales belong to the layer, not
+ * to blocks), padded to 256 bytes; kvq_swap_block_bytes returns its size
+ * (SIZE_MAX for unsupported arguments).  The buffer holds num_slots slots,
+ * is owned by the caller and may be device memory or pinned host memory
+ * (hipHostMalloc), which the kernel reads and writes across the bus.
+ *
+ *   block_slot_pairs  int32 [num_pairs][2] = (pool block, swap slot),
+ *                     device-accessible; pairs with a block outside the pool
+ *                     or a slot outside [0, num_slots) are skipped.  The
+ *                     slots (swap out) or blocks (swap in) written must be
+ *                     distinct.
+ *   kvq_swap_out      copies each pool block into its slot of dst.
+ *   kvq_swap_in       copies each slot of src into its pool block.
+ * Asynchronous on stream; the caller synchronizes before it reads a host
+ * buffer or reuses the swapped-out blocks.
+ */
+KVQ_API size_t kvq_swap_block_bytes(int32_t num_kv_heads, int32_t head_dim,
+                                    int32_t block_size, int32_t dtype,
+                                    int32_t group_size);
+
+KVQ_API kvq_status kvq_swap_out(const int32_t *block_slot_pairs, int32_t num_pairs,
+                        int32_t num_kv_heads, int32_t head_dim,
+                        int32_t block_size, int32_t num_blocks,
+                        int32_t dtype, int32_t group_size,
+                        const void *k_pool, const void *v_pool,
+                        const float *k_scale, const float *v_scale,
+                        void *dst, int64_t num_slots, void *stream);
+
+KVQ_API kvq_status kvq_swap_in(const int32_t *block_slot_pairs, int32_t num_pairs,
+                       int32_t num_kv_heads, int32_t head_dim,
+                       int32_t block_size, int32_t num_blocks,
+                       int32_t dtype, int32_t group_size,
+                       const void *src, int64_t num_slots,
+                       void *k_pool, void *v_pool,
+                       float *k_scale, float *v_scale, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -9,8 +9,17 @@ sequence must write into a block that others still share.
 
 Physical ids come from a shuffled free list, so consecutive logical blocks
 land anywhere in the pool.  The manager never touches device memory: it
-returns slots for ``kvq_cache_write`` and (src, dst) block pairs for
-``kvq_copy_blocks``.
+returns slots for ``kvq_cache_write``, (src, dst) block pairs for
+``kvq_copy_blocks`` and (block, swap slot) pairs for ``kvq_swap_out`` /
+``kvq_swap_in``.
+
+Eviction and preemption (xpshop.cn article 402, s3: blocks are evicted by
+block-level LRU, so a long session's early context is not lost to its own
+tail; article 312, s3 and s6: under memory pressure a low-priority request
+is preempted, its KV swapped out and brought back later): every block keeps
+the step it was last read at (``touch``), ``preempt`` picks victims by
+priority and then by least recent use, and ``swap_out`` / ``swap_in`` move a
+sequence's blocks to host swap slots and back into freshly allocated blocks.
 """
 from __future__ import annotations
 
@@ -26,6 +35,25 @@ class PoolExhausted(RuntimeError):
     """Raised when no free block is left (a serving layer would queue)."""
 
 
+class SwapSpace:
+    """Host-side free list of swap slots (one block each)."""
+
+    def __init__(self, num_slots: int):
+        self.num_slots = num_slots
+        self._free: List[int] = list(range(num_slots))[::-1]
+
+    def alloc(self, n: int) -> List[int]:
+        if n > len(self._free):
+            raise PoolExhausted("no free swap slot")
+        return [self._free.pop() for _ in range(n)]
+
+    def release(self, slots: List[int]) -> None:
+        self._free.extend(slots)
+
+    def num_free(self) -> int:
+        return len(self._free)
+
+
 class BlockManager:
     def __init__(self, num_blocks: int, block_size: int,
                  rng: Optional[np.random.Generator] = None):
@@ -38,8 +66,11 @@ class BlockManager:
             order = rng.permutation(num_blocks)
         self._free: List[int] = [int(x) for x in order[::-1]]  # pop() = order[0]
         self.refcount = np.zeros(num_blocks, np.int32)
+        self.last_use = np.zeros(num_blocks, np.int64)  # step of the last read
+        self._clock = 0
         self._blocks: Dict[int, List[int]] = {}
         self._len: Dict[int, int] = {}
+        self._swapped: Dict[int, List[int]] = {}         # seq -> swap slots
 
     # ------------------------------------------------------------ sequences
     def add_sequence(self, seq: int) -> None:
@@ -48,9 +79,14 @@ class BlockManager:
         self._blocks[seq] = []
         self._len[seq] = 0
 
-    def drop_sequence(self, seq: int) -> None:
-        for blk in self._blocks.pop(seq):
-            self._release(blk)
+    def drop_sequence(self, seq: int, space: Optional[SwapSpace] = None) -> None:
+        if seq in self._swapped:
+            slots = self._swapped.pop(seq)
+            if space is not None:
+                space.release(slots)
+        else:
+            for blk in self._blocks.pop(seq):
+                self._release(blk)
         del self._len[seq]
 
     def fork(self, parent: int, child: int) -> None:
@@ -91,6 +127,65 @@ class BlockManager:
                 copy = (last, dst)
         self._len[seq] = n + 1
         return blocks[-1] * self.block_size + off, copy
+
+    # ------------------------------------------------------------ LRU, swap
+    def touch(self, seqs) -> None:
+        """One decode step read every block of ``seqs``."""
+        self._clock += 1
+        for s in seqs:
+            for blk in self._blocks[s]:
+                self.last_use[blk] = self._clock
+
+    def lru_blocks(self) -> List[int]:
+        """Blocks in use, least recently read first (ties by id)."""
+        used = np.nonzero(self.refcount > 0)[0]
+        return [int(b) for b in used[np.lexsort((used, self.last_use[used]))]]
+
+    def resident(self, seq: int) -> bool:
+        return seq in self._blocks
+
+    def swap_out(self, seq: int, space: SwapSpace) -> List[Tuple[int, int]]:
+        """Move ``seq`` to host swap slots.  Returns the (block, slot) pairs
+        to copy with ``kvq_swap_out``; its blocks are released at once, so
+        the copy must be issued before anything writes into them (same
+        stream order is enough).  Blocks still shared with resident
+        sequences stay in the pool for them."""
+        blocks = self._blocks.pop(seq)
+        slots = space.alloc(len(blocks))
+        for blk in blocks:
+            self._release(blk)
+        self._swapped[seq] = slots
+        return list(zip(blocks, slots))
+
+    def swap_in(self, seq: int, space: SwapSpace) -> List[Tuple[int, int]]:
+        """Bring ``seq`` back into freshly allocated blocks.  Returns the
+        (block, slot) pairs to copy with ``kvq_swap_in``; the slots are free
+        again once that copy has run."""
+        slots = self._swapped[seq]
+        if len(slots) > len(self._free):
+            raise PoolExhausted("not enough free KV blocks to swap in")
+        del self._swapped[seq]
+        blocks = [self._alloc() for _ in slots]
+        self._blocks[seq] = blocks
+        space.release(slots)
+        return list(zip(blocks, slots))
+
+    def preempt(self, need_blocks: int, priority: Dict[int, int],
+                space: SwapSpace) -> List[Tuple[int, List[Tuple[int, int]]]]:
+        """Swap out resident sequences until ``need_blocks`` blocks are free:
+        lowest priority first, then the sequence whose blocks were read least
+        recently.  Returns ``[(seq, pairs)]`` in swap-out order."""
+        out = []
+        cands = [s for s in self._blocks if self._blocks[s]]
+        cands.sort(key=lambda s: (priority.get(s, 0),
+                                  int(self.last_use[self._blocks[s]].max()), s))
+        for s in cands:
+            if len(self._free) >= need_blocks:
+                break
+            out.append((s, self.swap_out(s, space)))
+        if len(self._free) < need_blocks:
+            raise PoolExhausted("preemption cannot free %d blocks" % need_blocks)
+        return out
 
     # ------------------------------------------------------------ tables
     def tables(self, num_seqs: int, max_blocks: Optional[int] = None,

@@ -467,4 +467,87 @@ kvq_status kvq_copy_blocks(const int32_t *block_pairs, int32_t num_pairs, int32_
     return launch_status();
 }
 
+size_t kvq_swap_block_bytes(int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                            int32_t dtype, int32_t group_size)
+{
+    if (num_kv_heads <= 0 || check_format(dtype, head_dim, block_size, group_size) != KVQ_OK)
+        return SIZE_MAX;
+    const int eb = dtype == KVQ_FP16 ? 2 : 1;
+    const bool group_scales = (dtype == KVQ_INT8 || dtype == KVQ_FP8_E4M3) && group_size > 0;
+    const size_t codes = (size_t)num_kv_heads * block_size * head_dim * eb;
+    const size_t scales =
+        group_scales ? (size_t)num_kv_heads * block_size * (head_dim / group_size) * 4 : 0;
+    return (2 * codes + 2 * scales + 255) / 256 * 256;
+}
+
+namespace {
+
+kvq_status swap_blocks(const int32_t *pairs, int32_t num_pairs, int32_t num_kv_heads,
+                       int32_t head_dim, int32_t block_size, int32_t num_blocks, int32_t dtype,
+                       int32_t group_size, void *k_pool, void *v_pool, float *k_scale,
+                       float *v_scale, void *buffer, int64_t num_slots, int to_buffer,
+                       void *stream)
+{
+    kvq_status st = check_format(dtype, head_dim, block_size, group_size);
+    if (st != KVQ_OK)
+        return st;
+    if (num_pairs < 0 || num_kv_heads <= 0 || num_blocks <= 0 || num_slots < 0)
+        return KVQ_ERR_INVALID_ARG;
+    if (num_pairs == 0)
+        return KVQ_OK;
+    const bool group_scales = (dtype == KVQ_INT8 || dtype == KVQ_FP8_E4M3) && group_size > 0;
+    if (!pairs || !k_pool || !v_pool || !buffer || (group_scales && (!k_scale || !v_scale)))
+        return KVQ_ERR_INVALID_ARG;
+    if (!aligned16(k_pool) || !aligned16(v_pool) || !aligned16(buffer) ||
+        (group_scales && (!aligned16(k_scale) || !aligned16(v_scale))))
+        return KVQ_ERR_INVALID_ARG;
+    st = check_device();
+    if (st != KVQ_OK)
+        return st;
+    SwapParams p;
+    p.pairs = pairs;
+    p.k_pool = static_cast<uint8_t *>(k_pool);
+    p.v_pool = static_cast<uint8_t *>(v_pool);
+    p.k_scale = group_scales ? reinterpret_cast<uint8_t *>(k_scale) : nullptr;
+    p.v_scale = group_scales ? reinterpret_cast<uint8_t *>(v_scale) : nullptr;
+    p.buf = static_cast<uint8_t *>(buffer);
+    const int eb = dtype == KVQ_FP16 ? 2 : 1;
+    p.block_bytes = (int64_t)num_kv_heads * block_size * head_dim * eb;
+    p.scale_bytes =
+        group_scales ? (int64_t)num_kv_heads * block_size * (head_dim / group_size) * 4 : 0;
+    p.slot_bytes = (int64_t)kvq_swap_block_bytes(num_kv_heads, head_dim, block_size, dtype,
+                                                 group_size);
+    p.num_slots = num_slots;
+    p.num_blocks = num_blocks;
+    p.to_buffer = to_buffer;
+    const unsigned chunks = (unsigned)((p.block_bytes / 16 + 255) / 256);
+    hipLaunchKernelGGL(swap_blocks_kernel, dim3((unsigned)num_pairs, chunks), dim3(256), 0,
+                       static_cast<hipStream_t>(stream), p);
+    return launch_status();
+}
+
+}  // namespace
+
+kvq_status kvq_swap_out(const int32_t *block_slot_pairs, int32_t num_pairs,
+                        int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                        int32_t num_blocks, int32_t dtype, int32_t group_size,
+                        const void *k_pool, const void *v_pool, const float *k_scale,
+                        const float *v_scale, void *dst, int64_t num_slots, void *stream)
+{
+    return swap_blocks(block_slot_pairs, num_pairs, num_kv_heads, head_dim, block_size,
+                       num_blocks, dtype, group_size, const_cast<void *>(k_pool),
+                       const_cast<void *>(v_pool), const_cast<float *>(k_scale),
+                       const_cast<float *>(v_scale), dst, num_slots, 1, stream);
+}
+
+kvq_status kvq_swap_in(const int32_t *block_slot_pairs, int32_t num_pairs, int32_t num_kv_heads,
+                       int32_t head_dim, int32_t block_size, int32_t num_blocks, int32_t dtype,
+                       int32_t group_size, const void *src, int64_t num_slots, void *k_pool,
+                       void *v_pool, float *k_scale, float *v_scale, void *stream)
+{
+    return swap_blocks(block_slot_pairs, num_pairs, num_kv_heads, head_dim, block_size,
+                       num_blocks, dtype, group_size, k_pool, v_pool, k_scale, v_scale,
+                       const_cast<void *>(src), num_slots, 0, stream);
+}
+
 }  // extern "C"

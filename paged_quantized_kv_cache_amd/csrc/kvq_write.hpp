@@ -194,4 +194,57 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(CopyParams p)
     }
 }
 
+// Swap of whole blocks between the pools and a caller-owned staging buffer
+// (device memory, or pinned host memory the GPU writes and reads across the
+// bus): preemption moves a sequence's blocks out and back in, possibly to
+// other physical blocks (xpshop.cn article 312, s3 and s6: under memory
+// pressure a low-priority request is preempted, its KV swapped out and
+// brought back later).
+// One swap slot holds [K codes][V codes][K scales][V scales] of one block
+// (scales only for per-group formats).  pairs[2i] = pool block, pairs[2i+1]
+// = swap slot; blockIdx.x = pair, grid-stride over 16-byte units.
+struct SwapParams {
+    const int32_t *pairs;
+    uint8_t *k_pool;
+    uint8_t *v_pool;
+    uint8_t *k_scale;           // per-group scale arrays as bytes (or null)
+    uint8_t *v_scale;
+    uint8_t *buf;
+    int64_t block_bytes;        // codes of one block in one pool
+    int64_t scale_bytes;        // scales of one block in one scale array
+    int64_t slot_bytes;         // one swap slot
+    int64_t num_slots;
+    int32_t num_blocks;
+    int32_t to_buffer;          // 1: pools -> buffer, 0: buffer -> pools
+};
+
+__global__ __launch_bounds__(256) void swap_blocks_kernel(SwapParams p)
+{
+    const int32_t blk = p.pairs[2 * blockIdx.x];
+    const int32_t slot = p.pairs[2 * blockIdx.x + 1];
+    if (blk < 0 || blk >= p.num_blocks || slot < 0 || slot >= p.num_slots)
+        return;
+    uint8_t *base = p.buf + (int64_t)slot * p.slot_bytes;
+    uint8_t *pool_ptr[4] = {p.k_pool + blk * p.block_bytes, p.v_pool + blk * p.block_bytes,
+                            p.k_scale ? p.k_scale + blk * p.scale_bytes : nullptr,
+                            p.v_scale ? p.v_scale + blk * p.scale_bytes : nullptr};
+    const int64_t len[4] = {p.block_bytes, p.block_bytes, p.k_scale ? p.scale_bytes : 0,
+                            p.v_scale ? p.scale_bytes : 0};
+    int64_t off = 0;
+    const int64_t stride = (int64_t)blockDim.x * gridDim.y;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        uint4 *pool16 = reinterpret_cast<uint4 *>(pool_ptr[r]);
+        uint4 *buf16 = reinterpret_cast<uint4 *>(base + off);
+        for (int64_t i = (int64_t)blockIdx.y * blockDim.x + threadIdx.x; i < len[r] / 16;
+             i += stride) {
+            if (p.to_buffer)
+                buf16[i] = pool16[i];
+            else
+                pool16[i] = buf16[i];
+        }
+        off += len[r];
+    }
+}
+
 }  // namespace kvq

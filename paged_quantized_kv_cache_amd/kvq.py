@@ -39,10 +39,13 @@ def scale_mode(fmt: str, group_size: int) -> str:
     if group_size > 0:
         return "group"
     return "channel" if fmt == "int8" else "head"
+
+
 STATUS = {0: "KVQ_OK", -1: "KVQ_ERR_INVALID_ARG", -2: "KVQ_ERR_UNSUPPORTED",
           -3: "KVQ_ERR_WORKSPACE", -4: "KVQ_ERR_HIP"}
 EXPORTS = ("kvq_status_string", "kvq_version", "kvq_cache_write",
-           "kvq_paged_decode", "kvq_decode_workspace_size", "kvq_copy_blocks")
+           "kvq_paged_decode", "kvq_decode_workspace_size", "kvq_copy_blocks",
+           "kvq_swap_block_bytes", "kvq_swap_out", "kvq_swap_in")
 
 
 class KvqError(RuntimeError):
@@ -84,6 +87,14 @@ def lib() -> ctypes.CDLL:
             L.kvq_copy_blocks.restype = i32
             L.kvq_copy_blocks.argtypes = [P, i32, i32, i32, i32, i32, i32, i32,
                                           P, P, P, P, P]
+            L.kvq_swap_block_bytes.restype = ctypes.c_size_t
+            L.kvq_swap_block_bytes.argtypes = [i32] * 5
+            L.kvq_swap_out.restype = i32
+            L.kvq_swap_out.argtypes = [P, i32, i32, i32, i32, i32, i32, i32,
+                                       P, P, P, P, P, i64, P]
+            L.kvq_swap_in.restype = i32
+            L.kvq_swap_in.argtypes = [P, i32, i32, i32, i32, i32, i32, i32,
+                                      P, i64, P, P, P, P, P]
             _lib = L
     return _lib
 
@@ -242,3 +253,51 @@ def kvq_copy_blocks(block_pairs: torch.Tensor, k_pool: torch.Tensor, v_pool: tor
                                _ptr(k_scale) if scale_ok else None,
                                _ptr(v_scale) if scale_ok else None, _stream(stream))
     _check(st, "kvq_copy_blocks")
+
+
+# ------------------------------------------------------------------ swap
+def kvq_swap_block_bytes(num_kv_heads: int, head_dim: int, block_size: int, fmt: str,
+                         group_size: int = 0) -> int:
+    """Bytes of one swap slot (one block's codes and per-group scales)."""
+    n = lib().kvq_swap_block_bytes(num_kv_heads, head_dim, block_size, _fmt(fmt),
+                                   group_size)
+    if n == ctypes.c_size_t(-1).value:
+        raise ValueError("unsupported swap arguments")
+    return int(n)
+
+
+def _swap_args(pairs, k_pool, fmt, group_size, buf):
+    num_blocks, hkv, bs, d = _pool_geometry(k_pool, fmt)
+    if pairs.dtype != torch.int32 or (pairs.numel() and pairs.shape[-1] != 2):
+        raise ValueError("block_slot_pairs must be int32 [n][2]")
+    if buf.dtype != torch.uint8 or not buf.is_contiguous():
+        raise ValueError("swap buffer must be a contiguous uint8 tensor")
+    slot = kvq_swap_block_bytes(hkv, d, bs, fmt, group_size)
+    return num_blocks, hkv, bs, d, pairs.numel() // 2, buf.numel() // slot
+
+
+def kvq_swap_out(block_slot_pairs: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
+                 k_scale: Optional[torch.Tensor], v_scale: Optional[torch.Tensor],
+                 fmt: str, group_size: int, dst: torch.Tensor, stream=None) -> None:
+    """Copy pool blocks into swap slots of ``dst`` (device or pinned host
+    uint8 buffer of whole slots).  ``block_slot_pairs``: int32 [n][2]."""
+    nb, hkv, bs, d, n, slots = _swap_args(block_slot_pairs, k_pool, fmt, group_size, dst)
+    grp = scale_mode(fmt, group_size) == "group"
+    st = lib().kvq_swap_out(_ptr(block_slot_pairs), n, hkv, d, bs, nb, _fmt(fmt), group_size,
+                            _ptr(k_pool), _ptr(v_pool), _ptr(k_scale) if grp else None,
+                            _ptr(v_scale) if grp else None, _ptr(dst), slots, _stream(stream))
+    _check(st, "kvq_swap_out")
+
+
+def kvq_swap_in(block_slot_pairs: torch.Tensor, src: torch.Tensor, k_pool: torch.Tensor,
+                v_pool: torch.Tensor, k_scale: Optional[torch.Tensor],
+                v_scale: Optional[torch.Tensor], fmt: str, group_size: int,
+                stream=None) -> None:
+    """Copy swap slots of ``src`` into pool blocks."""
+    nb, hkv, bs, d, n, slots = _swap_args(block_slot_pairs, k_pool, fmt, group_size, src)
+    grp = scale_mode(fmt, group_size) == "group"
+    st = lib().kvq_swap_in(_ptr(block_slot_pairs), n, hkv, d, bs, nb, _fmt(fmt), group_size,
+                           _ptr(src), slots, _ptr(k_pool), _ptr(v_pool),
+                           _ptr(k_scale) if grp else None, _ptr(v_scale) if grp else None,
+                           _stream(stream))
+    _check(st, "kvq_swap_in")

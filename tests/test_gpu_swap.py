@@ -1,0 +1,94 @@
+"""GPU: swap of whole blocks out of the pools and back (preemption; xpshop.cn
+article 312, s3 and s6), through the C ABI.
+
+A set of sequences is swapped out to a staging buffer (pinned host memory or
+device memory), the staged bytes are checked against the pool bytes, the old
+blocks are poisoned, and the data are swapped back into *other* physical
+blocks; after the block tables are rewritten, decode must give bit-identical
+output (the result depends only on the logical content, never on where the
+blocks sit).
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+from paged_quantized_kv_cache_amd import kvq
+from paged_quantized_kv_cache_amd.block_manager import SHARED_HINT
+from paged_quantized_kv_cache_amd.harness import DecodeCase
+
+from test_gpu_parity import SMALL_CASES
+
+pytestmark = pytest.mark.gpu
+
+ID_MASK = SHARED_HINT - 1
+
+
+def _block_bytes(pool, blk):
+    return pool[blk].reshape(-1).view(torch.uint8)
+
+
+@pytest.mark.parametrize("staging", ["pinned_host", "device"])
+@pytest.mark.parametrize("name", ["gqa_int8_g64_outliers", "fp8_token_g128", "gqa_fp16",
+                                  "e5m2_bs16", "int8_channel"])
+def test_swap_round_trip_preserves_decode(name, staging, gpu):
+    print("case", name, staging, flush=True)
+    spec = dataclasses.replace(SMALL_CASES[name], pool_blocks=1024)
+    case = DecodeCase(spec, device=gpu, gen_device="cpu")
+    case.setup_layer(0)
+    p = case.pools[0]
+    ws = case.workspace(0)
+    out0 = case.decode(0, workspace=ws).clone()
+
+    bt = case.block_tables.cpu().numpy()
+    nblk = -(-case.lens // spec.BS)
+    victims = list(range(0, spec.B, 2))
+    old = sorted({int(bt[b, i]) & ID_MASK for b in victims for i in range(nblk[b])})
+    used = {int(x) & ID_MASK for b in range(spec.B) for x in bt[b, :nblk[b]]}
+    free = [x for x in range(p.k_pool.shape[0]) if x not in used and x != case.pad_block]
+    new = free[:len(old)]
+    assert len(new) == len(old)
+
+    slot_bytes = kvq.kvq_swap_block_bytes(spec.Hkv, spec.D, spec.BS, p.fmt, spec.G)
+    n = len(old)
+    if staging == "pinned_host":
+        buf = torch.empty(n * slot_bytes, dtype=torch.uint8, pin_memory=True)
+    else:
+        buf = torch.empty(n * slot_bytes, dtype=torch.uint8, device=gpu)
+    buf.fill_(0xA5)
+    pairs_out = torch.tensor([[b, i] for i, b in enumerate(old)], dtype=torch.int32, device=gpu)
+    kvq.kvq_swap_out(pairs_out, p.k_pool, p.v_pool, p.k_scale, p.v_scale, p.fmt, spec.G, buf)
+    torch.cuda.synchronize()
+
+    # the staged slot holds the block's K codes, V codes and per-group scales
+    group = kvq.scale_mode(p.fmt, spec.G) == "group"
+    host = buf.cpu()
+    for i, blk in enumerate(old):
+        parts = [_block_bytes(p.k_pool, blk), _block_bytes(p.v_pool, blk)]
+        if group:
+            parts += [_block_bytes(p.k_scale, blk), _block_bytes(p.v_scale, blk)]
+        want = torch.cat(parts).cpu()
+        got = host[i * slot_bytes: i * slot_bytes + want.numel()]
+        assert torch.equal(got, want), "slot %d (block %d)" % (i, blk)
+
+    # poison the old blocks, bring the data back into other blocks
+    idx = torch.tensor(old, dtype=torch.long, device=gpu)
+    p.k_pool.index_fill_(0, idx, 0xFF if p.fmt != "fp16" else float("nan"))
+    p.v_pool.index_fill_(0, idx, 0xFF if p.fmt != "fp16" else float("nan"))
+    if group:
+        p.k_scale.index_fill_(0, idx, float("nan"))
+        p.v_scale.index_fill_(0, idx, float("inf"))
+    pairs_in = torch.tensor([[nb, i] for i, nb in enumerate(new)], dtype=torch.int32, device=gpu)
+    kvq.kvq_swap_in(pairs_in, buf, p.k_pool, p.v_pool, p.k_scale, p.v_scale, p.fmt, spec.G)
+
+    remap = dict(zip(old, new))
+    bt2 = bt.copy()
+    for b in victims:
+        for i in range(nblk[b]):
+            e = int(bt[b, i])
+            bt2[b, i] = remap[e & ID_MASK] | (e & SHARED_HINT)
+    case.block_tables = torch.from_numpy(bt2).to(gpu)
+    out1 = case.decode(0, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out0, out1)

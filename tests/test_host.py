@@ -215,3 +215,85 @@ def test_bad_arguments_rejected_before_any_device_work(lib):
                                None) == -1
     assert lib.kvq_copy_blocks(None, 0, 1, 64, 16, 4, 1, 64, None, None, None, None,
                                None) == 0
+
+
+# ------------------------------------------------------------------ LRU, preemption, swap
+def test_block_lru_order_and_preemption():
+    from paged_quantized_kv_cache_amd.block_manager import (BlockManager, PoolExhausted,
+                                                            SwapSpace)
+    bm, space = BlockManager(16, 16), SwapSpace(8)
+    for s in (0, 2, 3):
+        bm.add_sequence(s)
+    for _ in range(40):
+        bm.append_slot(0)                           # 3 blocks
+    bm.fork(0, 1)                                   # shares them
+    for _ in range(20):
+        bm.append_slot(2)                           # 2 blocks
+    for _ in range(5):
+        bm.append_slot(3)                           # 1 block
+    bm.touch([2])
+    bm.touch([0, 1, 3])
+    order = bm.lru_blocks()
+    assert order[:2] == sorted(bm.blocks(2))        # read least recently
+    # seq 3 has the lowest priority; seq 2 is the least recently read of the rest
+    free0 = bm.num_free()
+    out = bm.preempt(free0 + 3, {0: 9, 1: 9, 2: 5, 3: 1}, space)
+    assert [s for s, _ in out] == [3, 2]
+    assert bm.num_free() == free0 + 3 and not bm.resident(2) and not bm.resident(3)
+    # preempting seq 1 alone frees nothing: its blocks are shared with seq 0
+    shared = bm.blocks(1)
+    pairs = bm.swap_out(1, space)
+    assert [b for b, _ in pairs] == shared and bm.num_free() == free0 + 3
+    assert all(bm.refcount[b] == 1 for b in shared)
+    with pytest.raises(PoolExhausted):
+        bm.preempt(100, {}, space)
+
+
+def test_swap_round_trip_bookkeeping():
+    from paged_quantized_kv_cache_amd.block_manager import BlockManager, SwapSpace
+    bm, space = BlockManager(12, 16, rng=np.random.default_rng(3)), SwapSpace(6)
+    bm.add_sequence(0)
+    bm.add_sequence(1)
+    for _ in range(37):
+        bm.append_slot(0)
+    for _ in range(3):
+        bm.append_slot(1)
+    old = bm.blocks(0)
+    pairs = bm.swap_out(0, space)
+    assert [b for b, _ in pairs] == old and space.num_free() == 3
+    slots = [s for _, s in pairs]
+    for _ in range(20):                             # someone else takes the blocks
+        bm.append_slot(1)
+    back = bm.swap_in(0, space)
+    assert [s for _, s in back] == slots and space.num_free() == 6
+    assert bm.length(0) == 37 and len(bm.blocks(0)) == 3
+    assert set(bm.blocks(0)).isdisjoint(bm.blocks(1))
+    slot, copy = bm.append_slot(0)                  # continues in its last block
+    assert copy is None and slot == bm.blocks(0)[-1] * 16 + 37 % 16
+    pairs = bm.swap_out(1, space)
+    bm.drop_sequence(1, space)                      # dropping a swapped sequence frees its slots
+    assert space.num_free() == 6
+
+
+def test_swap_block_bytes_and_arguments(lib):
+    from paged_quantized_kv_cache_amd import kvq
+    P = ctypes.c_void_p
+    sb = kvq.kvq_swap_block_bytes
+    assert sb(8, 128, 16, "int8", 64) == 2 * 8 * 16 * 128 + 2 * 8 * 16 * 2 * 4
+    assert sb(8, 128, 16, "fp16") == 2 * 8 * 16 * 128 * 2
+    assert sb(8, 128, 16, "fp8", 0) == 2 * 8 * 16 * 128
+    assert sb(8, 128, 32, "fp8", 128) == 2 * 8 * 32 * 128 + 2 * 8 * 32 * 4
+    assert sb(1, 64, 16, "int8", 0) == 2 * 16 * 64            # static scales stay put
+    assert sb(3, 64, 16, "e5m2") % 256 == 0
+    with pytest.raises(ValueError):
+        sb(8, 128, 16, "e5m2", 64)
+    dummy = P(16)
+    # null buffer / pairs; nothing to do
+    assert lib.kvq_swap_out(dummy, 1, 1, 64, 16, 4, 1, 64, dummy, dummy, dummy, dummy,
+                            None, 1, None) == -1
+    assert lib.kvq_swap_in(None, 1, 1, 64, 16, 4, 1, 64, dummy, 1, dummy, dummy, dummy,
+                           dummy, None) == -1
+    assert lib.kvq_swap_out(None, 0, 1, 64, 16, 4, 1, 64, None, None, None, None,
+                            None, 0, None) == 0
+    assert lib.kvq_swap_out(dummy, 1, 1, 96, 16, 4, 1, 64, dummy, dummy, dummy, dummy,
+                            dummy, 1, None) == -2
