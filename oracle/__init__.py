@@ -81,6 +81,9 @@ def _L():
             lib.orc_int8_quantize_channels.restype = i32
             lib.orc_int8_quantize_channels.argtypes = [P, i64, i32, i32, P, P]
             lib.orc_int8_dequantize_channels.argtypes = [P, i64, i32, i32, P, P]
+            lib.orc_prefill_attention.restype = i32
+            lib.orc_prefill_attention.argtypes = [P, P, P, P, P, i32, i32, i32,
+                                                  i32, ctypes.c_double, P]
             lib.orc_decode_attention.restype = i32
             lib.orc_decode_attention.argtypes = [P, P, P, P, i32, i32, i32,
                                                  i32, ctypes.c_double, P]
@@ -283,6 +286,34 @@ def decode_attention(q, K: np.ndarray, V: np.ndarray, context_lens,
                                    Hkv, d, sm, _ptr(out))
     if rc != 0:
         raise ValueError("oracle: invalid attention arguments (%d)" % rc)
+    return out
+
+
+def prefill_attention(q, K: np.ndarray, V: np.ndarray, chunk_lens, context_lens,
+                      softmax_scale: float = 0.0) -> np.ndarray:
+    """fp64 causal attention of chunk queries over contiguous K/V.
+
+    q: [sum n][Hq][d] fp16 (chunks in batch order); K, V: [sum ctx][Hkv][d]
+    fp64; sequence b's chunk is its last n_b tokens.  Returns [sum n][Hq][d]."""
+    qb = _f16_bits(q)
+    T, Hq, d = qb.shape
+    K = np.ascontiguousarray(K, np.float64)
+    V = np.ascontiguousarray(V, np.float64)
+    Hkv = K.shape[1]
+    n = np.asarray(chunk_lens, np.int64)
+    c = np.asarray(context_lens, np.int64)
+    B = n.size
+    cu_q = np.zeros(B + 1, np.int64)
+    cu_q[1:] = np.cumsum(n)
+    cu_k = np.zeros(B + 1, np.int64)
+    cu_k[1:] = np.cumsum(c)
+    assert cu_q[-1] == T and K.shape == (cu_k[-1], Hkv, d) and V.shape == K.shape
+    sm = float(softmax_scale) if softmax_scale else 1.0 / np.sqrt(d)
+    out = np.empty((T, Hq, d), np.float64)
+    rc = _L().orc_prefill_attention(_ptr(qb), _ptr(K), _ptr(V), _ptr(cu_q), _ptr(cu_k),
+                                    B, Hq, Hkv, d, sm, _ptr(out))
+    if rc != 0:
+        raise ValueError("oracle: invalid prefill arguments (%d)" % rc)
     return out
 
 

@@ -14,7 +14,7 @@ from typing import List, Optional, Sequence
 
 import numpy as np
 
-from . import (decode_attention, fp8_dequantize, fp8_dequantize_groups,
+from . import (decode_attention, prefill_attention, fp8_dequantize, fp8_dequantize_groups,
                fp8_quantize, fp8_quantize_groups, f16_to_f64,
                int8_dequantize, int8_dequantize_channels, int8_quantize,
                int8_quantize_channels)
@@ -60,6 +60,17 @@ def attention(q: np.ndarray, kq: Quantized, vq: Quantized,
     idx = np.concatenate([np.asarray(t, np.int64) for t in seq_tokens])
     lens = [len(t) for t in seq_tokens]
     return decode_attention(q, kq.deq[idx], vq.deq[idx], lens, softmax_scale)
+
+
+def prefill(q: np.ndarray, kq: Quantized, vq: Quantized,
+            seq_tokens: Sequence[np.ndarray], chunk_lens: Sequence[int],
+            softmax_scale: float = 0.0) -> np.ndarray:
+    """fp64 chunked-prefill attention: sequence b reads unique tokens
+    seq_tokens[b] in order, the last chunk_lens[b] of which are its chunk.
+    q: fp16 [sum chunk][Hq][D].  Returns [sum chunk][Hq][D] fp64."""
+    idx = np.concatenate([np.asarray(t, np.int64) for t in seq_tokens])
+    lens = [len(t) for t in seq_tokens]
+    return prefill_attention(q, kq.deq[idx], vq.deq[idx], chunk_lens, lens, softmax_scale)
 
 
 def tolerance_ok(got: np.ndarray, ref: np.ndarray, atol: float = 2e-3,

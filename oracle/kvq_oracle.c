@@ -502,6 +502,86 @@ ORC_API int orc_decode_attention(const uint16_t *q, const double *K,
 }
 
 /* ------------------------------------------------------------------ */
+/* Prefill (chunked) attention over contiguous dequantized K/V          */
+/* ([P3] s1.1: prefill computes the K/V of every prompt token and each   */
+/* token attends to the tokens before it; xpshop.cn article 312 s6:      */
+/* long prompts are processed in chunks).                                */
+/*                                                                      */
+/* Sequence b holds ctx_b tokens (its cached ones and then the n_b of    */
+/* this chunk, whose K/V are already in the cache); chunk token i is at  */
+/* position ctx_b - n_b + i and attends to tokens t <= that position.    */
+/* q     : [sum n][Hq][d] fp16 bits, chunks concatenated in batch order  */
+/* K, V  : [sum ctx][Hkv][d] fp64, sequences concatenated                */
+/* cu_q  : [B+1] chunk offsets in q;  cu_k : [B+1] offsets in K / V      */
+/* out   : [sum n][Hq][d] fp64                                          */
+/* ------------------------------------------------------------------ */
+ORC_API int orc_prefill_attention(const uint16_t *q, const double *K,
+                                  const double *V, const int64_t *cu_q,
+                                  const int64_t *cu_k, int B, int Hq, int Hkv,
+                                  int d, double sm, double *out)
+{
+    if (Hkv <= 0 || Hq % Hkv != 0)
+        return -2;
+    for (int b = 0; b < B; ++b) {
+        int64_t n = cu_q[b + 1] - cu_q[b], ctx = cu_k[b + 1] - cu_k[b];
+        if (n < 0 || n > ctx)
+            return -2;                  /* the chunk is part of the context */
+    }
+    int r = Hq / Hkv;
+    int64_t total = cu_q[B];
+    int err = 0;
+#pragma omp parallel for schedule(dynamic, 4) reduction(| : err)
+    for (int64_t row = 0; row < total; ++row) {
+        int b = 0;
+        while (cu_q[b + 1] <= row)
+            ++b;
+        int64_t n = cu_q[b + 1] - cu_q[b], ctx = cu_k[b + 1] - cu_k[b];
+        int64_t pos = ctx - n + (row - cu_q[b]);
+        int64_t len = pos + 1;          /* causal: tokens 0 .. pos */
+        double *z = (double *)malloc(sizeof(double) * (size_t)len);
+        double *qd = (double *)malloc(sizeof(double) * (size_t)d);
+        if (!z || !qd) {
+            free(z);
+            free(qd);
+            err = 1;
+            continue;
+        }
+        for (int g = 0; g < Hq; ++g) {
+            int h = g / r;
+            for (int i = 0; i < d; ++i)
+                qd[i] = orc_f16_to_f64(q[(row * Hq + g) * d + i]);
+            double zmax = -INFINITY;
+            for (int64_t t = 0; t < len; ++t) {
+                const double *kr = K + ((cu_k[b] + t) * Hkv + h) * d;
+                double acc = 0.0;
+                for (int i = 0; i < d; ++i)
+                    acc += qd[i] * kr[i];
+                z[t] = acc * sm;
+                if (z[t] > zmax)
+                    zmax = z[t];
+            }
+            double L = 0.0;
+            for (int64_t t = 0; t < len; ++t) {
+                z[t] = exp(z[t] - zmax);
+                L += z[t];
+            }
+            double *o = out + (row * Hq + g) * d;
+            for (int i = 0; i < d; ++i)
+                o[i] = 0.0;
+            for (int64_t t = 0; t < len; ++t) {
+                const double *vr = V + ((cu_k[b] + t) * Hkv + h) * d;
+                double w = z[t] / L;
+                for (int i = 0; i < d; ++i)
+                    o[i] += w * vr[i];
+            }
+        }
+        free(z);
+        free(qd);
+    }
+    return err ? -3 : 0;
+}
+
+/* ------------------------------------------------------------------ */
 /* KV byte formula ([P3] s1.2): 2 * batch * seq_len * layers * kv_heads  */
 /* * head_dim * bytes_per_element.  The INT8 per-group layout adds one   */
 /* fp32 scale per group for K and for V (the pages do not print this     */
