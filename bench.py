@@ -157,6 +157,115 @@ def swap_bandwidth(case, spec, reps: int = 3) -> dict:
             "in_GBps": round(nbytes / (best["in"] * 1e-3) / 1e9, 1)}
 
 
+PREFILL_METRIC = ("paged INT8 GQA prefill attention prompt-tokens/s + achieved TFLOP/s "
+                  "(% of MI355X fp16 dense MFMA peak)")
+MFMA_FP16_PEAK_TFLOPS = 2500.0
+
+
+def prefill_cpu_baseline(case, spec, q, chunk, min_seconds: float) -> dict:
+    """The oracle's chunked prefill on the first sequence of the workload,
+    repeated to about ``min_seconds``."""
+    import numpy as np
+    import oracle
+    from oracle import expected as E
+    from paged_quantized_kv_cache_amd import kvq
+    d = case.data[0]
+    fmt = spec.fmt_of_layer(0)
+    ids = np.asarray(case.layout.seq_tokens[0], np.int64)
+    sk = sv = None
+    if kvq.scale_mode(fmt, spec.G) in ("head", "channel"):
+        sk = case.pools[0].k_scale.cpu().numpy()
+        sv = case.pools[0].v_scale.cpu().numpy()
+    k16 = d.k.cpu().numpy()[ids]
+    v16 = d.v.cpu().numpy()[ids]
+    qh = q.cpu().numpy()[:int(chunk[0])]
+    total, passes = 0.0, 0
+    while total < min_seconds and passes < 20:
+        t0 = time.perf_counter()
+        kq = E.quantize(k16, fmt, spec.G, sk)
+        vq = E.quantize(v16, fmt, spec.G, sv)
+        E.prefill(qh, kq, vq, [np.arange(ids.size)], [int(chunk[0])])
+        total += time.perf_counter() - t0
+        passes += 1
+    return {"value": int(chunk[0]) * passes / total, "unit": "prompt-tokens/s",
+            "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": "sequence 0 (%d-token chunk over %d tokens): quantize its K/V, fp64 "
+                      "causal attention; %d pass(es), %.1f s"
+                      % (int(chunk[0]), ids.size, passes, total)}
+
+
+def run_prefill(args, spec) -> int:
+    """A prefill workload: one step writes every prompt token's K/V into the
+    pool (kvq_cache_write) and runs causal attention of the prompts over it
+    (kvq_paged_prefill)."""
+    import numpy as np
+    import torch
+
+    from paged_quantized_kv_cache_amd import kvq
+    from paged_quantized_kv_cache_amd import workloads as W
+    from paged_quantized_kv_cache_amd.harness import DecodeCase
+
+    kvq.lib()
+    dev = torch.device("cuda:0")
+    case = DecodeCase(spec, device=dev, poison=False)
+    case.gen(0)
+    case.alloc(0)
+    chunk = np.minimum(case.lens, spec.chunk)
+    if np.any(chunk != case.lens):
+        raise SystemExit("prefill workloads here write whole prompts (chunk >= every length)")
+    q = case.chunk_queries(chunk)
+    out = torch.empty_like(q)
+    flops = W.prefill_flops(spec, case.lens, chunk)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        case.prefill(0)
+        case.append(0)
+        if ev is not None:
+            ev[0].record(stream)
+        case.prefill_attention(0, chunk, q, out=out)
+        if ev is not None:
+            ev[1].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(ev[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+    att_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    achieved = flops / (att_ms * 1e-3) / 1e12
+    result = {
+        "metric": PREFILL_METRIC,
+        "value": float(chunk.sum()) / (ms_per_step * 1e-3),
+        "unit": "prompt-tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": spec.fmt,
+        "data": "synthetic (seeded N(0,1) fp16 K/V/Q with outlier channels, shuffled "
+                "block pool)",
+        "config": {"workload": spec.name, "description": spec.description,
+                   "num_seqs": spec.B, "num_q_heads": spec.Hq, "num_kv_heads": spec.Hkv,
+                   "head_dim": spec.D, "block_size": spec.BS, "kv_format": spec.fmt,
+                   "group_size": spec.G, "prompt_tokens": int(chunk.sum())},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 1),
+                     "peak": MFMA_FP16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / MFMA_FP16_PEAK_TFLOPS, 4), "traffic": None,
+                     "kernel": "kvq_paged_prefill: paged_decode_kernel<prefill> (%s)" % spec.fmt,
+                     "flops_per_launch": flops, "avg_launch_ms": round(att_ms, 5)},
+        "cpu_baseline": (prefill_cpu_baseline(case, spec, q, chunk, args.cpu_min_seconds)
+                         if args.cpu_seqs > 0 else None),
+    }
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -189,6 +298,8 @@ def main(argv=None) -> int:
     kvq.lib()
     dev = torch.device("cuda:0")
     spec = W.spec(args.workload)
+    if spec.chunk > 0:
+        return run_prefill(args, spec)
     t_setup = time.perf_counter()
     case = DecodeCase(spec, device=dev, poison=False)
     inputs = []

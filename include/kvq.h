@@ -191,6 +191,41 @@ KVQ_API kvq_status kvq_paged_decode(const void *q, const void *k_pool,
                             int32_t split_tokens, void *out, void *workspace,
                             size_t workspace_bytes, void *stream);
 
+/*
+ * kvq_paged_prefill -- attention of a chunk of new tokens per sequence over
+ * the paged pool: prefill, or chunked prefill of a long prompt ("KV Cache优化
+ * 实战" s1.1: prefill computes the K/V of every prompt token, each token
+ * attending to the tokens before it; xpshop.cn article 312 s6: long prompts
+ * are processed in chunks).
+ *
+ * Sequence b's chunk is the last n_b = query_start[b+1] - query_start[b] of
+ * its ctx = context_lens[b] tokens; their K/V must already be in the pool
+ * (kvq_cache_write).  Chunk token i sits at position ctx - n_b + i and, for
+ * query head g (KV head h = g / (Hq / Hkv)):
+ *   out[query_start[b] + i][g] = sum_{t <= ctx - n_b + i} softmax_t(
+ *       softmax_scale * q[query_start[b] + i][g] . Khat[b][t][h]) Vhat[b][t][h]
+ *
+ *   q, out        fp16 [total chunk tokens][num_q_heads][head_dim].
+ *   query_start   int32 [num_seqs + 1] on the device, non-decreasing, with
+ *                 n_b <= context_lens[b]; max_query_len >= every n_b is the
+ *                 host-side bound that sizes the launch.
+ *   The other arguments are those of kvq_paged_decode (no workspace: every
+ *   (sequence, KV head, group of 16 / (Hq / Hkv) chunk tokens) is one
+ *   wavefront that walks the tokens it needs).
+ */
+KVQ_API kvq_status kvq_paged_prefill(const void *q, const int32_t *query_start,
+                             int32_t max_query_len, const void *k_pool,
+                             const void *v_pool, const float *k_scale,
+                             const float *v_scale, const int32_t *block_tables,
+                             int32_t max_blocks_per_seq,
+                             const int32_t *context_lens,
+                             int32_t max_context_len, int32_t num_seqs,
+                             int32_t num_q_heads, int32_t num_kv_heads,
+                             int32_t head_dim, int32_t block_size,
+                             int32_t num_blocks, int32_t dtype,
+                             int32_t group_size, float softmax_scale,
+                             void *out, void *stream);
+
 /* Workspace bytes kvq_paged_decode needs for these arguments on the
  * current device (an upper bound over formats and kernel occupancy).
  * Returns SIZE_MAX for invalid arguments. */

@@ -238,27 +238,48 @@ kvq_status launch_decode(DecodeParams p, const LaunchPlan &lp, hipStream_t s)
     return launch_status();
 }
 
+// Chunked prefill: one wavefront per (chunk-token group, sequence, KV head).
+template <int FMT, int D, int BS, int NG>
+kvq_status launch_prefill(const DecodeParams &p, hipStream_t s)
+{
+    const int64_t grid = (int64_t)p.groups * p.B * p.Hkv;
+    if (grid > (int64_t)INT32_MAX)
+        return KVQ_ERR_UNSUPPORTED;
+    if (grid == 0)
+        return KVQ_OK;
+    hipLaunchKernelGGL((paged_decode_kernel<FMT, D, BS, NG, true>), dim3((unsigned)grid),
+                       dim3(64), 0, s, p);
+    return launch_status();
+}
+
+template <int FMT, int D, int BS, int NG>
+kvq_status launch_attention(const DecodeParams &p, const LaunchPlan *lp, hipStream_t s)
+{
+    return lp ? launch_decode<FMT, D, BS, NG>(p, *lp, s) : launch_prefill<FMT, D, BS, NG>(p, s);
+}
+
 // Kernel instances: NG = head_dim / group_size for per-group scales, 0 for
-// static scales (FP8 per head, INT8 per channel) and fp16.
+// static scales (FP8 per head, INT8 per channel) and fp16.  lp == nullptr
+// selects chunked prefill.
 template <int FMT, int D, int BS>
-kvq_status dispatch_decode_ng(const DecodeParams &p, const LaunchPlan &lp, int G, hipStream_t s)
+kvq_status dispatch_decode_ng(const DecodeParams &p, const LaunchPlan *lp, int G, hipStream_t s)
 {
     if constexpr (FMT == FMT_INT8 || FMT == FMT_FP8) {
         if (G == 0)
-            return launch_decode<FMT, D, BS, 0>(p, lp, s);
+            return launch_attention<FMT, D, BS, 0>(p, lp, s);
         const int NG = D / G;
         if (NG == 1)
-            return launch_decode<FMT, D, BS, 1>(p, lp, s);
+            return launch_attention<FMT, D, BS, 1>(p, lp, s);
         if constexpr (D == 128)
-            return launch_decode<FMT, D, BS, 2>(p, lp, s);
+            return launch_attention<FMT, D, BS, 2>(p, lp, s);
         return KVQ_ERR_UNSUPPORTED;
     } else {
-        return launch_decode<FMT, D, BS, 0>(p, lp, s);
+        return launch_attention<FMT, D, BS, 0>(p, lp, s);
     }
 }
 
 template <int FMT>
-kvq_status dispatch_decode(const DecodeParams &p, const LaunchPlan &lp, int D, int BS, int G,
+kvq_status dispatch_decode(const DecodeParams &p, const LaunchPlan *lp, int D, int BS, int G,
                            hipStream_t s)
 {
     if (D == 64)
@@ -266,6 +287,17 @@ kvq_status dispatch_decode(const DecodeParams &p, const LaunchPlan &lp, int D, i
                         : dispatch_decode_ng<FMT, 64, 32>(p, lp, G, s);
     return BS == 16 ? dispatch_decode_ng<FMT, 128, 16>(p, lp, G, s)
                     : dispatch_decode_ng<FMT, 128, 32>(p, lp, G, s);
+}
+
+kvq_status dispatch_attention(const DecodeParams &p, const LaunchPlan *lp, int32_t dtype,
+                              int D, int BS, int G, hipStream_t s)
+{
+    switch (dtype) {
+    case KVQ_INT8: return dispatch_decode<FMT_INT8>(p, lp, D, BS, G, s);
+    case KVQ_FP8_E4M3: return dispatch_decode<FMT_FP8>(p, lp, D, BS, G, s);
+    case KVQ_FP8_E5M2: return dispatch_decode<FMT_E5M2>(p, lp, D, BS, 0, s);
+    default: return dispatch_decode<FMT_FP16>(p, lp, D, BS, 0, s);
+    }
 }
 
 }  // namespace
@@ -394,7 +426,7 @@ kvq_status kvq_paged_decode(const void *q, const void *k_pool, const void *v_poo
     if (st != KVQ_OK)
         return st;
 
-    DecodeParams p;
+    DecodeParams p = {};
     p.q = static_cast<const f16 *>(q);
     p.k_pool = static_cast<const uint8_t *>(k_pool);
     p.v_pool = static_cast<const uint8_t *>(v_pool);
@@ -417,17 +449,71 @@ kvq_status kvq_paged_decode(const void *q, const void *k_pool, const void *v_poo
     lp.max_ctx = max_context_len;
     lp.ws_bytes = workspace_bytes;
     lp.ws = static_cast<uint8_t *>(workspace);
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    switch (dtype) {
-    case KVQ_INT8:
-        return dispatch_decode<FMT_INT8>(p, lp, head_dim, block_size, group_size, s);
-    case KVQ_FP8_E4M3:
-        return dispatch_decode<FMT_FP8>(p, lp, head_dim, block_size, group_size, s);
-    case KVQ_FP8_E5M2:
-        return dispatch_decode<FMT_E5M2>(p, lp, head_dim, block_size, 0, s);
-    default:
-        return dispatch_decode<FMT_FP16>(p, lp, head_dim, block_size, 0, s);
-    }
+    return dispatch_attention(p, &lp, dtype, head_dim, block_size, group_size,
+                              static_cast<hipStream_t>(stream));
+}
+
+kvq_status kvq_paged_prefill(const void *q, const int32_t *query_start, int32_t max_query_len,
+                             const void *k_pool, const void *v_pool, const float *k_scale,
+                             const float *v_scale, const int32_t *block_tables,
+                             int32_t max_blocks_per_seq, const int32_t *context_lens,
+                             int32_t max_context_len, int32_t num_seqs, int32_t num_q_heads,
+                             int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                             int32_t num_blocks, int32_t dtype, int32_t group_size,
+                             float softmax_scale, void *out, void *stream)
+{
+    kvq_status st = check_format(dtype, head_dim, block_size, group_size);
+    if (st != KVQ_OK)
+        return st;
+    if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_blocks <= 0 ||
+        max_blocks_per_seq <= 0 || num_blocks > kBlockIdMask + 1 || max_query_len < 0)
+        return KVQ_ERR_INVALID_ARG;
+    if (num_q_heads % num_kv_heads != 0)
+        return KVQ_ERR_INVALID_ARG;
+    const int32_t r = num_q_heads / num_kv_heads;
+    if (r > 16)
+        return KVQ_ERR_UNSUPPORTED;
+    if (num_seqs == 0 || max_query_len == 0)
+        return KVQ_OK;
+    if (max_context_len < max_query_len ||
+        (int64_t)max_blocks_per_seq * block_size < max_context_len)
+        return KVQ_ERR_INVALID_ARG;
+    if (!(softmax_scale >= 0.0f) || std::isinf(softmax_scale))
+        return KVQ_ERR_INVALID_ARG;
+    if (!q || !query_start || !k_pool || !v_pool || !block_tables || !context_lens || !out)
+        return KVQ_ERR_INVALID_ARG;
+    if (dtype != KVQ_FP16 && (!k_scale || !v_scale))
+        return KVQ_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(out) || !aligned16(k_pool) || !aligned16(v_pool) ||
+        (k_scale && !aligned16(k_scale)) || (v_scale && !aligned16(v_scale)))
+        return KVQ_ERR_INVALID_ARG;
+    st = check_device();
+    if (st != KVQ_OK)
+        return st;
+
+    DecodeParams p = {};
+    p.q = static_cast<const f16 *>(q);
+    p.k_pool = static_cast<const uint8_t *>(k_pool);
+    p.v_pool = static_cast<const uint8_t *>(v_pool);
+    p.k_scale = k_scale;
+    p.v_scale = v_scale;
+    p.block_tables = block_tables;
+    p.context_lens = context_lens;
+    p.out = static_cast<f16 *>(out);
+    p.B = num_seqs;
+    p.max_blocks = max_blocks_per_seq;
+    p.max_ctx = max_context_len;
+    p.num_blocks = num_blocks;
+    p.Hq = num_q_heads;
+    p.Hkv = num_kv_heads;
+    p.r = r;
+    const float sm = softmax_scale > 0.0f ? softmax_scale : 1.0f / std::sqrt((float)head_dim);
+    p.score_scale = sm * 1.4426950408889634f;
+    p.q_start = query_start;
+    p.qpc = 16 / r;
+    p.groups = (max_query_len + p.qpc - 1) / p.qpc;
+    return dispatch_attention(p, nullptr, dtype, head_dim, block_size, group_size,
+                              static_cast<hipStream_t>(stream));
 }
 
 kvq_status kvq_copy_blocks(const int32_t *block_pairs, int32_t num_pairs, int32_t num_kv_heads,

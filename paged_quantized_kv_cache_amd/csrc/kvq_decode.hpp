@@ -96,6 +96,10 @@ struct DecodeParams {
     int32_t r;
     int32_t W;           // wavefronts launched
     float score_scale;   // softmax_scale * log2(e)
+    // chunked prefill only
+    const int32_t *q_start;  // [B + 1] chunk offsets in q / out
+    int32_t qpc;             // chunk tokens per wavefront (16 / r)
+    int32_t groups;          // ceil(max chunk length / qpc)
 };
 
 struct PlanParams {
@@ -276,7 +280,8 @@ __device__ __forceinline__ void load_tile(const DecodeParams &p, TileData<FMT, D
     }
 }
 
-template <int FMT, int D, int BS, int NG>
+// kPrefill: chunked prefill instead of decode (see the end of the kernel).
+template <int FMT, int D, int BS, int NG, bool kPrefill = false>
 __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
 {
     constexpr int KS = D / 16;   // MFMA k-steps over head_dim
@@ -297,63 +302,67 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
     const int lane = threadIdx.x;
     const int col = lane & 15;
     const int grp = lane >> 4;
-    PlanRecord rec;
-    if (p.inline_plan) {
-        // every wavefront scans the lengths: lane i holds sequences
-        // per*i .. per*i + per - 1
-        const int per = (p.B + 63) >> 6;
-        int tl[kInlineSeqs];
-        int sum = 0;
-#pragma unroll
-        for (int j = 0; j < kInlineSeqs; ++j) {
-            const int bb = lane * per + j;
-            tl[j] = (j < per && bb < p.B) ? ctx_tiles(p.context_lens, bb, p.max_ctx) : 0;
-            sum += tl[j];
-        }
-        int incl = sum;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-            const int y = __shfl_up(incl, o);
-            if (lane >= o)
-                incl += y;
-        }
-        // (readfirstlane: the values are wave-uniform; keep them scalar)
-        const int T = p.Hkv * __builtin_amdgcn_readfirstlane(__shfl(incl, 63));
-        const int W = min(p.W, T);
-        if (w == 0 && lane == 0)
-            p.plan_meta[0] = W;  // runs in use, for the merge launch
-        if (w >= W)
-            return;
-        const int g0 = (int)((int64_t)w * T / W);
-        const int g1 = (int)((int64_t)(w + 1) * T / W);
-        int s0 = incl - sum, found = -1, fbase = 0;
-#pragma unroll
-        for (int j = 0; j < kInlineSeqs; ++j) {
-            if (p.Hkv * s0 <= g0 && g0 < p.Hkv * (s0 + tl[j])) {
-                found = lane * per + j;
-                fbase = p.Hkv * s0;
+    PlanRecord rec{};
+    if constexpr (!kPrefill) {  // this wavefront's run of tiles
+        if (p.inline_plan) {
+            // every wavefront scans the lengths: lane i holds sequences
+            // per*i .. per*i + per - 1
+            const int per = (p.B + 63) >> 6;
+            int tl[kInlineSeqs];
+            int sum = 0;
+    #pragma unroll
+            for (int j = 0; j < kInlineSeqs; ++j) {
+                const int bb = lane * per + j;
+                tl[j] = (j < per && bb < p.B) ? ctx_tiles(p.context_lens, bb, p.max_ctx) : 0;
+                sum += tl[j];
             }
-            s0 += tl[j];
+            int incl = sum;
+    #pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const int y = __shfl_up(incl, o);
+                if (lane >= o)
+                    incl += y;
+            }
+            // (readfirstlane: the values are wave-uniform; keep them scalar)
+            const int T = p.Hkv * __builtin_amdgcn_readfirstlane(__shfl(incl, 63));
+            const int W = min(p.W, T);
+            if (w == 0 && lane == 0)
+                p.plan_meta[0] = W;  // runs in use, for the merge launch
+            if (w >= W)
+                return;
+            const int g0 = (int)((int64_t)w * T / W);
+            const int g1 = (int)((int64_t)(w + 1) * T / W);
+            int s0 = incl - sum, found = -1, fbase = 0;
+    #pragma unroll
+            for (int j = 0; j < kInlineSeqs; ++j) {
+                if (p.Hkv * s0 <= g0 && g0 < p.Hkv * (s0 + tl[j])) {
+                    found = lane * per + j;
+                    fbase = p.Hkv * s0;
+                }
+                s0 += tl[j];
+            }
+            const int src = __builtin_ctzll(__builtin_amdgcn_ballot_w64(found >= 0));
+            rec = PlanRecord{__builtin_amdgcn_readlane(found, src), g0, g1,
+                             __builtin_amdgcn_readlane(fbase, src)};
+            if (lane == 0)
+                p.plan_rec[w] = rec;  // for the merge launch
+        } else {
+            if (w >= p.plan_meta[0])
+                return;
+            rec = p.plan_rec[w];
         }
-        const int src = __builtin_ctzll(__builtin_amdgcn_ballot_w64(found >= 0));
-        rec = PlanRecord{__builtin_amdgcn_readlane(found, src), g0, g1,
-                         __builtin_amdgcn_readlane(fbase, src)};
-        if (lane == 0)
-            p.plan_rec[w] = rec;  // for the merge launch
-    } else {
-        if (w >= p.plan_meta[0])
-            return;
-        rec = p.plan_rec[w];
     }
-    const bool head_ok = col < p.r;
-
     float score_scale0 = p.score_scale;
 
-    // Attend over tiles [t0, t1) of unit (b, h); ctx clamped to the host bound.
+    // Attend over tiles [t0, t1) of unit (b, h); ctx clamped to the host
+    // bound.  Per lane: the query row of its column (active) or a harmless
+    // row (inactive: q is zeroed, nothing is written), the output row, and
+    // tcol, the column's own token bound (causal limit in prefill).
     auto attend = [&](const int b, const int h, const int ctx, const int n, const int t0,
-                      const int t1) {
-        const int qhead = h * p.r + col;
-        const int t_end = min(ctx, 16 * t1);  // token bound of this run
+                      const int t1, const f16 *qrow, const bool active, const int tcol,
+                      f16 *orow_base) {
+        const int t_end = min(ctx, 16 * t1);  // token bound of this run (data)
+        const int t_col = min(t_end, tcol);   // score bound of this lane's column
 
         // ---- query operand, in the k-step dim order of the K loads:
         //   1-byte codes: k-step s, lane group grp, element v -> dim
@@ -361,7 +370,6 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
         //   fp16:   32 (s/2) + 8 grp + 4 (s%2) + v
         f16x4 qop[KS];
         {
-            const f16 *qrow = p.q + ((int64_t)b * p.Hq + (head_ok ? qhead : h * p.r)) * D;
             if constexpr (EB == 1) {
 #pragma unroll
                 for (int c = 0; c < D / 64; ++c) {
@@ -380,7 +388,7 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
                     qop[2 * c + 1] = f16x4_from_u2(w4.z, w4.w);
                 }
             }
-            if (!head_ok) {
+            if (!active) {
 #pragma unroll
                 for (int s = 0; s < KS; ++s)
                     qop[s] = f16x4{0, 0, 0, 0};
@@ -508,7 +516,7 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
                 } else {
                     acc = sacc[0][v] * score_scale;
                 }
-                z[v] = (tok0 + v < t_end) ? acc : -INFINITY;
+                z[v] = (tok0 + v < t_col) ? acc : -INFINITY;
             }
             // ---- online softmax
             float mt = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
@@ -672,7 +680,7 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
             for (int tau = 0; tau < DT; ++tau)
                 o[tau] -= csum[(64 * (tau >> 2)) / G];
         }
-        if (!head_ok)
+        if (!active)
             return;
         if constexpr (kChannel) {
             // V channel scales: o[4 g4 + i][v] is dim 64 g4 + 16 grp + 4 v + i
@@ -690,7 +698,7 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
         }
         if (t0 == 0 && t1 == n) {  // the whole unit: final output
             const float inv = out_scale / lt;
-            f16 *orow = p.out + ((int64_t)b * p.Hq + qhead) * D + 16 * grp;
+            f16 *orow = orow_base + 16 * grp;
 #pragma unroll
             for (int g4 = 0; g4 < D / 64; ++g4) {
                 f16x4 hv[4];
@@ -720,7 +728,42 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
             *reinterpret_cast<float2 *>(p.ws_ml + 2 * idx) = make_float2(m, lt);
     };
 
-    // ---- walk the run [g0, g1) unit by unit (all values wave-uniform)
+    if constexpr (kPrefill) {
+        // ---- chunked prefill ("KV Cache优化实战" s1.1: every prompt token
+        // attends to the tokens before it; xpshop.cn article 312 s6: long
+        // prompts go in chunks).  Sequence b's chunk is the last nq of its
+        // ctx tokens (their K/V already written); chunk token i sits at
+        // position ctx - nq + i.  One wavefront takes (b, KV head h, group gi
+        // of qpc consecutive chunk tokens): MFMA column col is chunk token
+        // gi * qpc + col / r with query head h * r + col % r, so one pass
+        // over the tiles serves qpc tokens x r heads.  Groups are numbered
+        // so that the later (longer) ones start first.
+        const int BH = p.B * p.Hkv;
+        const int gi = p.groups - 1 - w / BH;
+        const int b = (w % BH) / p.Hkv;
+        const int h = (w % BH) % p.Hkv;
+        const int ctx = min(max(p.context_lens[b], 0), p.max_ctx);
+        const int qs = p.q_start[b];
+        const int nq = min(p.q_start[b + 1] - qs, ctx);
+        const int i0 = gi * p.qpc;
+        if (i0 >= nq)
+            return;
+        const int c0 = ctx - nq;                       // cached before the chunk
+        const int i_end = min(i0 + p.qpc, nq);
+        const int ic = i0 + col / p.r, jc = col % p.r;
+        const bool active = col < p.qpc * p.r && ic < i_end;
+        const int tl = c0 + i_end;                     // tokens this group reads
+        const int n = (tl + 15) >> 4;
+        const f16 *qrow = p.q + ((int64_t)(qs + (active ? ic : i0)) * p.Hq + h * p.r +
+                                 (active ? jc : 0)) * D;
+        f16 *orow = p.out + ((int64_t)(qs + (active ? ic : i0)) * p.Hq + h * p.r +
+                             (active ? jc : 0)) * D;
+        attend(b, h, tl, n, 0, n, qrow, active, active ? c0 + ic + 1 : tl, orow);
+        return;
+    }
+
+    // ---- decode: walk the run [g0, g1) unit by unit (values wave-uniform)
+    const bool head_ok = col < p.r;
     int b = rec.b;
     int g = rec.g0;
     int n = ctx_tiles(p.context_lens, b, p.max_ctx);
@@ -736,7 +779,9 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
         const int t0 = g - base - h * n;
         const int t1 = min(n, t0 + (rec.g1 - g));
         const int ctx = min(p.context_lens[b], p.max_ctx);
-        attend(b, h, ctx, n, t0, t1);
+        const int qhead = h * p.r + col;
+        const int64_t row = (int64_t)b * p.Hq + (head_ok ? qhead : h * p.r);
+        attend(b, h, ctx, n, t0, t1, p.q + row * D, head_ok, 1 << 30, p.out + row * D);
         g += t1 - t0;
     }
 }

@@ -154,6 +154,29 @@ class DecodeCase:
                                     softmax_scale=softmax_scale, split_tokens=split_tokens,
                                     out=out, workspace=workspace)
 
+    def chunk_queries(self, chunk_lens, seed: int = 7) -> torch.Tensor:
+        """Seeded fp16 queries ``[sum chunk][Hq][D]`` for a prefill chunk."""
+        s = self.spec
+        g = torch.Generator(device="cpu")
+        g.manual_seed(seed)
+        n = int(np.asarray(chunk_lens).sum())
+        q = torch.randn((n, s.Hq, s.D), generator=g, dtype=torch.float32)
+        return q.to(torch.float16).to(self.device)
+
+    def prefill_attention(self, layer: int, chunk_lens, q: torch.Tensor,
+                          out=None) -> torch.Tensor:
+        """Chunked prefill: sequence b's last chunk_lens[b] tokens attend
+        causally (their K/V are already in the pool)."""
+        p, s = self.pools[layer], self.spec
+        n = np.asarray(chunk_lens, np.int64)
+        qs = np.zeros(n.size + 1, np.int32)
+        qs[1:] = np.cumsum(n)
+        query_start = torch.from_numpy(qs).to(self.device)
+        return kvq.kvq_paged_prefill(q, query_start, int(n.max()) if n.size else 0,
+                                     p.k_pool, p.v_pool, p.k_scale, p.v_scale,
+                                     self.block_tables, self.context_lens,
+                                     self.max_context_len, p.fmt, s.G, out=out)
+
     # ------------------------------------------------------------ readback
     def gather_codes(self, layer: int, seqs=None):
         """Read the pools back through the block tables: per sequence,

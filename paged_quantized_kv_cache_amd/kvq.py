@@ -45,7 +45,7 @@ STATUS = {0: "KVQ_OK", -1: "KVQ_ERR_INVALID_ARG", -2: "KVQ_ERR_UNSUPPORTED",
           -3: "KVQ_ERR_WORKSPACE", -4: "KVQ_ERR_HIP"}
 EXPORTS = ("kvq_status_string", "kvq_version", "kvq_cache_write",
            "kvq_paged_decode", "kvq_decode_workspace_size", "kvq_copy_blocks",
-           "kvq_swap_block_bytes", "kvq_swap_out", "kvq_swap_in")
+           "kvq_swap_block_bytes", "kvq_swap_out", "kvq_swap_in", "kvq_paged_prefill")
 
 
 class KvqError(RuntimeError):
@@ -82,6 +82,10 @@ def lib() -> ctypes.CDLL:
                                            i32, i32, i32, i32, i32, i32, i32,
                                            ctypes.c_float, i32, P, P,
                                            ctypes.c_size_t, P]
+            L.kvq_paged_prefill.restype = i32
+            L.kvq_paged_prefill.argtypes = [P, P, i32, P, P, P, P, P, i32, P, i32, i32,
+                                            i32, i32, i32, i32, i32, i32, i32,
+                                            ctypes.c_float, P, P]
             L.kvq_decode_workspace_size.restype = ctypes.c_size_t
             L.kvq_decode_workspace_size.argtypes = [i32] * 7
             L.kvq_copy_blocks.restype = i32
@@ -301,3 +305,33 @@ def kvq_swap_in(block_slot_pairs: torch.Tensor, src: torch.Tensor, k_pool: torch
                            _ptr(k_scale) if grp else None, _ptr(v_scale) if grp else None,
                            _stream(stream))
     _check(st, "kvq_swap_in")
+
+
+# ------------------------------------------------------------------ prefill
+def kvq_paged_prefill(q: torch.Tensor, query_start: torch.Tensor, max_query_len: int,
+                      k_pool: torch.Tensor, v_pool: torch.Tensor,
+                      k_scale: Optional[torch.Tensor], v_scale: Optional[torch.Tensor],
+                      block_tables: torch.Tensor, context_lens: torch.Tensor,
+                      max_context_len: int, fmt: str, group_size: int = 0,
+                      softmax_scale: float = 0.0, out: Optional[torch.Tensor] = None,
+                      stream=None) -> torch.Tensor:
+    """Causal attention of each sequence's chunk (its last n_b tokens, already
+    in the pool) over its cached tokens.  q: fp16 [sum n][Hq][D];
+    query_start: int32 [B + 1] on the device."""
+    num_blocks, hkv, bs, d = _pool_geometry(k_pool, fmt)
+    T, hq, dq = q.shape
+    B = context_lens.numel()
+    if dq != d or q.dtype != torch.float16 or not q.is_contiguous():
+        raise ValueError("q must be contiguous fp16 [tokens][Hq][head_dim]")
+    if query_start.dtype != torch.int32 or query_start.numel() != B + 1:
+        raise ValueError("query_start must be int32 [B + 1]")
+    if out is None:
+        out = torch.empty_like(q)
+    st = lib().kvq_paged_prefill(_ptr(q), _ptr(query_start), max_query_len, _ptr(k_pool),
+                                 _ptr(v_pool), _ptr(k_scale), _ptr(v_scale),
+                                 _ptr(block_tables), block_tables.shape[1],
+                                 _ptr(context_lens), max_context_len, B, hq, hkv, d, bs,
+                                 num_blocks, _fmt(fmt), group_size, softmax_scale, _ptr(out),
+                                 _stream(stream))
+    _check(st, "kvq_paged_prefill")
+    return out

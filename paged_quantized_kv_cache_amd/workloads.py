@@ -57,6 +57,7 @@ class Spec:
     layer_fmts: Optional[Tuple[str, ...]] = None   # per-layer format
     shared_prefix: int = 0        # tokens shared by all sequences
     fork_pairs: int = 0           # pairs (2k, 2k+1) also sharing a partial tail
+    chunk: int = 0                # > 0: a prefill workload, chunks of min(chunk, ctx)
     description: str = ""
 
     @property
@@ -120,6 +121,12 @@ SPECS: Dict[str, Spec] = {
         lens="lognormal", lens_args=(2048, 16, 8192), seed=0,
         k_out=Outliers(5, 10.0),
         description="the GQA layer, INT8 with static per-channel scales"),
+    "p1_prefill_gqa": Spec(
+        "p1_prefill_gqa", B=16, Hq=32, Hkv=8, D=128, BS=16, fmt="int8", G=64,
+        lens="fixed", lens_args=(2048,) * 16, seed=0, k_out=Outliers(5, 10.0),
+        chunk=2048,
+        description="prefill of 16 prompts of 2048 tokens into the GQA INT8 g64 "
+                    "pool, causal attention over the quantized cache"),
     "c5_prefix_mixed": Spec(
         "c5_prefix_mixed", B=128, Hq=32, Hkv=8, D=128, BS=16, fmt="int8",
         G=128, lens="prefix_tails", lens_args=(64, 4096), seed=0, layers=32,
@@ -372,6 +379,18 @@ def static_scales(fmt: str, group_size: int, x: torch.Tensor) -> Optional[torch.
     if group_size > 0 or fmt == "fp16":
         return None
     return int8_channel_scales(x) if fmt == "int8" else fp8_static_scales(x, fmt)
+
+
+def prefill_flops(s: Spec, lens: np.ndarray, chunk_lens: np.ndarray) -> int:
+    """Multiply-add flops of causal chunk attention: query at position p
+    reads p + 1 tokens, 2 * D flops each for q.k and again for p.v, for
+    every query head."""
+    lens = np.asarray(lens, np.int64)
+    n = np.asarray(chunk_lens, np.int64)
+    c = lens - n
+    # sum over i < n of (c + i + 1)
+    keys = int(np.sum(n * c + n * (n + 1) // 2))
+    return 4 * s.Hq * s.D * keys
 
 
 # ----------------------------------------------------------------- bytes

@@ -1,0 +1,108 @@
+"""GPU parity of chunked-prefill attention over the paged pools
+(kvq_paged_prefill through the C ABI) against the CPU oracle.
+
+Each sequence's chunk is its last n_b tokens (already written by
+kvq_cache_write); chunk token i attends to every token up to its position.
+Chunks: whole prompts, a fixed-size tail chunk after cached tokens, and one
+token (where prefill must agree with decode).  Tolerance as for decode:
+|gpu - oracle| <= 2e-3 + 1e-3 |oracle|.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import expected as E
+from paged_quantized_kv_cache_amd import kvq
+from paged_quantized_kv_cache_amd import workloads as W
+from paged_quantized_kv_cache_amd.harness import DecodeCase
+
+from test_gpu_parity import SMALL_CASES
+
+pytestmark = pytest.mark.gpu
+
+ATOL, RTOL = 2e-3, 1e-3
+CASES = ["c1_tiny", "gqa_int8_g64_outliers", "mha_int8_g128", "gqa_fp16", "fp8_bs32",
+         "int8_bs32_g128_r8", "int8_d64_bs32_r16", "e5m2_bs16", "fp8_token_g128",
+         "int8_channel"]
+
+
+def _quantized(case, layer, seqs):
+    s, fmt = case.spec, case.fmt(layer)
+    d = case.data[layer]
+    sk = sv = None
+    if kvq.scale_mode(fmt, s.G) in ("head", "channel"):
+        sk = case.pools[layer].k_scale.cpu().numpy()
+        sv = case.pools[layer].v_scale.cpu().numpy()
+    ids = np.unique(np.concatenate([case.layout.seq_tokens[b] for b in seqs]))
+    remap = np.full(case.layout.n_unique, -1, np.int64)
+    remap[ids] = np.arange(ids.size)
+    idx = torch.from_numpy(ids).to(d.k.device)
+    kq = E.quantize(d.k.index_select(0, idx).cpu().numpy(), fmt, s.G, sk)
+    vq = E.quantize(d.v.index_select(0, idx).cpu().numpy(), fmt, s.G, sv)
+    toks = [remap[case.layout.seq_tokens[b]] for b in seqs]
+    return kq, vq, toks
+
+
+def _chunks(lens, mode):
+    if mode == "whole":
+        return lens.copy()
+    if mode == "tail":
+        return np.minimum(lens, 37)
+    return np.ones_like(lens)
+
+
+@pytest.mark.parametrize("mode", ["whole", "tail", "one"])
+@pytest.mark.parametrize("name", CASES)
+def test_prefill_within_tolerance(name, mode, gpu):
+    print("case", name, mode, flush=True)
+    spec = SMALL_CASES[name]
+    case = DecodeCase(spec, device=gpu, gen_device="cpu")
+    case.setup_layer(0)
+    n = _chunks(case.lens, mode)
+    q = case.chunk_queries(n)
+    got = case.prefill_attention(0, n, q).float().cpu().numpy()
+    assert np.isfinite(got).all()
+    kq, vq, toks = _quantized(case, 0, range(spec.B))
+    ref = E.prefill(q.cpu().numpy(), kq, vq, toks, n)
+    ok, mabs, mrel, excess = E.tolerance_ok(got, ref, ATOL, RTOL)
+    assert ok, "%s/%s: max_abs %.3g max_rel %.3g excess %.3g" % (name, mode, mabs, mrel, excess)
+
+
+@pytest.mark.parametrize("name", ["gqa_int8_g64_outliers", "fp8_bs16", "gqa_fp16"])
+def test_one_token_chunk_agrees_with_decode(name, gpu):
+    spec = SMALL_CASES[name]
+    case = DecodeCase(spec, device=gpu, gen_device="cpu")
+    case.setup_layer(0)
+    q = case.data[0].q.to(gpu).contiguous()
+    dec = case.decode(0, q=q, workspace=case.workspace(0)).float().cpu().numpy()
+    pre = case.prefill_attention(0, np.ones_like(case.lens), q).float().cpu().numpy()
+    kq, vq, toks = _quantized(case, 0, range(spec.B))
+    ref = E.attention(q.cpu().numpy(), kq, vq, toks)
+    assert np.all(np.abs(dec - pre) <= 2 * (ATOL + RTOL * np.abs(ref)))
+
+
+def test_full_size_prefill_sampled_rows(gpu):
+    # the prefill workload: 16 prompts of 2048 tokens, GQA 32/8, INT8 g64;
+    # row i of a prompt equals decode over its first i + 1 tokens
+    spec = W.spec("p1_prefill_gqa")
+    print("workload", spec.name, flush=True)
+    case = DecodeCase(spec, device=gpu, poison=True)
+    case.setup_layer(0)
+    n = case.lens.copy()
+    q = case.chunk_queries(n)
+    got = case.prefill_attention(0, n, q).float()
+    assert torch.isfinite(got).all()
+    got = got.cpu().numpy()
+    qh = q.cpu().numpy()
+    seqs = [0, spec.B - 1]
+    kq, vq, toks = _quantized(case, 0, seqs)
+    starts = np.concatenate([[0], np.cumsum(n)])
+    rows, qrows, ctx = [], [], []
+    for j, b in enumerate(seqs):
+        for i in (0, 1, 15, 16, 17, 511, 1024, int(n[b]) - 1):
+            rows.append(starts[b] + i)
+            qrows.append(qh[starts[b] + i])
+            ctx.append(toks[j][:i + 1])
+    ref = E.attention(np.stack(qrows), kq, vq, ctx)
+    ok, mabs, mrel, excess = E.tolerance_ok(got[rows], ref, ATOL, RTOL)
+    assert ok, "max_abs %.3g max_rel %.3g excess %.3g" % (mabs, mrel, excess)
