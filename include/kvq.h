@@ -226,6 +226,49 @@ KVQ_API kvq_status kvq_paged_prefill(const void *q, const int32_t *query_start,
                              int32_t group_size, float softmax_scale,
                              void *out, void *stream);
 
+/*
+ * Per-head mixed precision (xpshop.cn article 312, s6: the attention heads
+ * that are sensitive to quantization keep fp16, the others are quantized).
+ * A layer then keeps one set of pools per format, each holding a subset of
+ * the model's KV heads: pool head i is model KV head kv_head_ids[i]
+ * (int32 [pool heads] on the device, distinct, each < the model's KV heads).
+ *
+ * kvq_cache_write_heads -- kvq_cache_write into such a pool: k, v are
+ *   [num_tokens][num_kv_heads_src][head_dim] with all the model's KV heads;
+ *   the pool (and its scales) have num_kv_heads heads.
+ * kvq_paged_decode_heads -- kvq_paged_decode over such a pool: q and out
+ *   are [num_seqs][num_q_heads][head_dim] with all the model's query heads
+ *   (num_q_heads / num_kv_heads per KV head); only the rows of the query heads
+ *   of the pool's KV heads are read and written, so one call per pool fills
+ *   out.  The workspace is sized with kvq_decode_workspace_size(num_seqs,
+ *   pool_heads * num_q_heads / num_kv_heads, pool_heads, ...); calls that
+ *   share a workspace must be ordered.
+ */
+KVQ_API kvq_status kvq_cache_write_heads(const void *k, const void *v,
+                                 const int64_t *slot_mapping, int32_t num_tokens,
+                                 int32_t num_kv_heads_src,
+                                 const int32_t *kv_head_ids, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t block_size,
+                                 int32_t num_blocks, int32_t dtype,
+                                 int32_t group_size, void *k_pool, void *v_pool,
+                                 float *k_scale, float *v_scale, void *stream);
+
+KVQ_API kvq_status kvq_paged_decode_heads(const void *q, const void *k_pool,
+                                  const void *v_pool, const float *k_scale,
+                                  const float *v_scale,
+                                  const int32_t *block_tables,
+                                  int32_t max_blocks_per_seq,
+                                  const int32_t *context_lens,
+                                  int32_t max_context_len, int32_t num_seqs,
+                                  int32_t num_q_heads, int32_t num_kv_heads,
+                                  const int32_t *kv_head_ids, int32_t pool_heads,
+                                  int32_t head_dim, int32_t block_size,
+                                  int32_t num_blocks, int32_t dtype,
+                                  int32_t group_size, float softmax_scale,
+                                  int32_t split_tokens, void *out,
+                                  void *workspace, size_t workspace_bytes,
+                                  void *stream);
+
 /* Workspace bytes kvq_paged_decode needs for these arguments on the
  * current device (an upper bound over formats and kernel occupancy).
  * Returns SIZE_MAX for invalid arguments. */

@@ -318,13 +318,14 @@ const char *kvq_status_string(kvq_status status)
 
 int32_t kvq_version(void) { return 100; }
 
-kvq_status kvq_cache_write(const void *k, const void *v, const int64_t *slot_mapping,
-                           int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
-                           int32_t block_size, int32_t num_blocks, int32_t dtype,
-                           int32_t group_size, void *k_pool, void *v_pool, float *k_scale,
-                           float *v_scale, void *stream)
+static kvq_status write_impl(const void *k, const void *v, const int64_t *slot_mapping,
+                             int32_t num_tokens, int32_t num_kv_heads_src,
+                             const int32_t *head_ids, int32_t num_kv_heads, int32_t head_dim,
+                             int32_t block_size, int32_t num_blocks, int32_t dtype,
+                             int32_t group_size, void *k_pool, void *v_pool, float *k_scale,
+                             float *v_scale, void *stream)
 {
-    if (num_tokens < 0 || num_kv_heads <= 0 || num_blocks <= 0)
+    if (num_tokens < 0 || num_kv_heads <= 0 || num_blocks <= 0 || num_kv_heads_src <= 0)
         return KVQ_ERR_INVALID_ARG;
     kvq_status st = check_format(dtype, head_dim, block_size, group_size);
     if (st != KVQ_OK)
@@ -354,6 +355,8 @@ kvq_status kvq_cache_write(const void *k, const void *v, const int64_t *slot_map
     p.Hkv = num_kv_heads;
     p.block_size = block_size;
     p.num_slots = (int64_t)num_blocks * block_size;
+    p.head_ids = head_ids;
+    p.Hkv_src = num_kv_heads_src;
     hipStream_t s = static_cast<hipStream_t>(stream);
     switch (dtype) {
     case KVQ_INT8: return dispatch_write_d<FMT_INT8>(p, head_dim, group_size, s);
@@ -361,6 +364,31 @@ kvq_status kvq_cache_write(const void *k, const void *v, const int64_t *slot_map
     case KVQ_FP8_E5M2: return dispatch_write_d<FMT_E5M2>(p, head_dim, 0, s);
     default: return dispatch_write_d<FMT_FP16>(p, head_dim, 0, s);
     }
+}
+
+kvq_status kvq_cache_write(const void *k, const void *v, const int64_t *slot_mapping,
+                           int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                           int32_t block_size, int32_t num_blocks, int32_t dtype,
+                           int32_t group_size, void *k_pool, void *v_pool, float *k_scale,
+                           float *v_scale, void *stream)
+{
+    return write_impl(k, v, slot_mapping, num_tokens, num_kv_heads, nullptr, num_kv_heads,
+                      head_dim, block_size, num_blocks, dtype, group_size, k_pool, v_pool,
+                      k_scale, v_scale, stream);
+}
+
+kvq_status kvq_cache_write_heads(const void *k, const void *v, const int64_t *slot_mapping,
+                                 int32_t num_tokens, int32_t num_kv_heads_src,
+                                 const int32_t *kv_head_ids, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                 int32_t dtype, int32_t group_size, void *k_pool, void *v_pool,
+                                 float *k_scale, float *v_scale, void *stream)
+{
+    if (!kv_head_ids && num_tokens > 0)
+        return KVQ_ERR_INVALID_ARG;
+    return write_impl(k, v, slot_mapping, num_tokens, num_kv_heads_src, kv_head_ids,
+                      num_kv_heads, head_dim, block_size, num_blocks, dtype, group_size,
+                      k_pool, v_pool, k_scale, v_scale, stream);
 }
 
 size_t kvq_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
@@ -381,21 +409,25 @@ size_t kvq_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t 
     return w.total;
 }
 
-kvq_status kvq_paged_decode(const void *q, const void *k_pool, const void *v_pool,
-                            const float *k_scale, const float *v_scale,
-                            const int32_t *block_tables, int32_t max_blocks_per_seq,
-                            const int32_t *context_lens, int32_t max_context_len,
-                            int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
-                            int32_t head_dim, int32_t block_size, int32_t num_blocks,
-                            int32_t dtype, int32_t group_size, float softmax_scale,
-                            int32_t split_tokens, void *out, void *workspace,
-                            size_t workspace_bytes, void *stream)
+// num_q_heads / num_kv_heads: the model's heads (q and out rows, GQA ratio);
+// head_ids: the pool's heads as model KV heads (null: the pool holds all
+// num_kv_heads); pool_heads: heads in the pool.
+static kvq_status decode_impl(const void *q, const void *k_pool, const void *v_pool,
+                              const float *k_scale, const float *v_scale,
+                              const int32_t *block_tables, int32_t max_blocks_per_seq,
+                              const int32_t *context_lens, int32_t max_context_len,
+                              int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                              const int32_t *head_ids, int32_t pool_heads, int32_t head_dim,
+                              int32_t block_size, int32_t num_blocks, int32_t dtype,
+                              int32_t group_size, float softmax_scale, int32_t split_tokens,
+                              void *out, void *workspace, size_t workspace_bytes, void *stream)
 {
     kvq_status st = check_format(dtype, head_dim, block_size, group_size);
     if (st != KVQ_OK)
         return st;
     if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_blocks <= 0 ||
-        max_blocks_per_seq <= 0 || num_blocks > kBlockIdMask + 1)
+        max_blocks_per_seq <= 0 || num_blocks > kBlockIdMask + 1 || pool_heads <= 0 ||
+        pool_heads > num_kv_heads)
         return KVQ_ERR_INVALID_ARG;
     if (num_q_heads % num_kv_heads != 0)
         return KVQ_ERR_INVALID_ARG;
@@ -408,7 +440,7 @@ kvq_status kvq_paged_decode(const void *q, const void *k_pool, const void *v_poo
         return KVQ_ERR_INVALID_ARG;
     if (!valid_split(split_tokens))
         return KVQ_ERR_INVALID_ARG;
-    if (max_tiles(num_seqs, num_kv_heads, max_context_len) >= (int64_t)1 << 30)
+    if (max_tiles(num_seqs, pool_heads, max_context_len) >= (int64_t)1 << 30)
         return KVQ_ERR_UNSUPPORTED;
     if (!(softmax_scale >= 0.0f) || std::isinf(softmax_scale))
         return KVQ_ERR_INVALID_ARG;
@@ -440,8 +472,9 @@ kvq_status kvq_paged_decode(const void *q, const void *k_pool, const void *v_poo
     p.max_ctx = max_context_len;
     p.num_blocks = num_blocks;
     p.Hq = num_q_heads;
-    p.Hkv = num_kv_heads;
+    p.Hkv = pool_heads;
     p.r = r;
+    p.head_ids = head_ids;
     const float sm = softmax_scale > 0.0f ? softmax_scale : 1.0f / std::sqrt((float)head_dim);
     p.score_scale = sm * 1.4426950408889634f;  // log2(e): softmax in base 2
     LaunchPlan lp;
@@ -451,6 +484,43 @@ kvq_status kvq_paged_decode(const void *q, const void *k_pool, const void *v_poo
     lp.ws = static_cast<uint8_t *>(workspace);
     return dispatch_attention(p, &lp, dtype, head_dim, block_size, group_size,
                               static_cast<hipStream_t>(stream));
+}
+
+kvq_status kvq_paged_decode(const void *q, const void *k_pool, const void *v_pool,
+                            const float *k_scale, const float *v_scale,
+                            const int32_t *block_tables, int32_t max_blocks_per_seq,
+                            const int32_t *context_lens, int32_t max_context_len,
+                            int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                            int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                            int32_t dtype, int32_t group_size, float softmax_scale,
+                            int32_t split_tokens, void *out, void *workspace,
+                            size_t workspace_bytes, void *stream)
+{
+    return decode_impl(q, k_pool, v_pool, k_scale, v_scale, block_tables, max_blocks_per_seq,
+                       context_lens, max_context_len, num_seqs, num_q_heads, num_kv_heads,
+                       nullptr, num_kv_heads, head_dim, block_size, num_blocks, dtype,
+                       group_size, softmax_scale, split_tokens, out, workspace,
+                       workspace_bytes, stream);
+}
+
+kvq_status kvq_paged_decode_heads(const void *q, const void *k_pool, const void *v_pool,
+                                  const float *k_scale, const float *v_scale,
+                                  const int32_t *block_tables, int32_t max_blocks_per_seq,
+                                  const int32_t *context_lens, int32_t max_context_len,
+                                  int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                  const int32_t *kv_head_ids, int32_t pool_heads,
+                                  int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                  int32_t dtype, int32_t group_size, float softmax_scale,
+                                  int32_t split_tokens, void *out, void *workspace,
+                                  size_t workspace_bytes, void *stream)
+{
+    if (!kv_head_ids && num_seqs > 0)
+        return KVQ_ERR_INVALID_ARG;
+    return decode_impl(q, k_pool, v_pool, k_scale, v_scale, block_tables, max_blocks_per_seq,
+                       context_lens, max_context_len, num_seqs, num_q_heads, num_kv_heads,
+                       kv_head_ids, pool_heads, head_dim, block_size, num_blocks, dtype,
+                       group_size, softmax_scale, split_tokens, out, workspace,
+                       workspace_bytes, stream);
 }
 
 kvq_status kvq_paged_prefill(const void *q, const int32_t *query_start, int32_t max_query_len,

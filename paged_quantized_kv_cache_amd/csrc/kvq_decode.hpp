@@ -96,6 +96,10 @@ struct DecodeParams {
     int32_t r;
     int32_t W;           // wavefronts launched
     float score_scale;   // softmax_scale * log2(e)
+    // KV-head subset (per-head mixed precision): the pool's head h is KV
+    // head head_ids[h] of the model; q / out rows have Hq query heads, of
+    // which KV head g serves g * r .. g * r + r - 1.  Null: the identity.
+    const int32_t *head_ids;
     // chunked prefill only
     const int32_t *q_start;  // [B + 1] chunk offsets in q / out
     int32_t qpc;             // chunk tokens per wavefront (16 / r)
@@ -113,6 +117,11 @@ struct PlanParams {
     int32_t W;            // balanced: runs wanted; fixed span: runs launched
     int32_t span_tiles;   // 0: balanced; else tiles per span
 };
+
+__device__ __forceinline__ int model_head(const DecodeParams &p, int h)
+{
+    return p.head_ids ? p.head_ids[h] : h;
+}
 
 __device__ __forceinline__ int ctx_tiles(const int32_t *lens, int b, int max_ctx)
 {
@@ -754,9 +763,10 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
         const bool active = col < p.qpc * p.r && ic < i_end;
         const int tl = c0 + i_end;                     // tokens this group reads
         const int n = (tl + 15) >> 4;
-        const f16 *qrow = p.q + ((int64_t)(qs + (active ? ic : i0)) * p.Hq + h * p.r +
+        const int gh = model_head(p, h);
+        const f16 *qrow = p.q + ((int64_t)(qs + (active ? ic : i0)) * p.Hq + gh * p.r +
                                  (active ? jc : 0)) * D;
-        f16 *orow = p.out + ((int64_t)(qs + (active ? ic : i0)) * p.Hq + h * p.r +
+        f16 *orow = p.out + ((int64_t)(qs + (active ? ic : i0)) * p.Hq + gh * p.r +
                              (active ? jc : 0)) * D;
         attend(b, h, tl, n, 0, n, qrow, active, active ? c0 + ic + 1 : tl, orow);
         return;
@@ -779,8 +789,8 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
         const int t0 = g - base - h * n;
         const int t1 = min(n, t0 + (rec.g1 - g));
         const int ctx = min(p.context_lens[b], p.max_ctx);
-        const int qhead = h * p.r + col;
-        const int64_t row = (int64_t)b * p.Hq + (head_ok ? qhead : h * p.r);
+        const int gh = model_head(p, h);
+        const int64_t row = (int64_t)b * p.Hq + gh * p.r + (head_ok ? col : 0);
         attend(b, h, ctx, n, t0, t1, p.q + row * D, head_ok, 1 << 30, p.out + row * D);
         g += t1 - t0;
     }
@@ -852,7 +862,7 @@ __global__ __launch_bounds__(64) void merge_runs_kernel(DecodeParams p)
             acc[i] += a[i] * wgt;
     }
     const float inv = 1.0f / ls;
-    f16 *orow = p.out + ((int64_t)b * p.Hq + h * p.r + col) * D + PER * lane;
+    f16 *orow = p.out + ((int64_t)b * p.Hq + model_head(p, h) * p.r + col) * D + PER * lane;
 #pragma unroll
     for (int i = 0; i < PER; ++i)
         orow[i] = (f16)(acc[i] * inv);

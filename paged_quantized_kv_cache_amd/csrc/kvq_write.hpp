@@ -33,9 +33,11 @@ struct WriteParams {
     float *k_scale;
     float *v_scale;
     int32_t num_tokens;
-    int32_t Hkv;
+    int32_t Hkv;        // heads in the pools
     int32_t block_size;
     int64_t num_slots;  // num_blocks * block_size
+    const int32_t *head_ids;  // pool head h is input head head_ids[h] (null: h)
+    int32_t Hkv_src;          // heads per token in k / v
 };
 
 constexpr int kWriteWaves = 4;
@@ -61,7 +63,8 @@ __global__ __launch_bounds__(64 * kWriteWaves) void cache_write_kernel(WritePara
     const bool is_v = lane >= 32;
     const int e0 = (lane & 31) * EPL;
 
-    const f16 *src = (is_v ? p.v : p.k) + ((int64_t)t * p.Hkv + h) * D + e0;
+    const int gh = p.head_ids ? p.head_ids[h] : h;
+    const f16 *src = (is_v ? p.v : p.k) + ((int64_t)t * p.Hkv_src + gh) * D + e0;
     float x[EPL];
     if constexpr (EPL == 4) {
         const uint2 raw = *reinterpret_cast<const uint2 *>(src);

@@ -45,7 +45,8 @@ STATUS = {0: "KVQ_OK", -1: "KVQ_ERR_INVALID_ARG", -2: "KVQ_ERR_UNSUPPORTED",
           -3: "KVQ_ERR_WORKSPACE", -4: "KVQ_ERR_HIP"}
 EXPORTS = ("kvq_status_string", "kvq_version", "kvq_cache_write",
            "kvq_paged_decode", "kvq_decode_workspace_size", "kvq_copy_blocks",
-           "kvq_swap_block_bytes", "kvq_swap_out", "kvq_swap_in", "kvq_paged_prefill")
+           "kvq_swap_block_bytes", "kvq_swap_out", "kvq_swap_in", "kvq_paged_prefill",
+           "kvq_cache_write_heads", "kvq_paged_decode_heads")
 
 
 class KvqError(RuntimeError):
@@ -82,6 +83,14 @@ def lib() -> ctypes.CDLL:
                                            i32, i32, i32, i32, i32, i32, i32,
                                            ctypes.c_float, i32, P, P,
                                            ctypes.c_size_t, P]
+            L.kvq_cache_write_heads.restype = i32
+            L.kvq_cache_write_heads.argtypes = [P, P, P, i32, i32, P, i32, i32, i32, i32,
+                                                i32, i32, P, P, P, P, P]
+            L.kvq_paged_decode_heads.restype = i32
+            L.kvq_paged_decode_heads.argtypes = [P, P, P, P, P, P, i32, P, i32, i32, i32,
+                                                 i32, P, i32, i32, i32, i32, i32, i32,
+                                                 ctypes.c_float, i32, P, P, ctypes.c_size_t,
+                                                 P]
             L.kvq_paged_prefill.restype = i32
             L.kvq_paged_prefill.argtypes = [P, P, i32, P, P, P, P, P, i32, P, i32, i32,
                                             i32, i32, i32, i32, i32, i32, i32,
@@ -334,4 +343,52 @@ def kvq_paged_prefill(q: torch.Tensor, query_start: torch.Tensor, max_query_len:
                                  num_blocks, _fmt(fmt), group_size, softmax_scale, _ptr(out),
                                  _stream(stream))
     _check(st, "kvq_paged_prefill")
+    return out
+
+
+# ------------------------------------------------------------------ head subsets
+def kvq_cache_write_heads(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor,
+                          kv_head_ids: torch.Tensor, k_pool: torch.Tensor,
+                          v_pool: torch.Tensor, k_scale: Optional[torch.Tensor],
+                          v_scale: Optional[torch.Tensor], fmt: str, group_size: int = 0,
+                          stream=None) -> None:
+    """kvq_cache_write into a pool that holds the model's KV heads
+    ``kv_head_ids`` (int32 on the device); k, v carry all the model's heads."""
+    num_blocks, hkv, bs, d = _pool_geometry(k_pool, fmt)
+    T, hsrc, dk = k.shape
+    if kv_head_ids.dtype != torch.int32 or kv_head_ids.numel() != hkv:
+        raise ValueError("kv_head_ids must be int32 [pool heads]")
+    st = lib().kvq_cache_write_heads(_ptr(k), _ptr(v), _ptr(slot_mapping), T, hsrc,
+                                     _ptr(kv_head_ids), hkv, d, bs, num_blocks, _fmt(fmt),
+                                     group_size, _ptr(k_pool), _ptr(v_pool), _ptr(k_scale),
+                                     _ptr(v_scale), _stream(stream))
+    _check(st, "kvq_cache_write_heads")
+
+
+def kvq_paged_decode_heads(q: torch.Tensor, num_kv_heads: int, kv_head_ids: torch.Tensor,
+                           k_pool: torch.Tensor, v_pool: torch.Tensor,
+                           k_scale: Optional[torch.Tensor], v_scale: Optional[torch.Tensor],
+                           block_tables: torch.Tensor, context_lens: torch.Tensor,
+                           max_context_len: int, fmt: str, group_size: int = 0,
+                           out: Optional[torch.Tensor] = None, workspace=None,
+                           softmax_scale: float = 0.0, split_tokens: int = 0,
+                           stream=None) -> torch.Tensor:
+    """kvq_paged_decode over a pool holding the model KV heads
+    ``kv_head_ids``; writes only their query heads' rows of ``out``."""
+    num_blocks, hkv, bs, d = _pool_geometry(k_pool, fmt)
+    B, hq, _ = q.shape
+    if out is None:
+        out = torch.zeros_like(q)
+    if workspace is None:
+        workspace = alloc_workspace(kvq_decode_workspace_size(
+            B, hkv * (hq // num_kv_heads), hkv, d, bs, max_context_len, split_tokens),
+            device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel()
+    st = lib().kvq_paged_decode_heads(_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(k_scale),
+                                      _ptr(v_scale), _ptr(block_tables), block_tables.shape[1],
+                                      _ptr(context_lens), max_context_len, B, hq,
+                                      num_kv_heads, _ptr(kv_head_ids), hkv, d, bs, num_blocks,
+                                      _fmt(fmt), group_size, softmax_scale, split_tokens,
+                                      _ptr(out), _ptr(workspace), ws_bytes, _stream(stream))
+    _check(st, "kvq_paged_decode_heads")
     return out

@@ -209,6 +209,23 @@ def test_bad_arguments_rejected_before_any_device_work(lib):
     assert dec(dt=3, G=0) == -3                   # E5M2 per head: valid, needs a workspace
     assert dec(dt=1, G=0) == -3                   # INT8 per channel: valid
     assert dec(dt=2, G=64) == -3                  # E4M3 per group: valid
+    # head subsets: a head list is required; the pool cannot hold more heads
+    # than the model has
+    a = dict(args)
+    assert lib.kvq_paged_decode_heads(a["q"], a["kp"], a["vp"], a["ks"], a["vs"], a["bt"],
+                                      a["mb"], a["cl"], a["mcl"], a["B"], a["Hq"], a["Hkv"],
+                                      None, 1, a["D"], a["BS"], a["nb"], a["dt"], a["G"],
+                                      a["sm"], 0, a["out"], None, 0, None) == -1
+    assert lib.kvq_paged_decode_heads(a["q"], a["kp"], a["vp"], a["ks"], a["vs"], a["bt"],
+                                      a["mb"], a["cl"], a["mcl"], a["B"], a["Hq"], a["Hkv"],
+                                      dummy, 3, a["D"], a["BS"], a["nb"], a["dt"], a["G"],
+                                      a["sm"], 0, a["out"], None, 0, None) == -1
+    assert lib.kvq_paged_decode_heads(a["q"], a["kp"], a["vp"], a["ks"], a["vs"], a["bt"],
+                                      a["mb"], a["cl"], a["mcl"], a["B"], a["Hq"], a["Hkv"],
+                                      dummy, 1, a["D"], a["BS"], a["nb"], a["dt"], a["G"],
+                                      a["sm"], 0, a["out"], None, 0, None) == -3
+    assert lib.kvq_cache_write_heads(dummy, dummy, dummy, 1, 2, None, 1, 64, 16, 4, 1, 64,
+                                     dummy, dummy, dummy, dummy, None) == -1
     assert dec(B=0) == 0
     assert dec(dt=1, ks=None) == -1
     assert lib.kvq_copy_blocks(dummy, 1, 1, 64, 16, 4, 1, 64, dummy, dummy, None, None,
