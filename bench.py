@@ -194,6 +194,97 @@ def prefill_cpu_baseline(case, spec, q, chunk, min_seconds: float) -> dict:
                       % (int(chunk[0]), ids.size, passes, total)}
 
 
+def run_mixed_heads(args, spec) -> int:
+    """Per-head mixed precision: the KV heads in spec.fp16_heads live in an
+    fp16 pool, the others in a pool of spec.fmt; a step appends one token per
+    sequence to both pools and runs one decode call per pool into the same
+    output."""
+    import dataclasses
+    import numpy as np
+    import torch
+
+    from paged_quantized_kv_cache_amd import kvq
+    from paged_quantized_kv_cache_amd import workloads as W
+    from paged_quantized_kv_cache_amd.harness import DecodeCase
+
+    kvq.lib()
+    dev = torch.device("cuda:0")
+    case = DecodeCase(spec, device=dev, poison=False)
+    d = case.gen(0)
+    L = case.layout
+    sens = list(spec.fp16_heads)
+    rest = [h for h in range(spec.Hkv) if h not in sens]
+    pools = []
+    for fmt, G, ids in ((spec.fmt, spec.G, rest), ("fp16", 0, sens)):
+        kp, vp, ks, vs = kvq.alloc_pools(L.num_blocks, len(ids), spec.BS, spec.D, fmt, G,
+                                         device=dev)
+        if W.static_scales(fmt, G, d.k[:, ids]) is not None:
+            ks.copy_(W.static_scales(fmt, G, d.k[:, ids]))
+            vs.copy_(W.static_scales(fmt, G, d.v[:, ids]))
+        ids_t = torch.tensor(ids, dtype=torch.int32, device=dev)
+        k = d.k.index_select(0, case.prefill_ids).to(dev).contiguous()
+        v = d.v.index_select(0, case.prefill_ids).to(dev).contiguous()
+        kvq.kvq_cache_write_heads(k, v, case.prefill_slots, ids_t, kp, vp, ks, vs, fmt, G)
+        ws = kvq.alloc_workspace(kvq.kvq_decode_workspace_size(
+            spec.B, len(ids) * spec.r, len(ids), spec.D, spec.BS, case.max_context_len),
+            device=dev)
+        pools.append((fmt, G, ids_t, kp, vp, ks, vs, ws))
+    ka, va = case.append_inputs(0)
+    q = d.q.to(dev).contiguous()
+    out = torch.empty_like(q)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        for fmt, G, ids_t, kp, vp, ks, vs, ws in pools:
+            kvq.kvq_cache_write_heads(ka, va, case.append_slots, ids_t, kp, vp, ks, vs, fmt, G)
+        if ev is not None:
+            ev[0].record(stream)
+        for fmt, G, ids_t, kp, vp, ks, vs, ws in pools:
+            kvq.kvq_paged_decode_heads(q, spec.Hkv, ids_t, kp, vp, ks, vs, case.block_tables,
+                                       case.context_lens, case.max_context_len, fmt, G,
+                                       out=out, workspace=ws)
+        if ev is not None:
+            ev[1].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(ev[i])
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    dec_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    nbytes = 0
+    for fmt, G, ids in ((spec.fmt, spec.G, rest), ("fp16", 0, sens)):
+        sub = dataclasses.replace(spec, Hkv=len(ids), Hq=len(ids) * spec.r, fmt=fmt, G=G)
+        nbytes += W.algorithmic_bytes(sub, case.lens, fmt)
+    achieved = nbytes / (dec_ms * 1e-3) / 1e9
+    result = {
+        "metric": METRIC, "value": spec.B / (ms_per_step * 1e-3), "unit": "seq-steps/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "mixed",
+        "data": "synthetic (seeded N(0,1) fp16 K/V/Q with outlier channels, shuffled "
+                "block pool)",
+        "config": {"workload": spec.name, "description": spec.description,
+                   "num_seqs": spec.B, "num_q_heads": spec.Hq, "num_kv_heads": spec.Hkv,
+                   "fp16_kv_heads": sens, "head_dim": spec.D, "block_size": spec.BS,
+                   "cached_tokens": int(case.lens.sum())},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": None,
+                     "kernel": "kvq_paged_decode_heads x2 (int8 pool + fp16 pool)",
+                     "algorithmic_bytes_per_launch": int(nbytes),
+                     "avg_launch_ms": round(dec_ms, 5)},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 def run_prefill(args, spec) -> int:
     """A prefill workload: one step writes every prompt token's K/V into the
     pool (kvq_cache_write) and runs causal attention of the prompts over it
@@ -300,6 +391,8 @@ def main(argv=None) -> int:
     spec = W.spec(args.workload)
     if spec.chunk > 0:
         return run_prefill(args, spec)
+    if spec.fp16_heads:
+        return run_mixed_heads(args, spec)
     t_setup = time.perf_counter()
     case = DecodeCase(spec, device=dev, poison=False)
     inputs = []

@@ -58,6 +58,7 @@ class Spec:
     shared_prefix: int = 0        # tokens shared by all sequences
     fork_pairs: int = 0           # pairs (2k, 2k+1) also sharing a partial tail
     chunk: int = 0                # > 0: a prefill workload, chunks of min(chunk, ctx)
+    fp16_heads: Tuple[int, ...] = ()   # KV heads kept in an fp16 pool of their own
     description: str = ""
 
     @property
@@ -121,6 +122,12 @@ SPECS: Dict[str, Spec] = {
         lens="lognormal", lens_args=(2048, 16, 8192), seed=0,
         k_out=Outliers(5, 10.0),
         description="the GQA layer, INT8 with static per-channel scales"),
+    "c3_mixed_heads": Spec(
+        "c3_mixed_heads", B=256, Hq=32, Hkv=8, D=128, BS=16, fmt="int8", G=64,
+        lens="lognormal", lens_args=(2048, 16, 8192), seed=0,
+        k_out=Outliers(5, 10.0), fp16_heads=(2, 5),
+        description="the GQA layer with KV heads 2 and 5 in fp16 and the other six "
+                    "in INT8 g64 (per-head mixed precision)"),
     "p1_prefill_gqa": Spec(
         "p1_prefill_gqa", B=16, Hq=32, Hkv=8, D=128, BS=16, fmt="int8", G=64,
         lens="fixed", lens_args=(2048,) * 16, seed=0, k_out=Outliers(5, 10.0),
