@@ -61,6 +61,8 @@ def _L():
             lib.orc_int8_quantize_rows.restype = i32
             lib.orc_int8_quantize_rows.argtypes = [P, i64, i32, i32, P, P]
             lib.orc_int8_dequantize_rows.argtypes = [P, P, i64, i32, i32, P]
+            lib.orc_int4_quantize_rows.restype = i32
+            lib.orc_int4_quantize_rows.argtypes = [P, i64, i32, i32, P, P]
             lib.orc_e4m3_decode.restype = ctypes.c_double
             lib.orc_e4m3_decode.argtypes = [ctypes.c_uint8]
             lib.orc_e4m3_encode.restype = ctypes.c_uint8
@@ -138,6 +140,24 @@ def int8_quantize(x, group_size: int):
     codes = np.empty(bits.shape, np.int8)
     scales = np.empty(bits.shape[:-1] + (d // group_size,), np.float32)
     rc = _L().orc_int8_quantize_rows(_ptr(bits), rows, d, group_size,
+                                     _ptr(codes), _ptr(scales))
+    if rc != 0:
+        raise ValueError("oracle: non-finite input or bad group size (%d)" % rc)
+    return codes, scales
+
+
+def int4_quantize(x, group_size: int):
+    """Per-group absmax INT4 along the last axis (codes in [-7, 7]).
+
+    Returns ``(codes int8 same shape, scales float32 [..., d/G])``."""
+    bits = _f16_bits(x)
+    d = bits.shape[-1]
+    if d % group_size:
+        raise ValueError("group_size must divide the last dimension")
+    rows = bits.size // d
+    codes = np.empty(bits.shape, np.int8)
+    scales = np.empty(bits.shape[:-1] + (d // group_size,), np.float32)
+    rc = _L().orc_int4_quantize_rows(_ptr(bits), rows, d, group_size,
                                      _ptr(codes), _ptr(scales))
     if rc != 0:
         raise ValueError("oracle: non-finite input or bad group size (%d)" % rc)

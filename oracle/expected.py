@@ -15,7 +15,7 @@ from typing import List, Optional, Sequence
 import numpy as np
 
 from . import (decode_attention, prefill_attention, fp8_dequantize, fp8_dequantize_groups,
-               fp8_quantize, fp8_quantize_groups, f16_to_f64,
+               fp8_quantize, fp8_quantize_groups, f16_to_f64, int4_quantize,
                int8_dequantize, int8_dequantize_channels, int8_quantize,
                int8_quantize_channels)
 
@@ -34,6 +34,9 @@ def quantize(x: np.ndarray, fmt: str, group_size: int = 0,
     fmt "int8": group_size > 0 per-group absmax; 0 per-channel with
     static_scale [Hkv][D].  fmt "fp8" (E4M3) / "e5m2": group_size 0 static
     per-head static_scale [Hkv]; > 0 dynamic per-group scales."""
+    if fmt == "int4":
+        c, s = int4_quantize(x, group_size)
+        return Quantized(c, s, int8_dequantize(c, s))
     if fmt == "int8":
         if group_size == 0:
             c = int8_quantize_channels(x, static_scale)

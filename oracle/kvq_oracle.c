@@ -139,7 +139,49 @@ ORC_API int orc_int8_quantize_rows(const uint16_t *x, int64_t rows, int d,
     return bad ? -1 : 0;
 }
 
-/* x_hat = code * scale, exact in fp64. */
+/* ------------------------------------------------------------------ */
+/* INT4 per-group absmax symmetric codec ([P3] s2.3 lists int4 among the */
+/* cache quantization methods; s3.3 and xpshop.cn article 402 s3 report  */
+/* its quality loss): the INT8 rule with 7 in place of 127.              */
+/* x: [rows][d] fp16 bits; codes: [rows][d] in [-7, 7]; scales [rows][d/G]*/
+/* ------------------------------------------------------------------ */
+ORC_API int orc_int4_quantize_rows(const uint16_t *x, int64_t rows, int d,
+                                   int G, int8_t *codes, float *scales)
+{
+    if (G <= 0 || d % G != 0)
+        return -2;
+    int ng = d / G;
+    int bad = 0;
+#pragma omp parallel for schedule(static) reduction(| : bad)
+    for (int64_t r = 0; r < rows; ++r)
+        for (int j = 0; j < ng; ++j) {
+            const uint16_t *xg = x + r * d + j * G;
+            float absmax = 0.0f;
+            for (int i = 0; i < G; ++i) {
+                double xd = orc_f16_to_f64(xg[i]);
+                if (!isfinite(xd))
+                    bad = 1;
+                else if (fabsf((float)xd) > absmax)
+                    absmax = fabsf((float)xd);
+            }
+            float s = absmax / 7.0f;                  /* IEEE fp32 division */
+            scales[r * ng + j] = s;
+            for (int i = 0; i < G; ++i) {
+                int8_t c = 0;
+                if (s != 0.0f) {
+                    float y = (float)orc_f16_to_f64(xg[i]) / s;
+                    float q = rintf(y);
+                    if (q > 7.0f) q = 7.0f;
+                    if (q < -7.0f) q = -7.0f;
+                    c = (int8_t)q;
+                }
+                codes[r * d + j * G + i] = c;
+            }
+        }
+    return bad ? -1 : 0;
+}
+
+/* x_hat = code * scale, exact in fp64 (INT8 and INT4 alike). */
 ORC_API void orc_int8_dequantize_rows(const int8_t *codes, const float *scales,
                                       int64_t rows, int d, int G, double *out)
 {

@@ -177,3 +177,29 @@ def test_fp8_static_zero_scale_gives_code_zero(fmt):
     codes = oracle.fp8_quantize(x16, S, fmt)
     assert np.all(codes[:, 1] == 0)
     assert np.all(oracle.fp8_dequantize(codes, S, fmt)[:, 1] == 0)
+
+
+# ------------------------------------------------------------------ INT4, per-group
+@pytest.mark.parametrize("G", [64, 128])
+def test_int4_codec_matches_independent_path(G):
+    rng = np.random.default_rng(15)
+    x = rng.standard_normal((300, 2, 128)).astype(np.float32)
+    x[:, :, 9] *= 30.0                  # an outlier channel
+    x[4, 1, :] = 0.0                    # an all-zero token-head
+    x16 = x.astype(np.float16)
+    codes, scales = oracle.int4_quantize(x16, G)
+    xg = x16.astype(np.float32).reshape(300, 2, 128 // G, G)
+    a = np.abs(xg).max(-1)
+    s = (a / np.float32(7)).astype(np.float32)          # IEEE fp32 division
+    safe = np.where(s == 0, np.float32(1), s)
+    y = (xg / safe[..., None]).astype(np.float32)
+    ref = np.clip(np.rint(y), -7, 7).astype(np.int8)
+    ref = np.where((s == 0)[..., None], np.int8(0), ref).reshape(codes.shape)
+    assert np.array_equal(scales, s) and np.array_equal(codes, ref)
+    # absmax element codes to +-7; error within half a step
+    assert np.all(np.abs(codes.reshape(xg.shape)).max(-1)[s > 0] == 7)
+    deq = oracle.int8_dequantize(codes, scales)
+    step = np.repeat(scales.astype(np.float64), G, axis=-1).reshape(deq.shape)
+    assert np.all(np.abs(deq - x16.astype(np.float64)) <= step * (0.5 + 2.0 ** -16))
+    q = E.quantize(x16, "int4", G)
+    assert np.array_equal(q.codes, codes) and np.array_equal(q.deq, deq)
