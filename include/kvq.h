@@ -38,6 +38,8 @@
  *      KVQ_FP8_E4M3  group_size 0: static per-KV-head scales; 64 / 128:
  *                    per-group scales computed by the cache write.
  *      KVQ_FP8_E5M2  group_size 0 only: static per-KV-head scales.
+ *      KVQ_INT4      head_dim 128 only; group_size 64 / 128: per-group
+ *                    scales computed by the cache write (s = absmax / 7).
  *      KVQ_FP16      group_size ignored, no scales.
  *  - Pointers to q, out, pools, scales and workspace must be 16-byte aligned.
  *
@@ -55,7 +57,15 @@
  *         half of a block).
  *   These orders let every 16-byte load of the decode kernel cover, across a
  *   wavefront, one contiguous KiB of whole cache lines.
- *   Per-group scales (INT8 or E4M3, group_size G > 0): k_scale, v_scale
+ *   INT4 (head_dim 128): codes in excess-8 form (nibble = code + 8), tiles of
+ *   block_size * 64 bytes.  Element (t, d) sits in the byte
+ *     K:  t * 64 + 16 * ((d%64)/16) + 4 * (2*(d/64) + (d%16)/8) + d%4,
+ *         high nibble if d%8 >= 4 (a dword holds 8 dims of one token),
+ *     V:  (t/16) * 1024 + ((((d%64)/4) * 4 + (t%16)/4) * 4 + 2*(d/64)
+ *           + (d%4)/2) * 4 + t%4,  high nibble if d is odd (a byte holds
+ *         two dims of one token, so writes of different tokens never share
+ *         a byte).
+ *   Per-group scales (INT8, INT4 or E4M3, group_size G > 0): k_scale, v_scale
  *   [num_blocks][Hkv][block_size][head_dim/G] fp32, one per (token slot,
  *   group of G consecutive head_dim elements), written by the cache write.
  *   Static per-channel scales (INT8, group_size 0): k_scale, v_scale
@@ -82,7 +92,8 @@ enum {
     KVQ_FP16 = 0,
     KVQ_INT8 = 1,      /* symmetric, |code| <= 127, per-group or per-channel */
     KVQ_FP8_E4M3 = 2,  /* OCP E4M3FN (max 448), per-head or per-group       */
-    KVQ_FP8_E5M2 = 3   /* OCP E5M2 (max 57344), per-head                    */
+    KVQ_FP8_E5M2 = 3,  /* OCP E5M2 (max 57344), per-head                    */
+    KVQ_INT4 = 4       /* symmetric, |code| <= 7, two per byte, per-group   */
 };
 
 typedef int32_t kvq_status;
@@ -127,6 +138,8 @@ KVQ_API int32_t kvq_version(void);
  *                 KVQ_FP8_E4M3, group_size G > 0: per group, s = fl32(a /
  *                   448), code = E4M3(fl32(x / s)) (a == 0: s = 0, codes 0);
  *                   s written to k_scale / v_scale like INT8.
+ *                 KVQ_INT4: the INT8 rule with 7 in place of 127; codes go
+ *                   to the pools as nibbles code + 8.
  *                 KVQ_FP16: the values are copied.
  * Tokens are independent; two tokens mapped to the same slot race.
  */

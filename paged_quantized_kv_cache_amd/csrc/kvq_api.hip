@@ -62,7 +62,10 @@ kvq_status check_format(int32_t dtype, int32_t head_dim, int32_t block_size,
                         int32_t group_size)
 {
     if (dtype != KVQ_FP16 && dtype != KVQ_INT8 && dtype != KVQ_FP8_E4M3 &&
-        dtype != KVQ_FP8_E5M2)
+        dtype != KVQ_FP8_E5M2 && dtype != KVQ_INT4)
+        return KVQ_ERR_UNSUPPORTED;
+    if (dtype == KVQ_INT4 &&
+        (head_dim != 128 || (group_size != 64 && group_size != 128)))
         return KVQ_ERR_UNSUPPORTED;
     if (head_dim != 64 && head_dim != 128)
         return KVQ_ERR_UNSUPPORTED;
@@ -78,6 +81,20 @@ kvq_status check_format(int32_t dtype, int32_t head_dim, int32_t block_size,
     if (dtype == KVQ_FP8_E5M2 && group_size != 0)
         return KVQ_ERR_UNSUPPORTED;
     return KVQ_OK;
+}
+
+// Per-group scale arrays exist (written by the cache write).
+bool has_group_scales(int32_t dtype, int32_t group_size)
+{
+    return (dtype == KVQ_INT8 || dtype == KVQ_FP8_E4M3 || dtype == KVQ_INT4) && group_size > 0;
+}
+
+// Bytes of one block's codes in one pool.
+int64_t block_code_bytes(int32_t dtype, int32_t num_kv_heads, int32_t block_size,
+                         int32_t head_dim)
+{
+    const int64_t elems = (int64_t)num_kv_heads * block_size * head_dim;
+    return dtype == KVQ_FP16 ? 2 * elems : (dtype == KVQ_INT4 ? elems / 2 : elems);
 }
 
 kvq_status launch_status()
@@ -148,7 +165,16 @@ void launch_write(const WriteParams &p, hipStream_t s)
 template <int FMT, int D>
 kvq_status dispatch_write_g(const WriteParams &p, int G, hipStream_t s)
 {
-    if constexpr (FMT == FMT_INT8 || FMT == FMT_FP8) {
+    if constexpr (FMT == FMT_INT4) {
+        if constexpr (D == 128) {
+            if (G == 64)
+                launch_write<FMT, D, 64>(p, s);
+            else
+                launch_write<FMT, D, 128>(p, s);
+        } else {
+            return KVQ_ERR_UNSUPPORTED;
+        }
+    } else if constexpr (FMT == FMT_INT8 || FMT == FMT_FP8) {
         if (G == 0)
             launch_write<FMT, D, 0>(p, s);
         else if (G == 64)
@@ -264,7 +290,12 @@ kvq_status launch_attention(const DecodeParams &p, const LaunchPlan *lp, hipStre
 template <int FMT, int D, int BS>
 kvq_status dispatch_decode_ng(const DecodeParams &p, const LaunchPlan *lp, int G, hipStream_t s)
 {
-    if constexpr (FMT == FMT_INT8 || FMT == FMT_FP8) {
+    if constexpr (FMT == FMT_INT4) {
+        if constexpr (D == 128)
+            return G == 64 ? launch_attention<FMT, D, BS, 2>(p, lp, s)
+                           : launch_attention<FMT, D, BS, 1>(p, lp, s);
+        return KVQ_ERR_UNSUPPORTED;
+    } else if constexpr (FMT == FMT_INT8 || FMT == FMT_FP8) {
         if (G == 0)
             return launch_attention<FMT, D, BS, 0>(p, lp, s);
         const int NG = D / G;
@@ -296,6 +327,7 @@ kvq_status dispatch_attention(const DecodeParams &p, const LaunchPlan *lp, int32
     case KVQ_INT8: return dispatch_decode<FMT_INT8>(p, lp, D, BS, G, s);
     case KVQ_FP8_E4M3: return dispatch_decode<FMT_FP8>(p, lp, D, BS, G, s);
     case KVQ_FP8_E5M2: return dispatch_decode<FMT_E5M2>(p, lp, D, BS, 0, s);
+    case KVQ_INT4: return dispatch_decode<FMT_INT4>(p, lp, D, BS, G, s);
     default: return dispatch_decode<FMT_FP16>(p, lp, D, BS, 0, s);
     }
 }
@@ -362,6 +394,7 @@ static kvq_status write_impl(const void *k, const void *v, const int64_t *slot_m
     case KVQ_INT8: return dispatch_write_d<FMT_INT8>(p, head_dim, group_size, s);
     case KVQ_FP8_E4M3: return dispatch_write_d<FMT_FP8>(p, head_dim, group_size, s);
     case KVQ_FP8_E5M2: return dispatch_write_d<FMT_E5M2>(p, head_dim, 0, s);
+    case KVQ_INT4: return dispatch_write_d<FMT_INT4>(p, head_dim, group_size, s);
     default: return dispatch_write_d<FMT_FP16>(p, head_dim, 0, s);
     }
 }
@@ -600,7 +633,7 @@ kvq_status kvq_copy_blocks(const int32_t *block_pairs, int32_t num_pairs, int32_
         return KVQ_OK;
     if (!block_pairs || !k_pool || !v_pool || !aligned16(k_pool) || !aligned16(v_pool))
         return KVQ_ERR_INVALID_ARG;
-    const bool group_scales = (dtype == KVQ_INT8 || dtype == KVQ_FP8_E4M3) && group_size > 0;
+    const bool group_scales = has_group_scales(dtype, group_size);
     if (group_scales && (!k_scale || !v_scale))
         return KVQ_ERR_INVALID_ARG;
     st = check_device();
@@ -612,8 +645,7 @@ kvq_status kvq_copy_blocks(const int32_t *block_pairs, int32_t num_pairs, int32_
     p.v_pool = static_cast<uint8_t *>(v_pool);
     p.k_scale = k_scale;
     p.v_scale = v_scale;
-    const int eb = dtype == KVQ_FP16 ? 2 : 1;
-    p.block_bytes = (int64_t)num_kv_heads * block_size * head_dim * eb;
+    p.block_bytes = block_code_bytes(dtype, num_kv_heads, block_size, head_dim);
     p.scale_block_floats =
         group_scales ? (int64_t)num_kv_heads * block_size * (head_dim / group_size) : 0;
     p.num_blocks = num_blocks;
@@ -628,9 +660,8 @@ size_t kvq_swap_block_bytes(int32_t num_kv_heads, int32_t head_dim, int32_t bloc
 {
     if (num_kv_heads <= 0 || check_format(dtype, head_dim, block_size, group_size) != KVQ_OK)
         return SIZE_MAX;
-    const int eb = dtype == KVQ_FP16 ? 2 : 1;
-    const bool group_scales = (dtype == KVQ_INT8 || dtype == KVQ_FP8_E4M3) && group_size > 0;
-    const size_t codes = (size_t)num_kv_heads * block_size * head_dim * eb;
+    const bool group_scales = has_group_scales(dtype, group_size);
+    const size_t codes = (size_t)block_code_bytes(dtype, num_kv_heads, block_size, head_dim);
     const size_t scales =
         group_scales ? (size_t)num_kv_heads * block_size * (head_dim / group_size) * 4 : 0;
     return (2 * codes + 2 * scales + 255) / 256 * 256;
@@ -651,7 +682,7 @@ kvq_status swap_blocks(const int32_t *pairs, int32_t num_pairs, int32_t num_kv_h
         return KVQ_ERR_INVALID_ARG;
     if (num_pairs == 0)
         return KVQ_OK;
-    const bool group_scales = (dtype == KVQ_INT8 || dtype == KVQ_FP8_E4M3) && group_size > 0;
+    const bool group_scales = has_group_scales(dtype, group_size);
     if (!pairs || !k_pool || !v_pool || !buffer || (group_scales && (!k_scale || !v_scale)))
         return KVQ_ERR_INVALID_ARG;
     if (!aligned16(k_pool) || !aligned16(v_pool) || !aligned16(buffer) ||
@@ -667,8 +698,7 @@ kvq_status swap_blocks(const int32_t *pairs, int32_t num_pairs, int32_t num_kv_h
     p.k_scale = group_scales ? reinterpret_cast<uint8_t *>(k_scale) : nullptr;
     p.v_scale = group_scales ? reinterpret_cast<uint8_t *>(v_scale) : nullptr;
     p.buf = static_cast<uint8_t *>(buffer);
-    const int eb = dtype == KVQ_FP16 ? 2 : 1;
-    p.block_bytes = (int64_t)num_kv_heads * block_size * head_dim * eb;
+    p.block_bytes = block_code_bytes(dtype, num_kv_heads, block_size, head_dim);
     p.scale_bytes =
         group_scales ? (int64_t)num_kv_heads * block_size * (head_dim / group_size) * 4 : 0;
     p.slot_bytes = (int64_t)kvq_swap_block_bytes(num_kv_heads, head_dim, block_size, dtype,

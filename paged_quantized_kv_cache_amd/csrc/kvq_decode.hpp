@@ -25,7 +25,8 @@
 //       micro-tile layout stores next to each other.
 // The head_dim order inside an MFMA k-step is a permutation chosen so that
 // each lane's K bytes are contiguous; q is loaded with the same permutation.
-// Codes are converted to exact fp16 (INT8 c + 1152, or E4M3 value * 2^-8)
+// Codes are converted to exact fp16 (INT8 c + 1152, INT4 c + 1032, or E4M3
+// value * 2^-8, or E5M2 value)
 // right before the MFMA; K group scales multiply the per-group partial dot
 // products (one accumulator per group); V group scales are folded into P
 // (rounded to fp16 once) so the token sum stays a single MFMA chain.
@@ -214,8 +215,9 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanParams p)
 // Per-lane registers of one 16-token tile.
 template <int FMT, int D>
 struct TileData {
-    static constexpr int EB = FMT == FMT_FP16 ? 2 : 1;
-    static constexpr int NL = D * EB / 64;  // 16-byte K loads (= V loads) per lane
+    static constexpr int EB = FMT == FMT_FP16 ? 2 : 1;  // INT4: q / output dim order as 1 byte
+    static constexpr int TB = FMT == FMT_INT4 ? D / 2 : D * EB;  // tile bytes per token
+    static constexpr int NL = TB / 64;      // 16-byte K loads (= V loads) per lane
     uint32_t k[4 * NL];
     uint32_t v[4 * NL];
     // INT8: one scale per lane.  Row grp (lanes 16 grp .. 16 grp + 15) holds
@@ -238,15 +240,16 @@ __device__ __forceinline__ void load_codes(const DecodeParams &p, TileData<FMT, 
                                            int col, int grp)
 {
     constexpr int EB = TileData<FMT, D>::EB;
+    constexpr int TB = TileData<FMT, D>::TB;
     constexpr int NL = TileData<FMT, D>::NL;
     // Buffer loads on a descriptor spanning one tile: the cache policy is an
     // immediate of each load (nt = bit 1 of the aux field on gfx950), and
     // offsets past the tile read zeros instead of faulting.
     constexpr int kAux = kNT ? 2 : 0;
     const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint8_t *>(kb), 0, BS * D * EB, kBufferConfig);
+        const_cast<uint8_t *>(kb), 0, BS * TB, kBufferConfig);
     const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint8_t *>(vb), 0, BS * D * EB, kBufferConfig);
+        const_cast<uint8_t *>(vb), 0, BS * TB, kBufferConfig);
 #pragma unroll
     for (int x = 0; x < NL; ++x) {
         // K chunk x of token toff + col: bytes [16 grp, 16 grp + 16) of its row
@@ -261,8 +264,11 @@ __device__ __forceinline__ void load_codes(const DecodeParams &p, TileData<FMT, 
     for (int x = 0; x < NL; ++x) {
         // V micro-tile: part e, dim quad col + 16 * g4, token quad toff/4 + grp
         const int e = x % EB, g4 = x / EB;
-        const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(
-            rv, ((((toff / 16) * EB + e) * (D / 4) + col + 16 * g4) * 4 + grp) * 16, 0, kAux);
+        // INT4: one 16-byte slice per lane, dim quad col x token quad grp
+        const int voff = FMT == FMT_INT4
+                             ? ((toff / 16) * 64 + col * 4 + grp) * 16
+                             : ((((toff / 16) * EB + e) * (D / 4) + col + 16 * g4) * 4 + grp) * 16;
+        const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(rv, voff, 0, kAux);
         t.v[4 * x + 0] = w.x;
         t.v[4 * x + 1] = w.y;
         t.v[4 * x + 2] = w.z;
@@ -276,10 +282,10 @@ template <int FMT, int D, int BS, int NG, bool kNT>
 __device__ __forceinline__ void load_tile(const DecodeParams &p, TileData<FMT, D> &t,
                                           int phys, int h, int toff, int col, int grp)
 {
-    constexpr int EB = TileData<FMT, D>::EB;
+    constexpr int TB = TileData<FMT, D>::TB;
     const int64_t tile = (int64_t)phys * p.Hkv + h;
-    const uint8_t *kb = p.k_pool + tile * (BS * D * EB);
-    const uint8_t *vb = p.v_pool + tile * (BS * D * EB);
+    const uint8_t *kb = p.k_pool + tile * (BS * TB);
+    const uint8_t *vb = p.v_pool + tile * (BS * TB);
     load_codes<FMT, D, BS, NG, kNT>(p, t, kb, vb, toff, col, grp);
     if constexpr (NG > 0) {  // per-group scales
         const int e = col % (8 * NG);
@@ -302,8 +308,11 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
     constexpr bool kGroup = NG > 0;
     constexpr int NA = kGroup ? NG : 1;        // score accumulators per tile
     constexpr int G = kGroup ? D / NG : D;     // group size
-    constexpr bool kInt8 = FMT == FMT_INT8;
-    constexpr bool kChannel = kInt8 && !kGroup;
+    // INT8 and INT4 codes enter the MFMAs biased (c + kBias)
+    constexpr bool kInt8 = FMT == FMT_INT8 || FMT == FMT_INT4;
+    constexpr float kBias = FMT == FMT_INT4 ? kInt4Bias : kInt8Bias;
+    constexpr bool kChannel = FMT == FMT_INT8 && !kGroup;
+    static_assert(FMT != FMT_INT4 || (D == 128 && kGroup), "INT4: head_dim 128, group scales");
     constexpr float kCodeScale = FMT == FMT_FP8 ? 256.0f : 1.0f;  // E4M3 enters as value * 2^-8
     static_assert(!kGroup || G >= 64, "groups must cover a 64-dim chunk");
 
@@ -443,7 +452,7 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
                 }
                 sum += __shfl_xor(sum, 16);
                 sum += __shfl_xor(sum, 32);
-                qbias[j] = kInt8Bias * sum;
+                qbias[j] = kBias * sum;
             }
         }
         float score_scale = score_scale0;
@@ -496,7 +505,11 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
 #pragma unroll
             for (int s = 0; s < KS; ++s) {
                 f16x4 a;
-                if constexpr (FMT == FMT_INT8) {
+                if constexpr (FMT == FMT_INT4) {  // a dword holds k-steps 2q, 2q + 1
+                    f16x4 lo, hi;
+                    int4x8_to_f16x4_biased(cur.k[s >> 1], lo, hi);
+                    a = (s & 1) ? hi : lo;
+                } else if constexpr (FMT == FMT_INT8) {
                     a = int8x4_to_f16x4_biased(cur.k[s]);
                 } else if constexpr (FMT == FMT_FP8) {
                     a = fp8x4_to_f16x4_scaled(cur.k[s]);
@@ -583,7 +596,11 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
             for (int tau = 0; tau < DT; ++tau) {
                 const int g4 = tau >> 2, i = tau & 3;
                 f16x4 a;
-                if constexpr (FMT == FMT_INT8) {
+                if constexpr (FMT == FMT_INT4) {  // a dword holds dims 4 col + i, i = 2x, 2x + 1
+                    f16x4 lo, hi;
+                    int4x8_to_f16x4_biased(cur.v[2 * g4 + (i >> 1)], lo, hi);
+                    a = (i & 1) ? hi : lo;
+                } else if constexpr (FMT == FMT_INT8) {
                     a = int8x4_to_f16x4_biased(cur.v[4 * g4 + i]);
                 } else if constexpr (FMT == FMT_FP8) {
                     a = fp8x4_to_f16x4_scaled(cur.v[4 * g4 + i]);
@@ -683,7 +700,7 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
             for (int j = 0; j < NA; ++j) {
                 float c = csum[j] + __shfl_xor(csum[j], 16);
                 c += __shfl_xor(c, 32);
-                csum[j] = kInt8Bias * c;
+                csum[j] = kBias * c;
             }
 #pragma unroll
             for (int tau = 0; tau < DT; ++tau)

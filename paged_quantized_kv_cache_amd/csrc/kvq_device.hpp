@@ -23,8 +23,9 @@
 
 namespace kvq {
 
-// FMT_FP8 is E4M3; FMT_E5M2 is the other OCP FP8 format.
-enum { FMT_FP16 = 0, FMT_INT8 = 1, FMT_FP8 = 2, FMT_E5M2 = 3 };
+// FMT_FP8 is E4M3; FMT_E5M2 is the other OCP FP8 format; FMT_INT4 packs two
+// codes per byte (head_dim 128 only).
+enum { FMT_FP16 = 0, FMT_INT8 = 1, FMT_FP8 = 2, FMT_E5M2 = 3, FMT_INT4 = 4 };
 
 // Largest finite value of each FP8 format.
 template <int FMT>
@@ -65,6 +66,7 @@ __device__ __forceinline__ uint32_t byte_perm(uint32_t hi, uint32_t lo,
 
 // Four excess-128 INT8 bytes (one dword) -> 4 exact fp16 holding c + 1152.
 constexpr float kInt8Bias = 1152.0f;
+constexpr float kInt4Bias = 1032.0f;  // 1024 + 8 (excess-8 nibbles)
 __device__ __forceinline__ f16x4 int8x4_to_f16x4_biased(uint32_t w)
 {
     const uint32_t lo = byte_perm(0x64646464u, w, 0x04010400u);  // 0x64 | byte 0, 0x64 | byte 1
@@ -85,6 +87,20 @@ __device__ __forceinline__ f16x4 fp8x4_to_f16x4_scaled(uint32_t w)
     const f16x2 a = bit_cast<f16x2>(h0);
     const f16x2 b = bit_cast<f16x2>(h1);
     return f16x4{a.x, a.y, b.x, b.y};
+}
+
+// Eight excess-8 INT4 nibbles (one dword) -> two f16x4 holding c + 1032:
+// `lo` from the low nibbles of bytes 0..3, `hi` from the high nibbles.
+__device__ __forceinline__ void int4x8_to_f16x4_biased(uint32_t w, f16x4 &lo, f16x4 &hi)
+{
+    const uint32_t l = w & 0x0f0f0f0fu;
+    const uint32_t h = (w >> 4) & 0x0f0f0f0fu;
+    const f16x2 a = bit_cast<f16x2>(byte_perm(0x64646464u, l, 0x04010400u));
+    const f16x2 b = bit_cast<f16x2>(byte_perm(0x64646464u, l, 0x04030402u));
+    const f16x2 c = bit_cast<f16x2>(byte_perm(0x64646464u, h, 0x04010400u));
+    const f16x2 d = bit_cast<f16x2>(byte_perm(0x64646464u, h, 0x04030402u));
+    lo = f16x4{a.x, a.y, b.x, b.y};
+    hi = f16x4{c.x, c.y, d.x, d.y};
 }
 
 // Four E5M2 bytes -> 4 fp16 of the same values (each byte becomes the high
@@ -176,6 +192,26 @@ __host__ __device__ constexpr int v_offset(int BS, int t, int d)
     return (((((t / 16) * EB + (d % 4) / (4 / EB)) * (D / 4) + d / 4) * 4 + (t % 16) / 4) * 16 +
             ((d % 4) % (4 / EB)) * 4 * EB + (t % 4) * EB);
 }
+
+// INT4 tiles (head_dim 128): 64 bytes per token of K, and per 16 tokens 1 KiB
+// of V.  Byte of element (token t, dim d) and whether it is the high nibble:
+// K: row t of 64 bytes; a 16-byte lane slice g = (d % 64) / 16 holds dwords
+//    q = 2 (d / 64) + (d % 16) / 8 of 8 dims each, byte j of a dword holding
+//    dims base + j (low nibble) and base + 4 + j (high).
+// V: per 16-token half, [16 dim quads][4 token quads][4 dwords q][4 tokens]:
+//    dword q = 2 (d / 64) + (d % 4) / 2 holds dims (even, odd) of a pair, byte
+//    t % 4 the token's two codes (even dim low, odd dim high).
+__host__ __device__ constexpr int int4_k_byte(int t, int d)
+{
+    return t * 64 + 16 * ((d % 64) / 16) + 4 * (2 * (d / 64) + (d % 16) / 8) + d % 4;
+}
+__host__ __device__ constexpr bool int4_k_high(int d) { return (d % 8) >= 4; }
+__host__ __device__ constexpr int int4_v_byte(int t, int d)
+{
+    return (t / 16) * 1024 + ((((d % 64) / 4) * 4 + (t % 16) / 4) * 4 + 2 * (d / 64) + (d % 4) / 2) * 4 +
+           t % 4;
+}
+__host__ __device__ constexpr bool int4_v_high(int d) { return (d % 2) == 1; }
 
 __device__ __forceinline__ float wave_max(float x)
 {

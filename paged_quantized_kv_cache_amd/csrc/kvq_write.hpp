@@ -94,17 +94,19 @@ __global__ __launch_bounds__(64 * kWriteWaves) void cache_write_kernel(WritePara
 #pragma unroll
         for (int o = 1; o < LPG; o <<= 1)
             a = fmaxf(a, __shfl_xor(a, o));
-        constexpr float kMaxCode = FMT == FMT_INT8 ? 127.0f : fp8_max<FMT>();
+        constexpr float kMaxCode =
+            FMT == FMT_INT8 ? 127.0f : (FMT == FMT_INT4 ? 7.0f : fp8_max<FMT>());
         const float s = a / kMaxCode;           // IEEE division (correctly rounded)
 #pragma unroll
         for (int i = 0; i < EPL; ++i) {
-            if constexpr (FMT == FMT_INT8) {
+            if constexpr (FMT == FMT_INT8 || FMT == FMT_INT4) {
                 float q = 0.0f;
                 if (s != 0.0f) {
                     q = __builtin_rintf(x[i] / s);  // round half to even
-                    q = fminf(fmaxf(q, -127.0f), 127.0f);
+                    q = fminf(fmaxf(q, -kMaxCode), kMaxCode);
                 }
-                code[i] = (uint32_t)((int32_t)q + 128);  // stored in excess-128 form
+                // stored in excess-128 (INT8) / excess-8 (INT4) form
+                code[i] = (uint32_t)((int32_t)q + (FMT == FMT_INT8 ? 128 : 8));
             } else {
                 code[i] = s != 0.0f ? fp8_rne_sat<FMT>(x[i] / s) : 0u;
             }
@@ -131,6 +133,32 @@ __global__ __launch_bounds__(64 * kWriteWaves) void cache_write_kernel(WritePara
 #pragma unroll
         for (int i = 0; i < EPL; ++i)
             code[i] = S != 0.0f ? fp8_rne_sat<FMT>(x[i] / S) : 0u;  // zero scale: code 0
+    }
+
+    if constexpr (FMT == FMT_INT4) {
+        // nibble layouts: see int4_k_byte / int4_v_byte (kvq_device.hpp).  A
+        // K dword holds the 4 low-nibble dims of the even lane of a pair and
+        // the 4 high-nibble dims of the odd one; a V byte holds two dims of
+        // this token.
+        static_assert(D == 128 && EPL == 4, "INT4 tiles are laid out for head_dim 128");
+        uint8_t *tile = (is_v ? p.v_pool : p.k_pool) + head_base * ((int64_t)BS * 64);
+        uint32_t pc[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            pc[i] = (uint32_t)__shfl_xor((int)code[i], 1);
+        if (!is_v) {
+            if ((lane & 1) == 0) {
+                uint32_t wv = 0;
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    wv |= (code[j] | (pc[j] << 4)) << (8 * j);
+                *reinterpret_cast<uint32_t *>(tile + int4_k_byte(off, e0)) = wv;
+            }
+        } else {
+            tile[int4_v_byte(off, e0)] = (uint8_t)(code[0] | (code[1] << 4));
+            tile[int4_v_byte(off, e0 + 2)] = (uint8_t)(code[2] | (code[3] << 4));
+        }
+        return;
     }
 
     // Tile layouts: see k_offset / v_offset (kvq_device.hpp).

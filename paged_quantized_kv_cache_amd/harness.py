@@ -185,7 +185,13 @@ class DecodeCase:
         layout documented in include/kvq.h."""
         p, s = self.pools[layer], self.spec
         eb = 2 if p.fmt == "fp16" else 1
-        koff, voff = tile_offsets(s.BS, s.D, eb)
+        if p.fmt == "int4":
+            (koff, khi), (voff, vhi) = int4_tile_offsets(s.BS, s.D)
+            koff, voff = koff[..., None], voff[..., None]
+            shift = {"k": torch.from_numpy(khi.astype(np.int64) * 4).to(self.device),
+                     "v": torch.from_numpy(vhi.astype(np.int64) * 4).to(self.device)}
+        else:
+            koff, voff = tile_offsets(s.BS, s.D, eb)
         kflat = p.k_pool.view(torch.uint8).reshape(p.k_pool.shape[0], s.Hkv, -1)
         vflat = p.v_pool.view(torch.uint8).reshape(p.v_pool.shape[0], s.Hkv, -1)
         bt = self.layout.block_tables
@@ -200,6 +206,11 @@ class DecodeCase:
                 o = torch.from_numpy(offs).to(self.device)[off]       # [n][D][eb]
                 rows = flat[blk]                                        # [n][Hkv][bytes]
                 g = torch.gather(rows, 2, o.reshape(n, 1, -1).expand(n, s.Hkv, -1))
+                if p.fmt == "int4":     # nibble code + 8 -> signed code
+                    sh = shift[name][off].reshape(n, 1, s.D)
+                    g = ((g.to(torch.int64) >> sh) & 0xF) - 8
+                    item[name] = g.to(torch.int8).cpu().numpy()
+                    continue
                 g = g.reshape(n, s.Hkv, s.D, eb).contiguous().cpu().numpy()
                 if eb == 2:
                     g = g.view(np.float16).reshape(n, s.Hkv, s.D)
@@ -213,6 +224,19 @@ class DecodeCase:
                 item["v_scale"] = p.v_scale[blk, :, off, :].cpu().numpy()
             out.append(item)
         return out
+
+
+def int4_tile_offsets(BS: int, D: int):
+    """INT4 tiles (head_dim 128): ``(byte [BS][D], high-nibble flag [BS][D])``
+    of every element of a K and a V tile."""
+    t = np.arange(BS)[:, None]
+    d = np.arange(D)[None, :]
+    k = t * 64 + 16 * ((d % 64) // 16) + 4 * (2 * (d // 64) + (d % 16) // 8) + d % 4
+    khi = np.broadcast_to((d % 8) >= 4, k.shape)
+    v = ((t // 16) * 1024 + ((((d % 64) // 4) * 4 + (t % 16) // 4) * 4 + 2 * (d // 64)
+                             + (d % 4) // 2) * 4 + t % 4)
+    vhi = np.broadcast_to((d % 2) == 1, v.shape)
+    return (k.astype(np.int64), khi), (v.astype(np.int64), vhi)
 
 
 def tile_offsets(BS: int, D: int, eb: int):

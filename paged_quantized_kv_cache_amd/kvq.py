@@ -23,11 +23,13 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libkvq.so")
 
-KVQ_FP16, KVQ_INT8, KVQ_FP8_E4M3, KVQ_FP8_E5M2 = 0, 1, 2, 3
-FORMATS = {"fp16": KVQ_FP16, "int8": KVQ_INT8, "fp8": KVQ_FP8_E4M3, "e5m2": KVQ_FP8_E5M2}
-# INT8 pools hold excess-128 bytes (code + 128), FP8 pools E4M3 / E5M2 bytes.
+KVQ_FP16, KVQ_INT8, KVQ_FP8_E4M3, KVQ_FP8_E5M2, KVQ_INT4 = 0, 1, 2, 3, 4
+FORMATS = {"fp16": KVQ_FP16, "int8": KVQ_INT8, "fp8": KVQ_FP8_E4M3, "e5m2": KVQ_FP8_E5M2,
+           "int4": KVQ_INT4}
+# INT8 pools hold excess-128 bytes (code + 128), FP8 pools E4M3 / E5M2 bytes,
+# INT4 pools two excess-8 nibbles per byte (a pool's last axis is head_dim / 2).
 POOL_DTYPES = {"fp16": torch.float16, "int8": torch.uint8, "fp8": torch.uint8,
-               "e5m2": torch.uint8}
+               "e5m2": torch.uint8, "int4": torch.uint8}
 
 
 def scale_mode(fmt: str, group_size: int) -> str:
@@ -148,8 +150,9 @@ def alloc_pools(num_blocks: int, num_kv_heads: int, block_size: int,
     fill: [Hkv] per head (FP8), [Hkv][head_dim] per channel (INT8).  FP16 has
     no scales (None)."""
     dt = POOL_DTYPES[fmt]
-    kp = torch.empty((num_blocks, num_kv_heads, block_size, head_dim), dtype=dt, device=device)
-    vp = torch.empty((num_blocks, num_kv_heads, block_size, head_dim), dtype=dt, device=device)
+    last = head_dim // 2 if fmt == "int4" else head_dim
+    kp = torch.empty((num_blocks, num_kv_heads, block_size, last), dtype=dt, device=device)
+    vp = torch.empty((num_blocks, num_kv_heads, block_size, last), dtype=dt, device=device)
     mode = scale_mode(fmt, group_size)
     if mode == "group":
         ng = head_dim // group_size
@@ -168,6 +171,8 @@ def alloc_pools(num_blocks: int, num_kv_heads: int, block_size: int,
 
 def _pool_geometry(k_pool: torch.Tensor, fmt: str):
     num_blocks, hkv, bs, d = k_pool.shape
+    if fmt == "int4":
+        d *= 2
     if k_pool.dtype != POOL_DTYPES[fmt]:
         raise TypeError("pool dtype %s does not match format %s" % (k_pool.dtype, fmt))
     return num_blocks, hkv, bs, d

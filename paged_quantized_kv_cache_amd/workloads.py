@@ -25,7 +25,7 @@ import torch
 
 from .block_manager import BlockManager
 
-FORMATS = ("fp16", "int8", "fp8", "e5m2")   # fp8 = E4M3
+FORMATS = ("fp16", "int8", "fp8", "e5m2", "int4")   # fp8 = E4M3
 
 
 @dataclass
@@ -122,6 +122,11 @@ SPECS: Dict[str, Spec] = {
         lens="lognormal", lens_args=(2048, 16, 8192), seed=0,
         k_out=Outliers(5, 10.0),
         description="the GQA layer, INT8 with static per-channel scales"),
+    "c3_int4": Spec(
+        "c3_int4", B=256, Hq=32, Hkv=8, D=128, BS=16, fmt="int4", G=64,
+        lens="lognormal", lens_args=(2048, 16, 8192), seed=0,
+        k_out=Outliers(5, 10.0),
+        description="the GQA layer with an INT4 g64 cache"),
     "c3_mixed_heads": Spec(
         "c3_mixed_heads", B=256, Hq=32, Hkv=8, D=128, BS=16, fmt="int8", G=64,
         lens="lognormal", lens_args=(2048, 16, 8192), seed=0,
@@ -406,9 +411,9 @@ def algorithmic_bytes(s: Spec, lens: np.ndarray, fmt: str,
     """Bytes a decode step must move at least once: every valid cached token's
     K and V codes (+ their scales), Q in, O out, the block-table entries read
     and the context lengths.  ``unique_tokens`` counts shared blocks once."""
-    elem = 2 if fmt == "fp16" else 1
     ntok = int(unique_tokens if unique_tokens is not None else lens.sum())
-    per_tok = s.Hkv * 2 * s.D * elem
+    code_bytes = {"fp16": 2 * s.D, "int4": s.D // 2}.get(fmt, s.D)   # per token and head
+    per_tok = s.Hkv * 2 * code_bytes
     G = s.G if fmt != "fp16" else 0
     if G > 0:                                              # per token-group scales
         per_tok += s.Hkv * 2 * (s.D // G) * 4

@@ -89,7 +89,7 @@ def _run(name, layers=(0,)):
 
 @pytest.mark.parametrize("name", ["c1_tiny", "c2_mha", "c3_gqa", "c3_gqa_fp16",
                                   "c4_long_bs16", "c4_long_bs32", "c4_long_e5m2",
-                                  "c3_fp8_token", "c3_int8_channel"])
+                                  "c3_fp8_token", "c3_int8_channel", "c3_int4"])
 def test_full_size_single_layer(name, gpu):
     _run(name)
 

@@ -62,6 +62,11 @@ SMALL_CASES = {
                           lens_args=(1, 17, 100, 257, 700)),
     "int8_channel_d64_bs32": small("c1_tiny", fmt="int8", G=0, B=3, Hq=16, Hkv=1, BS=32,
                                    pool_blocks=0, lens="fixed", lens_args=(2, 40, 97)),
+    # INT4 (two codes per byte)
+    "int4_g64_outliers": small("c3_gqa", fmt="int4", G=64, B=5, Hq=8, Hkv=2, lens="fixed",
+                               lens_args=(1, 17, 100, 257, 700)),
+    "int4_g128_bs32_r8": small("c2_mha", fmt="int4", G=128, B=4, Hq=16, Hkv=2, BS=32,
+                               lens="fixed", lens_args=(31, 32, 65, 400)),
 }
 
 

@@ -23,7 +23,7 @@ pytestmark = pytest.mark.gpu
 ATOL, RTOL = 2e-3, 1e-3
 CASES = ["c1_tiny", "gqa_int8_g64_outliers", "mha_int8_g128", "gqa_fp16", "fp8_bs32",
          "int8_bs32_g128_r8", "int8_d64_bs32_r16", "e5m2_bs16", "fp8_token_g128",
-         "int8_channel"]
+         "int8_channel", "int4_g64_outliers"]
 
 
 def _quantized(case, layer, seqs):

@@ -31,7 +31,7 @@ def _block_bytes(pool, blk):
 
 @pytest.mark.parametrize("staging", ["pinned_host", "device"])
 @pytest.mark.parametrize("name", ["gqa_int8_g64_outliers", "fp8_token_g128", "gqa_fp16",
-                                  "e5m2_bs16", "int8_channel"])
+                                  "e5m2_bs16", "int8_channel", "int4_g64_outliers"])
 def test_swap_round_trip_preserves_decode(name, staging, gpu):
     print("case", name, staging, flush=True)
     spec = dataclasses.replace(SMALL_CASES[name], pool_blocks=1024)

@@ -314,3 +314,33 @@ def test_swap_block_bytes_and_arguments(lib):
                             None, 0, None) == 0
     assert lib.kvq_swap_out(dummy, 1, 1, 96, 16, 4, 1, 64, dummy, dummy, dummy, dummy,
                             dummy, 1, None) == -2
+
+
+def test_int4_tile_layouts_are_bijections():
+    from paged_quantized_kv_cache_amd.harness import int4_tile_offsets
+    for bs in (16, 32):
+        (k, kh), (v, vh) = int4_tile_offsets(bs, 128)
+        for off, hi in ((k, kh), (v, vh)):
+            key = off * 2 + hi
+            assert len(np.unique(key)) == key.size == bs * 128
+            assert key.min() == 0 and key.max() == bs * 128 - 1
+        # a V byte never holds two tokens; a K byte never holds two tokens
+        for off in (k, v):
+            tok = np.broadcast_to(np.arange(bs)[:, None], off.shape)
+            byte_tok = {}
+            for b, t in zip(off.ravel(), tok.ravel()):
+                assert byte_tok.setdefault(int(b), int(t)) == int(t)
+
+
+def test_int4_arguments(lib):
+    P = ctypes.c_void_p
+    dummy = P(16)
+    # INT4: head_dim 128 and a group size of 64 or 128 only
+    assert lib.kvq_cache_write(dummy, dummy, dummy, 1, 1, 64, 16, 4, 4, 64,
+                               dummy, dummy, dummy, dummy, None) == -2
+    assert lib.kvq_cache_write(dummy, dummy, dummy, 1, 1, 128, 16, 4, 4, 0,
+                               dummy, dummy, dummy, dummy, None) == -2
+    assert lib.kvq_cache_write(None, dummy, dummy, 1, 1, 128, 16, 4, 4, 64,
+                               dummy, dummy, dummy, dummy, None) == -1
+    from paged_quantized_kv_cache_amd import kvq
+    assert kvq.kvq_swap_block_bytes(8, 128, 16, "int4", 64) == 2 * 8 * 16 * 64 + 2 * 8 * 16 * 2 * 4
