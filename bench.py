@@ -97,16 +97,48 @@ def cpu_baseline(case, layer_inputs, spec, max_seqs: int, min_seconds: float = 1
             E.attention(q, kq, vq, toks)
             total += time.perf_counter() - t0
             passes += 1
+    cores = oracle.num_threads()
+    single = None
+    if spec.layers == 1:
+        # the same work on one thread, on the first sequences of the sample
+        n1 = min(16, nseq)
+        sub = np.unique(np.concatenate(toks[:n1]))
+        remap1 = np.full(int(sub.max()) + 1, -1, np.int64)
+        remap1[sub] = np.arange(sub.size)
+        k1, v1 = k16[sub], v16[sub]
+        toks1 = [remap1[t] for t in toks[:n1]]
+        oracle.set_num_threads(1)
+        try:
+            t0 = time.perf_counter()
+            kq = E.quantize(k1, fmt, spec.G, sk)
+            vq = E.quantize(v1, fmt, spec.G, sv)
+            E.attention(q[:n1], kq, vq, toks1)
+            single = n1 / (time.perf_counter() - t0)
+        finally:
+            oracle.set_num_threads(cores)
     return {
         "value": nseq * passes / total,
         "unit": "seq-steps/s",
-        "cores": oracle.num_threads(),
+        "cores": cores,
         "kind": "oracle",
         "sample": "first %d of %d sequences (%d cached tokens per layer-pass, %d layer(s)): "
                   "quantize every cached and appended token, dequantize, fp64 attention; "
                   "%d pass(es), %.1f s" % (nseq, spec.B, ntok // len(layers), len(layers),
                                            passes, total),
+        "single_thread_value": single,
+        "cpu_model": cpu_model(),
     }
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def copy_bandwidth(nbytes: int = 2 << 30, reps: int = 5) -> float:
@@ -507,6 +539,9 @@ def main(argv=None) -> int:
             "avg_launch_ms": round(dom_ms, 5),
         },
         "decode_ms_per_layer": [round(float(x), 5) for x in per_layer_ms] if nl > 1 else None,
+        # spread of the timed calls of the dominant format (event times)
+        "decode_ms_p10_p50_p90": [round(float(x), 5) for x in
+                                  np.percentile(dec_ms[:, dom].ravel(), [10, 50, 90])],
         "measured_copy_gbps": round(copy_gbps, 1),
         "swap": swap,
         "setup_s": round(setup_s, 1),

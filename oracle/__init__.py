@@ -94,6 +94,7 @@ def _L():
             lib.orc_kv_cache_bytes_int8_group.restype = i64
             lib.orc_kv_cache_bytes_int8_group.argtypes = [i64] * 6
             lib.orc_num_threads.restype = i32
+            lib.orc_set_num_threads.argtypes = [i32]
             _lib = lib
     return _lib
 
@@ -117,6 +118,11 @@ def _f16_bits(x) -> np.ndarray:
 
 def num_threads() -> int:
     return int(_L().orc_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Threads of the oracle's parallel loops from now on."""
+    _L().orc_set_num_threads(int(n))
 
 
 # ---------------------------------------------------------------- fp16

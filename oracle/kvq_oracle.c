@@ -652,3 +652,15 @@ ORC_API int orc_num_threads(void)
     return 1;
 #endif
 }
+
+/* Threads used by the parallel loops from now on (for timing the oracle at
+ * one thread and at all cores). */
+ORC_API void orc_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    if (n > 0)
+        omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
