@@ -268,7 +268,8 @@ kvq_status launch_decode(DecodeParams p, const LaunchPlan &lp, hipStream_t s)
 template <int FMT, int D, int BS, int NG>
 kvq_status launch_prefill(const DecodeParams &p, hipStream_t s)
 {
-    const int64_t grid = (int64_t)p.groups * p.B * p.Hkv;
+    // (sequence, KV head) pairs rounded up to the 8 XCDs (see the kernel)
+    const int64_t grid = (int64_t)p.groups * (((int64_t)p.B * p.Hkv + 7) / 8 * 8);
     if (grid > (int64_t)INT32_MAX)
         return KVQ_ERR_UNSUPPORTED;
     if (grid == 0)
