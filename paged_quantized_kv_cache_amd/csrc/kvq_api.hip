@@ -264,12 +264,15 @@ kvq_status launch_decode(DecodeParams p, const LaunchPlan &lp, hipStream_t s)
     return launch_status();
 }
 
-// Chunked prefill: one wavefront per (chunk-token group, sequence, KV head).
+// Chunked prefill: one wavefront per (kPrefillGroups chunk-token groups,
+// sequence, KV head).
 template <int FMT, int D, int BS, int NG>
 kvq_status launch_prefill(const DecodeParams &p, hipStream_t s)
 {
-    // (sequence, KV head) pairs rounded up to the 8 XCDs (see the kernel)
-    const int64_t grid = (int64_t)p.groups * (((int64_t)p.B * p.Hkv + 7) / 8 * 8);
+    // wavefronts per (sequence, KV head) pair, times the pairs rounded up to
+    // the 8 XCDs (see the kernel)
+    const int64_t grid = (int64_t)((p.groups + kPrefillGroups - 1) / kPrefillGroups) *
+                         (((int64_t)p.B * p.Hkv + 7) / 8 * 8);
     if (grid > (int64_t)INT32_MAX)
         return KVQ_ERR_UNSUPPORTED;
     if (grid == 0)

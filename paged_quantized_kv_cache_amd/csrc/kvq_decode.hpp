@@ -332,6 +332,20 @@ __device__ __forceinline__ void load_tile(const DecodeParams &p, TileData<FMT, D
     }
 }
 
+// Query columns of one MFMA column group: this lane's query row (active) or
+// a harmless row (inactive: q is zeroed, nothing is written), its output
+// row, and the column's token bound (causal limit in prefill).
+struct Cols {
+    const f16 *qrow;
+    f16 *orow;
+    int tcol;
+    bool active;
+};
+
+// Chunked prefill: column groups per wavefront.  Each tile is loaded and its
+// codes converted once for all of them.
+constexpr int kPrefillGroups = 2;
+
 // kPrefill: chunked prefill instead of decode (see the end of the kernel).
 template <int FMT, int D, int BS, int NG, bool kPrefill = false>
 __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
@@ -344,6 +358,7 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
     // one per (KV head, channel) (INT8), none (fp16).
     constexpr bool kGroup = NG > 0;
     constexpr int NA = kGroup ? NG : 1;        // score accumulators per tile
+    constexpr int NQ = kPrefill ? kPrefillGroups : 1;  // column groups per wavefront
     constexpr int G = kGroup ? D / NG : D;     // group size
     // INT8 and INT4 codes enter the MFMAs biased (c + kBias)
     constexpr bool kInt8 = FMT == FMT_INT8 || FMT == FMT_INT4;
@@ -413,49 +428,52 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
     int run_len = 0, run_after = 0;
 
     // Attend over tiles [t0, t1) of unit (b, h); ctx clamped to the host
-    // bound.  Per lane: the query row of its column (active) or a harmless
-    // row (inactive: q is zeroed, nothing is written), the output row, and
-    // tcol, the column's own token bound (causal limit in prefill).
+    // bound.  cg[q]: the columns of group q (see Cols); every loaded tile
+    // serves all NQ groups.
     auto attend = [&](const int b, const int h, const int ctx, const int n, const int t0,
-                      const int t1, const f16 *qrow, const bool active, const int tcol,
-                      f16 *orow_base) {
+                      const int t1, const Cols (&cg)[NQ]) {
         const int t_end = min(ctx, 16 * t1);  // token bound of this run (data)
-        const int t_col = min(t_end, tcol);   // score bound of this lane's column
+        int t_col[NQ];                        // score bound of this lane's columns
+#pragma unroll
+        for (int q = 0; q < NQ; ++q)
+            t_col[q] = min(t_end, cg[q].tcol);
 
         // ---- query operand, in the k-step dim order of the K loads:
         //   1-byte codes: k-step s, lane group grp, element v -> dim
         //       64 (s/4) + 16 grp + 4 (s%4) + v
         //   fp16:   32 (s/2) + 8 grp + 4 (s%2) + v
-        f16x4 qop[KS];
-        {
+        f16x4 qop[NQ][KS];
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+            const f16 *qrow = cg[q].qrow;
             if constexpr (EB == 1) {
 #pragma unroll
                 for (int c = 0; c < D / 64; ++c) {
                     const uint4 w0 = *reinterpret_cast<const uint4 *>(qrow + 64 * c + 16 * grp);
                     const uint4 w1 = *reinterpret_cast<const uint4 *>(qrow + 64 * c + 16 * grp + 8);
-                    qop[4 * c + 0] = f16x4_from_u2(w0.x, w0.y);
-                    qop[4 * c + 1] = f16x4_from_u2(w0.z, w0.w);
-                    qop[4 * c + 2] = f16x4_from_u2(w1.x, w1.y);
-                    qop[4 * c + 3] = f16x4_from_u2(w1.z, w1.w);
+                    qop[q][4 * c + 0] = f16x4_from_u2(w0.x, w0.y);
+                    qop[q][4 * c + 1] = f16x4_from_u2(w0.z, w0.w);
+                    qop[q][4 * c + 2] = f16x4_from_u2(w1.x, w1.y);
+                    qop[q][4 * c + 3] = f16x4_from_u2(w1.z, w1.w);
                 }
             } else {
 #pragma unroll
                 for (int c = 0; c < D / 32; ++c) {
                     const uint4 w4 = *reinterpret_cast<const uint4 *>(qrow + 32 * c + 8 * grp);
-                    qop[2 * c + 0] = f16x4_from_u2(w4.x, w4.y);
-                    qop[2 * c + 1] = f16x4_from_u2(w4.z, w4.w);
+                    qop[q][2 * c + 0] = f16x4_from_u2(w4.x, w4.y);
+                    qop[q][2 * c + 1] = f16x4_from_u2(w4.z, w4.w);
                 }
             }
-            if (!active) {
+            if (!cg[q].active) {
 #pragma unroll
                 for (int s = 0; s < KS; ++s)
-                    qop[s] = f16x4{0, 0, 0, 0};
+                    qop[q][s] = f16x4{0, 0, 0, 0};
             }
         }
         // INT8 per channel: K's channel scales ride on q, q' = q * s_d, as an
         // fp16 pair hi + lo (hi = fp16(q'), lo = fp16(q' - hi)) so the dot
         // products keep ~22 bits of q'; both halves go through the MFMA.
-        f16x4 qlo[kChannel ? KS : 1];
+        f16x4 qlo[NQ][kChannel ? KS : 1];
         if constexpr (kChannel) {
             const float *srow = p.k_scale + (int64_t)h * D;
 #pragma unroll
@@ -464,13 +482,16 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
                 for (int u = 0; u < 4; ++u) {  // dims 64 c + 16 grp + 4 u + (0..3)
                     const float4 sc4 = *reinterpret_cast<const float4 *>(srow + 64 * c + 16 * grp + 4 * u);
                     const float scv[4] = {sc4.x, sc4.y, sc4.z, sc4.w};
-                    f16x4 &hi = qop[4 * c + u];
 #pragma unroll
-                    for (int v = 0; v < 4; ++v) {
-                        const float qs = (float)hi[v] * scv[v];
-                        const f16 h16 = (f16)qs;
-                        hi[v] = h16;
-                        qlo[4 * c + u][v] = (f16)(qs - (float)h16);
+                    for (int q = 0; q < NQ; ++q) {
+                        f16x4 &hi = qop[q][4 * c + u];
+#pragma unroll
+                        for (int v = 0; v < 4; ++v) {
+                            const float qs = (float)hi[v] * scv[v];
+                            const f16 h16 = (f16)qs;
+                            hi[v] = h16;
+                            qlo[q][4 * c + u][v] = (f16)(qs - (float)h16);
+                        }
                     }
                 }
             }
@@ -479,20 +500,25 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
         // The score of group j is corrected by 1152 * (sum of q over the
         // group); the output by 1152 * (sum of the P^T operand entries of the
         // group), accumulated in csum with the same rescales as o.
-        float qbias[NA];
+        float qbias[NQ][NA];
         if constexpr (kInt8) {
+#pragma unroll
+            for (int q = 0; q < NQ; ++q)
 #pragma unroll
             for (int j = 0; j < NA; ++j) {
                 float sum = 0.0f;
 #pragma unroll
                 for (int s = j * (KS / NA); s < (j + 1) * (KS / NA); ++s) {
-                    sum += ((float)qop[s][0] + (float)qop[s][1]) + ((float)qop[s][2] + (float)qop[s][3]);
-                    if constexpr (kChannel)
-                        sum += ((float)qlo[s][0] + (float)qlo[s][1]) + ((float)qlo[s][2] + (float)qlo[s][3]);
+                    const f16x4 &x = qop[q][s];
+                    sum += ((float)x[0] + (float)x[1]) + ((float)x[2] + (float)x[3]);
+                    if constexpr (kChannel) {
+                        const f16x4 &y = qlo[q][s];
+                        sum += ((float)y[0] + (float)y[1]) + ((float)y[2] + (float)y[3]);
+                    }
                 }
                 sum += __shfl_xor(sum, 16);
                 sum += __shfl_xor(sum, 32);
-                qbias[j] = kBias * sum;
+                qbias[q][j] = kBias * sum;
             }
         }
         float score_scale = score_scale0;
@@ -513,17 +539,21 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
             lane_tok = 4 * grp + (e % (4 * NG)) / NG;
         }
 
-        // o[tau][v]: output dim 64 (tau / 4) + 16 grp + 4 v + tau % 4, head col
-        f32x4 o[DT];
+        // o[q][tau][v]: output dim 64 (tau / 4) + 16 grp + 4 v + tau % 4 of
+        // column col of group q; m, l, csum likewise per group
+        f32x4 o[NQ][DT];
+        float m[NQ], l[NQ], csum[NQ][NA];
 #pragma unroll
-        for (int i = 0; i < DT; ++i)
-            o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-        float m = -INFINITY;
-        float l = 0.0f;
-        float csum[NA];
+        for (int q = 0; q < NQ; ++q) {
 #pragma unroll
-        for (int j = 0; j < NA; ++j)
-            csum[j] = 0.0f;
+            for (int i = 0; i < DT; ++i)
+                o[q][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+            m[q] = -INFINITY;
+            l[q] = 0.0f;
+#pragma unroll
+            for (int j = 0; j < NA; ++j)
+                csum[q][j] = 0.0f;
+        }
 
         // One tile of 16 tokens starting at logical token ts, data in `cur`.
         auto process = [&](const TileData<FMT, D> &cur, const int ts) {
@@ -537,11 +567,13 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
                     sv[i / NG][i % NG] = row_bcast<4 * NG + i>(sc);
                 });
             }
-            // ---- S^T = K Q^T, one accumulator per scale group
-            f32x4 sacc[NA];
+            // ---- S^T = K Q^T, one accumulator per scale group (and column group)
+            f32x4 sacc[NQ][NA];
 #pragma unroll
-            for (int i = 0; i < NA; ++i)
-                sacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int q = 0; q < NQ; ++q)
+#pragma unroll
+                for (int i = 0; i < NA; ++i)
+                    sacc[q][i] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int s = 0; s < KS; ++s) {
                 f16x4 a;
@@ -559,61 +591,71 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
                     a = f16x4_from_u2(cur.k[2 * s], cur.k[2 * s + 1]);
                 }
                 const int gi = NA == 2 ? (s >> 2) : 0;
-                sacc[gi] = __builtin_amdgcn_mfma_f32_16x16x16f16(a, qop[s], sacc[gi], 0, 0, 0);
-                if constexpr (kChannel)
-                    sacc[0] = __builtin_amdgcn_mfma_f32_16x16x16f16(a, qlo[s], sacc[0], 0, 0, 0);
+#pragma unroll
+                for (int q = 0; q < NQ; ++q) {
+                    sacc[q][gi] =
+                        __builtin_amdgcn_mfma_f32_16x16x16f16(a, qop[q][s], sacc[q][gi], 0, 0, 0);
+                    if constexpr (kChannel)
+                        sacc[q][0] =
+                            __builtin_amdgcn_mfma_f32_16x16x16f16(a, qlo[q][s], sacc[q][0], 0, 0, 0);
+                }
             }
             // ---- scores of tokens ts + 4 grp + v for query head col (base 2)
             const int tok0 = ts + 4 * grp;
-            float z[4];
+            f16x4 pop[NQ][NA];
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                float acc;
-                if constexpr (kGroup) {
-                    acc = (kInt8 ? sacc[0][v] - qbias[0] : sacc[0][v]) * sk[v][0];
-                    if constexpr (NA == 2)
-                        acc += (kInt8 ? sacc[1][v] - qbias[1] : sacc[1][v]) * sk[v][1];
-                } else if constexpr (kInt8) {
-                    acc = (sacc[0][v] - qbias[0]) * score_scale;
-                } else {
-                    acc = sacc[0][v] * score_scale;
+            for (int q = 0; q < NQ; ++q) {
+                float z[4];
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    float acc;
+                    if constexpr (kGroup) {
+                        acc = (kInt8 ? sacc[q][0][v] - qbias[q][0] : sacc[q][0][v]) * sk[v][0];
+                        if constexpr (NA == 2)
+                            acc += (kInt8 ? sacc[q][1][v] - qbias[q][1] : sacc[q][1][v]) * sk[v][1];
+                    } else if constexpr (kInt8) {
+                        acc = (sacc[q][0][v] - qbias[q][0]) * score_scale;
+                    } else {
+                        acc = sacc[q][0][v] * score_scale;
+                    }
+                    z[v] = (tok0 + v < t_col[q]) ? acc : -INFINITY;
                 }
-                z[v] = (tok0 + v < t_col) ? acc : -INFINITY;
-            }
-            // ---- online softmax
-            float mt = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
-            mt = fmaxf(mt, __shfl_xor(mt, 16));
-            mt = fmaxf(mt, __shfl_xor(mt, 32));
-            if (__builtin_amdgcn_ballot_w64(mt > m)) {
-                const float mn = fmaxf(m, mt);
-                const float alpha = __builtin_amdgcn_exp2f(m - mn);
-                l *= alpha;
+                // ---- online softmax
+                float mt = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
+                mt = fmaxf(mt, __shfl_xor(mt, 16));
+                mt = fmaxf(mt, __shfl_xor(mt, 32));
+                if (__builtin_amdgcn_ballot_w64(mt > m[q])) {
+                    const float mn = fmaxf(m[q], mt);
+                    const float alpha = __builtin_amdgcn_exp2f(m[q] - mn);
+                    l[q] *= alpha;
 #pragma unroll
-                for (int i = 0; i < DT; ++i)
-                    o[i] *= alpha;
+                    for (int i = 0; i < DT; ++i)
+                        o[q][i] *= alpha;
 #pragma unroll
-                for (int j = 0; j < NA; ++j)
-                    csum[j] *= alpha;
-                m = mn;
-            }
-            float pr[4];
+                    for (int j = 0; j < NA; ++j)
+                        csum[q][j] *= alpha;
+                    m[q] = mn;
+                }
+                float pr[4];
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                pr[v] = __builtin_amdgcn_exp2f(z[v] - m);
-                l += pr[v];
-            }
-            // ---- P^T operands (V group scales folded in; masked tokens have
-            // pr = 0 and a zeroed scale)
-            f16x4 pop[NA];
+                for (int v = 0; v < 4; ++v) {
+                    pr[v] = __builtin_amdgcn_exp2f(z[v] - m[q]);
+                    l[q] += pr[v];
+                }
+                // ---- P^T operands (V group scales folded in; masked tokens
+                // have pr = 0 and a zeroed scale)
 #pragma unroll
-            for (int j = 0; j < NA; ++j) {
+                for (int j = 0; j < NA; ++j) {
 #pragma unroll
-                for (int v = 0; v < 4; ++v)
-                    pop[j][v] = kGroup ? (f16)(pr[v] * sv[v][j]) : (f16)pr[v];
-                if constexpr (kInt8) {
-                    const f16x2 ones = {(f16)1.0f, (f16)1.0f};
-                    csum[j] = __builtin_amdgcn_fdot2(f16x2{pop[j][0], pop[j][1]}, ones, csum[j], false);
-                    csum[j] = __builtin_amdgcn_fdot2(f16x2{pop[j][2], pop[j][3]}, ones, csum[j], false);
+                    for (int v = 0; v < 4; ++v)
+                        pop[q][j][v] = kGroup ? (f16)(pr[v] * sv[v][j]) : (f16)pr[v];
+                    if constexpr (kInt8) {
+                        const f16x2 ones = {(f16)1.0f, (f16)1.0f};
+                        csum[q][j] = __builtin_amdgcn_fdot2(f16x2{pop[q][j][0], pop[q][j][1]},
+                                                            ones, csum[q][j], false);
+                        csum[q][j] = __builtin_amdgcn_fdot2(f16x2{pop[q][j][2], pop[q][j][3]},
+                                                            ones, csum[q][j], false);
+                    }
                 }
             }
             // ---- O^T += V^T P^T; d-tile tau covers dims 64 (tau/4) + 4 m + tau%4
@@ -652,7 +694,9 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
                     a = f16x4_from_u2(cur.v[4 * x + wd] & vmask01, cur.v[4 * x + wd + 1] & vmask23);
                 }
                 const int gi = NA == 2 ? (64 * g4) / G : 0;
-                o[tau] = __builtin_amdgcn_mfma_f32_16x16x16f16(a, pop[gi], o[tau], 0, 0, 0);
+#pragma unroll
+                for (int q = 0; q < NQ; ++q)
+                    o[q][tau] = __builtin_amdgcn_mfma_f32_16x16x16f16(a, pop[q][gi], o[q][tau], 0, 0, 0);
             }
         };
 
@@ -736,66 +780,71 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
             walk(ts, t1, std::true_type{});
 
         // ---- epilogue: lane holds dims 64 g4 + 16 grp + (0..15) of head col
-        float lt = l + __shfl_xor(l, 16);
-        lt += __shfl_xor(lt, 32);
-        if constexpr (kInt8) {
-            // remove the code bias: o -= 1152 * (sum of P^T entries of the group)
 #pragma unroll
-            for (int j = 0; j < NA; ++j) {
-                float c = csum[j] + __shfl_xor(csum[j], 16);
-                c += __shfl_xor(c, 32);
-                csum[j] = kBias * c;
+        for (int q = 0; q < NQ; ++q) {
+            float lt = l[q] + __shfl_xor(l[q], 16);
+            lt += __shfl_xor(lt, 32);
+            if constexpr (kInt8) {
+                // remove the code bias: o -= 1152 * (sum of P^T entries of the group)
+                float cb[NA];
+#pragma unroll
+                for (int j = 0; j < NA; ++j) {
+                    float c = csum[q][j] + __shfl_xor(csum[q][j], 16);
+                    c += __shfl_xor(c, 32);
+                    cb[j] = kBias * c;
+                }
+#pragma unroll
+                for (int tau = 0; tau < DT; ++tau)
+                    o[q][tau] -= cb[(64 * (tau >> 2)) / G];
             }
+            if (!cg[q].active)
+                continue;
+            if constexpr (kChannel) {
+                // V channel scales: o[4 g4 + i][v] is dim 64 g4 + 16 grp + 4 v + i
+                const float *srow = p.v_scale + (int64_t)h * D + 16 * grp;
 #pragma unroll
-            for (int tau = 0; tau < DT; ++tau)
-                o[tau] -= csum[(64 * (tau >> 2)) / G];
-        }
-        if (!active)
-            return;
-        if constexpr (kChannel) {
-            // V channel scales: o[4 g4 + i][v] is dim 64 g4 + 16 grp + 4 v + i
-            const float *srow = p.v_scale + (int64_t)h * D + 16 * grp;
+                for (int g4 = 0; g4 < D / 64; ++g4)
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) {
+                        const float4 sc4 = *reinterpret_cast<const float4 *>(srow + 64 * g4 + 4 * v);
+                        o[q][4 * g4 + 0][v] *= sc4.x;
+                        o[q][4 * g4 + 1][v] *= sc4.y;
+                        o[q][4 * g4 + 2][v] *= sc4.z;
+                        o[q][4 * g4 + 3][v] *= sc4.w;
+                    }
+            }
+            if (t0 == 0 && t1 == n) {  // the whole unit: final output
+                const float inv = out_scale / lt;
+                f16 *orow = cg[q].orow + 16 * grp;
+#pragma unroll
+                for (int g4 = 0; g4 < D / 64; ++g4) {
+                    f16x4 hv[4];
+#pragma unroll
+                    for (int v = 0; v < 4; ++v)
+                        hv[v] = f16x4{(f16)(o[q][4 * g4 + 0][v] * inv), (f16)(o[q][4 * g4 + 1][v] * inv),
+                                      (f16)(o[q][4 * g4 + 2][v] * inv), (f16)(o[q][4 * g4 + 3][v] * inv)};
+#pragma unroll
+                    for (int v = 0; v < 4; ++v)
+                        *reinterpret_cast<f16x4 *>(orow + 64 * g4 + 4 * v) = hv[v];
+                }
+                continue;
+            }
+            // a piece of a unit: slot 0 if it continues a unit, slot 1 if it
+            // starts one (decode only: one column group)
+            const int slot = t0 > 0 ? 0 : 1;
+            const int64_t idx = ((int64_t)w * 2 + slot) * p.r + col;
+            float *wacc = p.ws_acc + idx * D + 16 * grp;
 #pragma unroll
             for (int g4 = 0; g4 < D / 64; ++g4)
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
-                    const float4 sc4 = *reinterpret_cast<const float4 *>(srow + 64 * g4 + 4 * v);
-                    o[4 * g4 + 0][v] *= sc4.x;
-                    o[4 * g4 + 1][v] *= sc4.y;
-                    o[4 * g4 + 2][v] *= sc4.z;
-                    o[4 * g4 + 3][v] *= sc4.w;
+                    const f32x4 wv = {o[q][4 * g4 + 0][v] * out_scale, o[q][4 * g4 + 1][v] * out_scale,
+                                      o[q][4 * g4 + 2][v] * out_scale, o[q][4 * g4 + 3][v] * out_scale};
+                    *reinterpret_cast<f32x4 *>(wacc + 64 * g4 + 4 * v) = wv;
                 }
+            if (grp == 0)
+                *reinterpret_cast<float2 *>(p.ws_ml + 2 * idx) = make_float2(m[q], lt);
         }
-        if (t0 == 0 && t1 == n) {  // the whole unit: final output
-            const float inv = out_scale / lt;
-            f16 *orow = orow_base + 16 * grp;
-#pragma unroll
-            for (int g4 = 0; g4 < D / 64; ++g4) {
-                f16x4 hv[4];
-#pragma unroll
-                for (int v = 0; v < 4; ++v)
-                    hv[v] = f16x4{(f16)(o[4 * g4 + 0][v] * inv), (f16)(o[4 * g4 + 1][v] * inv),
-                                  (f16)(o[4 * g4 + 2][v] * inv), (f16)(o[4 * g4 + 3][v] * inv)};
-#pragma unroll
-                for (int v = 0; v < 4; ++v)
-                    *reinterpret_cast<f16x4 *>(orow + 64 * g4 + 4 * v) = hv[v];
-            }
-            return;
-        }
-        // a piece of a unit: slot 0 if it continues a unit, slot 1 if it starts one
-        const int slot = t0 > 0 ? 0 : 1;
-        const int64_t idx = ((int64_t)w * 2 + slot) * p.r + col;
-        float *wacc = p.ws_acc + idx * D + 16 * grp;
-#pragma unroll
-        for (int g4 = 0; g4 < D / 64; ++g4)
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const f32x4 wv = {o[4 * g4 + 0][v] * out_scale, o[4 * g4 + 1][v] * out_scale,
-                                  o[4 * g4 + 2][v] * out_scale, o[4 * g4 + 3][v] * out_scale};
-                *reinterpret_cast<f32x4 *>(wacc + 64 * g4 + 4 * v) = wv;
-            }
-        if (grp == 0)
-            *reinterpret_cast<float2 *>(p.ws_ml + 2 * idx) = make_float2(m, lt);
     };
 
     if constexpr (kPrefill) {
@@ -803,23 +852,25 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
         // attends to the tokens before it; xpshop.cn article 312 s6: long
         // prompts go in chunks).  Sequence b's chunk is the last nq of its
         // ctx tokens (their K/V already written); chunk token i sits at
-        // position ctx - nq + i.  One wavefront takes (b, KV head h, group gi
-        // of qpc consecutive chunk tokens): MFMA column col is chunk token
-        // gi * qpc + col / r with query head h * r + col % r, so one pass
-        // over the tiles serves qpc tokens x r heads.  Groups are numbered
-        // so that the later (longer) ones start first.
+        // position ctx - nq + i.  Chunk tokens form groups of qpc = 16 / r;
+        // in group gi, MFMA column col is chunk token gi * qpc + col / r with
+        // query head h * r + col % r, so one MFMA column group serves qpc
+        // tokens x r heads.  A wavefront takes (b, KV head h) and NQ
+        // consecutive groups; the later (longer) ones start first.
         // Order for L2 reuse: every group of a (sequence, KV head) pair
         // reads the same K/V, so the pairs are spread over the XCDs and each
         // XCD walks its pairs one after another.  Workgroups are dispatched
         // round-robin, w to XCD w % 8: XCD x takes pairs x, x + 8, x + 16,
-        // ..., all groups of one pair (longest first) before the next, so
-        // the K/V it reads at a time (one or two pairs) stays in its L2.
+        // ..., all wavefronts of one pair (longest first) before the next,
+        // so the K/V it reads at a time (one or two pairs) stays in its L2.
         // Interleaving the pairs instead gave a 50 % L2 hit rate and fetched
-        // ~135x the unique K/V bytes from beyond L2.
+        // ~135x the unique K/V bytes from beyond L2.  A wavefront takes NQ
+        // consecutive groups, which share every tile it loads.
         const int BH = p.B * p.Hkv;
-        const int sl = w >> 3;               // slot in XCD (w % 8)'s sequence
-        const int pair = (w & 7) + 8 * (sl / p.groups);
-        const int gi = p.groups - 1 - sl % p.groups;
+        const int nw = (p.groups + NQ - 1) / NQ;  // wavefronts per pair
+        const int sl = w >> 3;                    // slot in XCD (w % 8)'s sequence
+        const int pair = (w & 7) + 8 * (sl / nw);
+        const int gw = nw - 1 - sl % nw;
         if (pair >= BH)
             return;
         const int b = pair / p.Hkv;
@@ -827,21 +878,25 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
         const int ctx = min(max(p.context_lens[b], 0), p.max_ctx);
         const int qs = p.q_start[b];
         const int nq = min(p.q_start[b + 1] - qs, ctx);
-        const int i0 = gi * p.qpc;
+        const int i0 = gw * NQ * p.qpc;           // first chunk token of the wavefront
         if (i0 >= nq)
             return;
-        const int c0 = ctx - nq;                       // cached before the chunk
-        const int i_end = min(i0 + p.qpc, nq);
-        const int ic = i0 + col / p.r, jc = col % p.r;
-        const bool active = col < p.qpc * p.r && ic < i_end;
-        const int tl = c0 + i_end;                     // tokens this group reads
+        const int c0 = ctx - nq;                  // cached before the chunk
+        const int tl = c0 + min(i0 + NQ * p.qpc, nq);  // tokens this wavefront reads
         const int n = (tl + 15) >> 4;
         const int gh = model_head(p, h);
-        const f16 *qrow = p.q + ((int64_t)(qs + (active ? ic : i0)) * p.Hq + gh * p.r +
-                                 (active ? jc : 0)) * D;
-        f16 *orow = p.out + ((int64_t)(qs + (active ? ic : i0)) * p.Hq + gh * p.r +
-                             (active ? jc : 0)) * D;
-        attend(b, h, tl, n, 0, n, qrow, active, active ? c0 + ic + 1 : tl, orow);
+        const int jc = col % p.r;
+        Cols cg[NQ];
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+            const int ib = i0 + q * p.qpc;        // group q's first chunk token
+            const int ic = ib + col / p.r;
+            const bool active = col < p.qpc * p.r && ic < min(ib + p.qpc, nq);
+            const int64_t row = (int64_t)(qs + (active ? ic : i0)) * p.Hq + gh * p.r +
+                                (active ? jc : 0);
+            cg[q] = Cols{p.q + row * D, p.out + row * D, active ? c0 + ic + 1 : tl, active};
+        }
+        attend(b, h, tl, n, 0, n, cg);
         return;
     }
 
@@ -866,7 +921,8 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
         const int gh = model_head(p, h);
         const int64_t row = (int64_t)b * p.Hq + gh * p.r + (head_ok ? col : 0);
         run_after = rec.g1 - g - (t1 - t0);
-        attend(b, h, ctx, n, t0, t1, p.q + row * D, head_ok, 1 << 30, p.out + row * D);
+        const Cols cg[NQ] = {Cols{p.q + row * D, p.out + row * D, 1 << 30, head_ok}};
+        attend(b, h, ctx, n, t0, t1, cg);
         g += t1 - t0;
     }
 }
