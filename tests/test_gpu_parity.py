@@ -274,3 +274,26 @@ def test_constant_keys_give_mean_of_values(gpu):
         mean = vq.deq[t].mean(0)                      # [Hkv][D]
         for g in range(spec.Hq):
             assert np.allclose(got[b, g], mean[g // spec.r], atol=ATOL, rtol=RTOL)
+
+
+@pytest.mark.parametrize("fmt,G", [("int8", 64), ("int4", 64), ("fp8", 128), ("fp16", 0),
+                                   ("int8", 0)])
+def test_extreme_magnitudes_stay_finite(fmt, G, gpu):
+    # K/V near the top of the fp16 range: group scales up to ~330 (INT8) or
+    # ~6000 (INT4) multiply P^T entries in fp16, and scores differ by
+    # thousands (a hard maximum); the output must still match the oracle
+    spec = W.spec("c3_gqa", fmt=fmt, G=G, B=3, Hq=8, Hkv=2, lens="fixed",
+                  lens_args=(40, 300, 700))
+    print("case", fmt, G, flush=True)
+    case = DecodeCase(spec, device=gpu, gen_device="cpu")
+    d = case.gen(0)
+    for x, f in ((d.k, 3000.0), (d.v, 12000.0)):
+        x.copy_((x.float() * f).clamp(-65000, 65000).to(torch.float16))
+    case.alloc(0)
+    case.prefill(0)
+    case.append(0)
+    _, _, _, ref = _expected(case, 0)
+    for split in (0, 64):
+        got = _host(case.decode(0, split_tokens=split)).astype(np.float64)
+        assert np.isfinite(got).all()
+        _check_out(got, ref, "%s g%d x-large split=%d" % (fmt, G, split))
