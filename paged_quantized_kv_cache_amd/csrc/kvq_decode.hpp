@@ -435,9 +435,18 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
                       const int t1, const Cols (&cg)[NQ]) {
         const int t_end = min(ctx, 16 * t1);  // token bound of this run (data)
         int t_col[NQ];                        // score bound of this lane's columns
+        int t_full = t_end;                   // below it every column takes every token
 #pragma unroll
-        for (int q = 0; q < NQ; ++q)
+        for (int q = 0; q < NQ; ++q) {
             t_col[q] = min(t_end, cg[q].tcol);
+            t_full = min(t_full, t_col[q]);
+        }
+        if constexpr (kPrefill) {
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1)
+                t_full = min(t_full, __shfl_xor(t_full, o));
+            t_full = __builtin_amdgcn_readfirstlane(t_full);
+        }
 
         // ---- query operand, in the k-step dim order of the K loads:
         //   1-byte codes: k-step s, lane group grp, element v -> dim
@@ -557,11 +566,14 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
         }
 
         // One tile of 16 tokens starting at logical token ts, data in `cur`.
-        auto process = [&](const TileData<FMT, D> &cur, const int ts) {
+        // kFull (chunked prefill): every token of the tile is below every
+        // column's bound, so no score or scale needs a mask.
+        auto process = [&](const TileData<FMT, D> &cur, const int ts, auto full_tag) {
+            constexpr bool kFull = decltype(full_tag)::value;
             // ---- this lane's scales: sk[v][j], sv[v][j] of tokens 4 grp + v
             float sk[4][NA], sv[4][NA];
             if constexpr (kGroup) {
-                const float sc = (ts + lane_tok < t_end) ? cur.sc * lane_fac : 0.0f;
+                const float sc = (kFull || ts + lane_tok < t_end) ? cur.sc * lane_fac : 0.0f;
                 static_for<0, 4 * NG>([&](auto I) {
                     constexpr int i = decltype(I)::value;
                     sk[i / NG][i % NG] = row_bcast<i>(sc);
@@ -619,7 +631,7 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
                     } else {
                         acc = sacc[q][0][v] * score_scale;
                     }
-                    z[v] = (tok0 + v < t_col[q]) ? acc : -INFINITY;
+                    z[v] = (kFull || tok0 + v < t_col[q]) ? acc : -INFINITY;
                 }
                 // ---- online softmax, with a lazy rescale: the reference m
                 // moves only when a score exceeds it by more than kSlack (base
@@ -677,7 +689,8 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
             // codes survive it; a V dword holds tokens 0..3 of the quad, one
             // byte each.
             uint32_t vmask01 = ~0u, vmask23 = ~0u, vmask8 = ~0u;
-            if constexpr (FMT == FMT_FP16) {
+            if constexpr (kFull) {
+            } else if constexpr (FMT == FMT_FP16) {
                 const int nv = t_end - tok0;  // valid tokens of this lane's quad (if < 4)
                 vmask01 = nv >= 2 ? ~0u : (nv == 1 ? 0xffffu : 0u);
                 vmask23 = nv >= 4 ? ~0u : (nv == 3 ? 0xffffu : 0u);
@@ -752,8 +765,9 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
         };
         // walk tiles [tb, te) with one cache policy; tile tb lies in window
         // wi or wi + 1
-        auto walk = [&](const int tb, const int te, auto nt_tag) {
+        auto walk = [&](const int tb, const int te, auto nt_tag, auto full_tag) {
             auto ldw = [&](TileData<FMT, D> &buf, int i) { ld(buf, min(i, te - 1), nt_tag); };
+            auto proc = [&](const TileData<FMT, D> &buf, int i) { process(buf, 16 * i, full_tag); };
             TileData<FMT, D> buf0, buf1;
             ldw(buf0, tb);
             // loop invariant: tile i lies in window wi and its data is in buf0
@@ -769,26 +783,36 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
                     win_c = load_win(wi + 2);
                 }
                 ldw(buf1, i + 1);
-                process(buf0, 16 * i);
+                proc(buf0, i);
                 ldw(buf0, i + 2);
                 if (i + 1 < te)
-                    process(buf1, 16 * (i + 1));
+                    proc(buf1, i + 1);
             }
         };
         auto has_shared = [&](int win) {
             return __builtin_amdgcn_ballot_w64((win & kSharedBlock) != 0) != 0;
         };
-        int ts = t0;  // end of the leading windows that hold shared blocks
-        if (has_shared(win_a)) {
-            ts = (wi + 1) * 64 * TPB;
-            if (has_shared(win_b))
-                ts = has_shared(win_c) ? t1 : (wi + 2) * 64 * TPB;
+        if constexpr (kPrefill) {
+            // every group of the pair reads these tiles: ordinary loads keep
+            // them in L2; the tiles below t_full need no masks
+            const int tf = min(max(t_full >> 4, t0), t1);
+            if (tf > t0)
+                walk(t0, tf, std::false_type{}, std::true_type{});
+            if (tf < t1)
+                walk(tf, t1, std::false_type{}, std::false_type{});
+        } else {
+            int ts = t0;  // end of the leading windows that hold shared blocks
+            if (has_shared(win_a)) {
+                ts = (wi + 1) * 64 * TPB;
+                if (has_shared(win_b))
+                    ts = has_shared(win_c) ? t1 : (wi + 2) * 64 * TPB;
+            }
+            ts = min(ts, t1);
+            if (ts > t0)
+                walk(t0, ts, std::false_type{}, std::false_type{});
+            if (ts < t1)
+                walk(ts, t1, std::true_type{}, std::false_type{});
         }
-        ts = min(ts, t1);
-        if (ts > t0)
-            walk(t0, ts, std::false_type{});
-        if (ts < t1)
-            walk(ts, t1, std::true_type{});
 
         // ---- epilogue: lane holds dims 64 g4 + 16 grp + (0..15) of head col
 #pragma unroll
