@@ -344,3 +344,10 @@ def test_int4_arguments(lib):
                                dummy, dummy, dummy, dummy, None) == -1
     from paged_quantized_kv_cache_amd import kvq
     assert kvq.kvq_swap_block_bytes(8, 128, 16, "int4", 64) == 2 * 8 * 16 * 64 + 2 * 8 * 16 * 2 * 4
+
+
+def test_bench_refuses_more_than_one_gpu(capsys):
+    # one GPU only: --gpus N > 1 exits with a message before touching a GPU
+    import bench
+    assert bench.main(["--gpus", "2"]) == 2
+    assert "one GPU" in capsys.readouterr().err
