@@ -720,7 +720,8 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
                 const int gi = NA == 2 ? (64 * g4) / G : 0;
 #pragma unroll
                 for (int q = 0; q < NQ; ++q)
-                    o[q][tau] = __builtin_amdgcn_mfma_f32_16x16x16f16(a, pop[q][gi], o[q][tau], 0, 0, 0);
+                    o[q][tau] =
+                        __builtin_amdgcn_mfma_f32_16x16x16f16(a, pop[q][gi], o[q][tau], 0, 0, 0);
             }
         };
 
@@ -841,7 +842,8 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
                 for (int g4 = 0; g4 < D / 64; ++g4)
 #pragma unroll
                     for (int v = 0; v < 4; ++v) {
-                        const float4 sc4 = *reinterpret_cast<const float4 *>(srow + 64 * g4 + 4 * v);
+                        const float4 sc4 =
+                            *reinterpret_cast<const float4 *>(srow + 64 * g4 + 4 * v);
                         o[q][4 * g4 + 0][v] *= sc4.x;
                         o[q][4 * g4 + 1][v] *= sc4.y;
                         o[q][4 * g4 + 2][v] *= sc4.z;
@@ -855,9 +857,11 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
                 for (int g4 = 0; g4 < D / 64; ++g4) {
                     f16x4 hv[4];
 #pragma unroll
-                    for (int v = 0; v < 4; ++v)
-                        hv[v] = f16x4{(f16)(o[q][4 * g4 + 0][v] * inv), (f16)(o[q][4 * g4 + 1][v] * inv),
-                                      (f16)(o[q][4 * g4 + 2][v] * inv), (f16)(o[q][4 * g4 + 3][v] * inv)};
+                    for (int v = 0; v < 4; ++v) {
+                        const f32x4 *t = &o[q][4 * g4];
+                        hv[v] = f16x4{(f16)(t[0][v] * inv), (f16)(t[1][v] * inv),
+                                      (f16)(t[2][v] * inv), (f16)(t[3][v] * inv)};
+                    }
 #pragma unroll
                     for (int v = 0; v < 4; ++v)
                         *reinterpret_cast<f16x4 *>(orow + 64 * g4 + 4 * v) = hv[v];
@@ -873,8 +877,9 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
             for (int g4 = 0; g4 < D / 64; ++g4)
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
-                    const f32x4 wv = {o[q][4 * g4 + 0][v] * out_scale, o[q][4 * g4 + 1][v] * out_scale,
-                                      o[q][4 * g4 + 2][v] * out_scale, o[q][4 * g4 + 3][v] * out_scale};
+                    const f32x4 *t = &o[q][4 * g4];
+                    const f32x4 wv = {t[0][v] * out_scale, t[1][v] * out_scale,
+                                      t[2][v] * out_scale, t[3][v] * out_scale};
                     *reinterpret_cast<f32x4 *>(wacc + 64 * g4 + 4 * v) = wv;
                 }
             if (grp == 0)
