@@ -104,15 +104,20 @@ kvq_status launch_status()
 
 // ---------------------------------------------------------------- run plan
 // split_tokens == 0: balanced runs, one per wavefront the GPU holds at once
-// (compute units x resident wavefronts per CU for the kernel instance, at
-// most three per SIMD), at most one run per 4 tiles of the largest possible
-// batch.  Past three waves per SIMD the loop is already fed from HBM; more
-// runs only add partial results to merge and per-run set-up (measured: a
-// fourth wave per SIMD was 1-5% slower on long-context batches).
+// (compute units x resident wavefronts per CU for the kernel instance, capped
+// at run_waves_per_cu), at most one run per 4 tiles of the largest possible
+// batch.  With the wavefront priorities, two waves per SIMD keep HBM as busy
+// as three for 1-byte and fp16 codes (and make fewer partials: measured equal
+// on C3 / C5 / fp16, 1-3 % faster on C2 / C4); INT4 tiles carry half the
+// bytes, so INT4 needs three per SIMD for the same bytes in flight (two were
+// 12 % slower).  A fourth wave per SIMD was 1-5 % slower.
 // split_tokens > 0: one run per span; the launch covers the largest
 // possible count.
 constexpr int kMaxWavesPerCU = 32;  // hardware bound used for workspace sizing
-constexpr int kRunWavesPerCU = 12;  // 3 per SIMD
+constexpr int run_waves_per_cu(int fmt)
+{
+    return fmt == FMT_INT4 ? 12 : 8;  // 3 / 2 per SIMD
+}
 
 bool valid_split(int32_t split_tokens)
 {
@@ -210,7 +215,7 @@ int waves_per_cu()
                 &n, reinterpret_cast<const void *>(&paged_decode_kernel<FMT, D, BS, NG>), 64,
                 0) != hipSuccess || n <= 0)
             n = 4;
-        v = std::min(n, kRunWavesPerCU);
+        v = std::min(n, run_waves_per_cu(FMT));
         cache[dev].store(v, std::memory_order_relaxed);
     }
     return v;
