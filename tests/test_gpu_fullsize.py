@@ -98,3 +98,15 @@ def test_full_size_prefix_sharing_mixed_precision(gpu):
     # the 32-layer workload: an fp16 first layer, INT8 middle layers and an
     # fp16 last layer, each over the shared-prefix layout with COW copies
     _run("c5_prefix_mixed", layers=(0, 1, 15, 31))
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "int8"])
+def test_single_long_sequence_split_over_every_wavefront(fmt, gpu):
+    # one 131,072-token sequence: each of its 8 units is cut into ~250
+    # pieces (more than a wavefront's 64 lanes), merged by one workgroup each
+    spec = W.spec("c4_long_bs16", fmt=fmt, G=0 if fmt == "fp8" else 64, B=1,
+                  lens="fixed", lens_args=(131072,))
+    print("case", fmt, flush=True)
+    case = DecodeCase(spec, device=gpu, poison=True)
+    case.setup_layer(0)
+    _check_layer(case, 0, [0])
