@@ -194,7 +194,8 @@ PREFILL_METRIC = ("paged INT8 GQA prefill attention prompt-tokens/s + achieved T
 MFMA_FP16_PEAK_TFLOPS = 2500.0
 
 
-def prefill_cpu_baseline(case, spec, q, chunk, min_seconds: float) -> dict:
+def prefill_cpu_baseline(case, spec, q, chunk, min_seconds: float,
+                         unit: str = "prompt-tokens/s") -> dict:
     """The oracle's chunked prefill on the first sequence of the workload,
     repeated to about ``min_seconds``."""
     import numpy as np
@@ -219,11 +220,112 @@ def prefill_cpu_baseline(case, spec, q, chunk, min_seconds: float) -> dict:
         E.prefill(qh, kq, vq, [np.arange(ids.size)], [int(chunk[0])])
         total += time.perf_counter() - t0
         passes += 1
-    return {"value": int(chunk[0]) * passes / total, "unit": "prompt-tokens/s",
+    return {"value": int(chunk[0]) * passes / total, "unit": unit,
             "cores": oracle.num_threads(), "kind": "oracle",
             "sample": "sequence 0 (%d-token chunk over %d tokens): quantize its K/V, fp64 "
                       "causal attention; %d pass(es), %.1f s"
                       % (int(chunk[0]), ids.size, passes, total)}
+
+
+SHORT_METRIC = ("paged INT8 GQA short-chunk attention chunk-tokens/s + achieved HBM GB/s "
+                "(% of MI355X peak)")
+
+
+def run_short_chunks(args, spec) -> int:
+    """Short chunks over long contexts (a few new tokens per sequence): one
+    step writes the chunks' K/V into their slots (kvq_cache_write) and runs
+    their causal attention over every cached token (kvq_paged_prefill, whose
+    short-chunk path deals the tiles over every wavefront like decode).  Bound
+    by HBM: every cached K/V byte is read once per step."""
+    import numpy as np
+    import torch
+
+    from paged_quantized_kv_cache_amd import kvq
+    from paged_quantized_kv_cache_amd import workloads as W
+    from paged_quantized_kv_cache_amd.harness import DecodeCase
+
+    kvq.lib()
+    dev = torch.device("cuda:0")
+    case = DecodeCase(spec, device=dev, poison=False)
+    case.setup_layer(0)              # every token written, the chunks' included
+    L = case.layout
+    chunk = np.minimum(case.lens, spec.chunk)
+    if chunk.max() * spec.r > 16 or L.cow_pairs.size:
+        raise SystemExit("short-chunk workloads: chunk x (Hq / Hkv) <= 16, no shared blocks")
+    slot_of = np.full(L.n_unique, -1, np.int64)
+    slot_of[L.prefill_ids] = L.prefill_slots
+    slot_of[L.append_ids] = L.append_slots
+    ids = np.concatenate([L.seq_tokens[b][len(L.seq_tokens[b]) - int(c):]
+                          for b, c in enumerate(chunk)])
+    d = case.data[0]
+    it = torch.from_numpy(ids).to(d.k.device)
+    k = d.k.index_select(0, it).to(dev).contiguous()
+    v = d.v.index_select(0, it).to(dev).contiguous()
+    slots = torch.from_numpy(slot_of[ids]).to(dev)
+    q = case.chunk_queries(chunk)
+    out = torch.empty_like(q)
+    ws = kvq.alloc_workspace(kvq.kvq_prefill_workspace_size(
+        spec.B, spec.Hq, spec.Hkv, spec.D, spec.BS, case.max_context_len,
+        int(chunk.max())), dev)
+    p = case.pools[0]
+    nchunk = int(chunk.sum())
+    # decode's algorithmic bytes with q / out for every chunk token, plus
+    # the chunk offsets
+    nbytes = (W.algorithmic_bytes(spec, case.lens, spec.fmt)
+              + 2 * (nchunk - spec.B) * spec.Hq * spec.D * 2 + 4 * (spec.B + 1))
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        kvq.kvq_cache_write(k, v, slots, p.k_pool, p.v_pool, p.k_scale, p.v_scale, p.fmt,
+                            spec.G)
+        if ev is not None:
+            ev[0].record(stream)
+        case.prefill_attention(0, chunk, q, out=out, workspace=ws)
+        if ev is not None:
+            ev[1].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(ev[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+    times = np.array([a.elapsed_time(b) for a, b in ev])
+    att_ms = float(times.mean())
+    gbps = nbytes / (att_ms * 1e-3) / 1e9
+    result = {
+        "metric": SHORT_METRIC,
+        "value": nchunk / (ms_per_step * 1e-3),
+        "unit": "chunk-tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": spec.fmt,
+        "data": "synthetic (seeded N(0,1) fp16 K/V/Q with outlier channels, shuffled "
+                "block pool)",
+        "config": {"workload": spec.name, "description": spec.description,
+                   "num_seqs": spec.B, "num_q_heads": spec.Hq, "num_kv_heads": spec.Hkv,
+                   "head_dim": spec.D, "block_size": spec.BS, "kv_format": spec.fmt,
+                   "group_size": spec.G, "chunk_tokens": nchunk,
+                   "cached_tokens": int(case.lens.sum())},
+        "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "kernel": "kvq_paged_prefill, short chunks: paged_decode_kernel + "
+                               "merge_runs_kernel (%s)" % spec.fmt,
+                     "algorithmic_bytes_per_launch": nbytes, "avg_launch_ms": round(att_ms, 5)},
+        "attention_ms_p10_p50_p90": [round(float(x), 5)
+                                     for x in np.percentile(times, [10, 50, 90])],
+        "cpu_baseline": (prefill_cpu_baseline(case, spec, q, chunk, args.cpu_min_seconds,
+                                              "chunk-tokens/s")
+                         if args.cpu_seqs > 0 else None),
+    }
+    print(json.dumps(result), flush=True)
+    return 0
 
 
 def run_mixed_heads(args, spec) -> int:
@@ -422,6 +524,8 @@ def main(argv=None) -> int:
     dev = torch.device("cuda:0")
     spec = W.spec(args.workload)
     if spec.chunk > 0:
+        if spec.chunk * spec.r <= 16:
+            return run_short_chunks(args, spec)
         return run_prefill(args, spec)
     if spec.fp16_heads:
         return run_mixed_heads(args, spec)

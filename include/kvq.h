@@ -222,9 +222,20 @@ KVQ_API kvq_status kvq_paged_decode(const void *q, const void *k_pool,
  *   query_start   int32 [num_seqs + 1] on the device, non-decreasing, with
  *                 n_b <= context_lens[b]; max_query_len >= every n_b is the
  *                 host-side bound that sizes the launch.
- *   The other arguments are those of kvq_paged_decode (no workspace: every
- *   (sequence, KV head, group of 16 / (Hq / Hkv) chunk tokens) is one
- *   wavefront that walks the tokens it needs).
+ *   workspace     device scratch of kvq_prefill_workspace_size(...) bytes
+ *                 for these arguments (its contents on entry do not matter;
+ *                 calls sharing it must be ordered).  That size is 0, and
+ *                 workspace may be NULL, unless the chunks are short:
+ *   How the work is cut:
+ *     max_query_len * (Hq / Hkv) <= 16 (short chunks, e.g. a few draft
+ *       tokens of speculative decoding over long contexts): the decode
+ *       partition -- the batch's 16-token tiles dealt in equal runs over
+ *       every wavefront the GPU holds, an MFMA column per (chunk token,
+ *       query head) of a KV head with its own causal bound, cut units merged
+ *       by log-sum-exp -- so a handful of sequences still fills the GPU;
+ *     otherwise: one wavefront per (sequence, KV head, group of
+ *       16 / (Hq / Hkv) chunk tokens) walks the tokens it needs.
+ *   The other arguments are those of kvq_paged_decode.
  */
 KVQ_API kvq_status kvq_paged_prefill(const void *q, const int32_t *query_start,
                              int32_t max_query_len, const void *k_pool,
@@ -237,7 +248,16 @@ KVQ_API kvq_status kvq_paged_prefill(const void *q, const int32_t *query_start,
                              int32_t head_dim, int32_t block_size,
                              int32_t num_blocks, int32_t dtype,
                              int32_t group_size, float softmax_scale,
-                             void *out, void *stream);
+                             void *out, void *workspace,
+                             size_t workspace_bytes, void *stream);
+
+/* Workspace bytes kvq_paged_prefill needs for these arguments on the current
+ * device: 0 unless max_query_len * (num_q_heads / num_kv_heads) <= 16.
+ * Returns SIZE_MAX for invalid arguments. */
+KVQ_API size_t kvq_prefill_workspace_size(int32_t num_seqs, int32_t num_q_heads,
+                                  int32_t num_kv_heads, int32_t head_dim,
+                                  int32_t block_size, int32_t max_context_len,
+                                  int32_t max_query_len);
 
 /*
  * Per-head mixed precision (xpshop.cn article 312, s6: the attention heads

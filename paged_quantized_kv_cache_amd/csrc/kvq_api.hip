@@ -143,17 +143,19 @@ struct WsLayout {
     size_t s_off, meta_off, rec_off, ml_off, acc_off, total;
 };
 
-bool workspace_layout(int32_t num_seqs, int32_t r, int32_t head_dim, int64_t runs, WsLayout &w)
+// cols: MFMA columns per unit (query heads per KV head, times the chunk
+// tokens of the short-chunk prefill path)
+bool workspace_layout(int32_t num_seqs, int32_t cols, int32_t head_dim, int64_t runs, WsLayout &w)
 {
-    if (num_seqs < 0 || r <= 0 || head_dim <= 0 || runs < 0)
+    if (num_seqs < 0 || cols <= 0 || head_dim <= 0 || runs < 0)
         return false;
     auto up256 = [](size_t x) { return (x + 255) / 256 * 256; };
     w.s_off = 0;
     w.meta_off = up256((size_t)(num_seqs + 1) * sizeof(int32_t));
     w.rec_off = w.meta_off + 256;
     w.ml_off = w.rec_off + up256((size_t)runs * sizeof(PlanRecord));
-    w.acc_off = w.ml_off + up256((size_t)runs * 2 * r * 2 * sizeof(float));
-    w.total = w.acc_off + up256((size_t)runs * 2 * r * head_dim * sizeof(float));
+    w.acc_off = w.ml_off + up256((size_t)runs * 2 * cols * 2 * sizeof(float));
+    w.total = w.acc_off + up256((size_t)runs * 2 * cols * head_dim * sizeof(float));
     return true;
 }
 
@@ -236,7 +238,7 @@ kvq_status launch_decode(DecodeParams p, const LaunchPlan &lp, hipStream_t s)
     if (runs > (1 << 30))
         return KVQ_ERR_UNSUPPORTED;
     WsLayout w;
-    workspace_layout(p.B, p.r, D, runs, w);
+    workspace_layout(p.B, p.cols, D, runs, w);
     if (!lp.ws || lp.ws_bytes < w.total)
         return KVQ_ERR_WORKSPACE;
     int32_t *S = reinterpret_cast<int32_t *>(lp.ws + w.s_off);
@@ -264,7 +266,7 @@ kvq_status launch_decode(DecodeParams p, const LaunchPlan &lp, hipStream_t s)
     hipLaunchKernelGGL((paged_decode_kernel<FMT, D, BS, NG>), dim3((unsigned)runs), dim3(64), 0,
                        s, p);
     if (runs > 1)
-        hipLaunchKernelGGL((merge_runs_kernel<D>), dim3((unsigned)(runs - 1), (unsigned)p.r),
+        hipLaunchKernelGGL((merge_runs_kernel<D>), dim3((unsigned)(runs - 1), (unsigned)p.cols),
                            dim3(64), 0, s, p);
     return launch_status();
 }
@@ -451,6 +453,35 @@ size_t kvq_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t 
     return w.total;
 }
 
+// Short chunks (at most 16 / r tokens each) are walked by the decode
+// partition: its runs and merge cover every wavefront however few
+// sequences and chunk tokens there are.  Longer chunks take the prefill
+// kernel (one wavefront per sequence, KV head and group of chunk tokens).
+static bool short_chunks(int32_t num_q_heads, int32_t num_kv_heads, int32_t max_query_len)
+{
+    return max_query_len >= 1 && (int64_t)max_query_len * (num_q_heads / num_kv_heads) <= 16;
+}
+
+size_t kvq_prefill_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                  int32_t head_dim, int32_t block_size,
+                                  int32_t max_context_len, int32_t max_query_len)
+{
+    (void)block_size;
+    if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
+        num_q_heads % num_kv_heads != 0 || head_dim <= 0 || max_query_len < 0 ||
+        max_context_len < max_query_len)
+        return SIZE_MAX;
+    if (!short_chunks(num_q_heads, num_kv_heads, max_query_len))
+        return 0;
+    const int64_t balanced = (int64_t)device_cus() * kMaxWavesPerCU;
+    const int64_t runs = runs_bound(num_seqs, num_kv_heads, max_context_len, 0, balanced);
+    WsLayout w;
+    if (!workspace_layout(num_seqs, max_query_len * (num_q_heads / num_kv_heads), head_dim,
+                          runs, w))
+        return SIZE_MAX;
+    return w.total;
+}
+
 // num_q_heads / num_kv_heads: the model's heads (q and out rows, GQA ratio);
 // head_ids: the pool's heads as model KV heads (null: the pool holds all
 // num_kv_heads); pool_heads: heads in the pool.
@@ -516,6 +547,7 @@ static kvq_status decode_impl(const void *q, const void *k_pool, const void *v_p
     p.Hq = num_q_heads;
     p.Hkv = pool_heads;
     p.r = r;
+    p.cols = r;
     p.head_ids = head_ids;
     const float sm = softmax_scale > 0.0f ? softmax_scale : 1.0f / std::sqrt((float)head_dim);
     p.score_scale = sm * 1.4426950408889634f;  // log2(e): softmax in base 2
@@ -572,7 +604,8 @@ kvq_status kvq_paged_prefill(const void *q, const int32_t *query_start, int32_t 
                              int32_t max_context_len, int32_t num_seqs, int32_t num_q_heads,
                              int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                              int32_t num_blocks, int32_t dtype, int32_t group_size,
-                             float softmax_scale, void *out, void *stream)
+                             float softmax_scale, void *out, void *workspace,
+                             size_t workspace_bytes, void *stream)
 {
     kvq_status st = check_format(dtype, head_dim, block_size, group_size);
     if (st != KVQ_OK)
@@ -597,8 +630,14 @@ kvq_status kvq_paged_prefill(const void *q, const int32_t *query_start, int32_t 
     if (dtype != KVQ_FP16 && (!k_scale || !v_scale))
         return KVQ_ERR_INVALID_ARG;
     if (!aligned16(q) || !aligned16(out) || !aligned16(k_pool) || !aligned16(v_pool) ||
-        (k_scale && !aligned16(k_scale)) || (v_scale && !aligned16(v_scale)))
+        (k_scale && !aligned16(k_scale)) || (v_scale && !aligned16(v_scale)) ||
+        (workspace && !aligned16(workspace)))
         return KVQ_ERR_INVALID_ARG;
+    const bool split = short_chunks(num_q_heads, num_kv_heads, max_query_len);
+    if (split && max_tiles(num_seqs, num_kv_heads, max_context_len) >= (int64_t)1 << 30)
+        return KVQ_ERR_UNSUPPORTED;
+    if (split && !workspace)
+        return KVQ_ERR_WORKSPACE;
     st = check_device();
     if (st != KVQ_OK)
         return st;
@@ -624,6 +663,17 @@ kvq_status kvq_paged_prefill(const void *q, const int32_t *query_start, int32_t 
     p.q_start = query_start;
     p.qpc = 16 / r;
     p.groups = (max_query_len + p.qpc - 1) / p.qpc;
+    if (split) {  // the decode partition, columns = (chunk token, query head)
+        p.cols = max_query_len * r;
+        LaunchPlan lp;
+        lp.split_tokens = 0;
+        lp.max_ctx = max_context_len;
+        lp.ws_bytes = workspace_bytes;
+        lp.ws = static_cast<uint8_t *>(workspace);
+        return dispatch_attention(p, &lp, dtype, head_dim, block_size, group_size,
+                                  static_cast<hipStream_t>(stream));
+    }
+    p.cols = r;
     return dispatch_attention(p, nullptr, dtype, head_dim, block_size, group_size,
                               static_cast<hipStream_t>(stream));
 }

@@ -62,6 +62,11 @@ constexpr int kBlockIdMask = 0x3fffffff;
 // Buffer descriptor word 3 for raw (untyped) buffer loads on gfx9-class GPUs.
 constexpr int kBufferConfig = 0x00020000;
 constexpr int kSharedBlock = 0x40000000;
+// Initial running maximum of the online softmax: finite, so that a column
+// whose tokens in a piece are all masked (a short chunk's causal bound) gets
+// P = 2^(-inf - kNoMax) = 0 rather than NaN, and its partial (m = kNoMax,
+// l = 0, acc = 0) weighs 0 in the merge.
+constexpr float kNoMax = -3.0e38f;
 
 struct PlanRecord {
     int32_t b;     // sequence holding tile g0
@@ -96,14 +101,16 @@ struct DecodeParams {
     int32_t Hq;
     int32_t Hkv;
     int32_t r;
+    int32_t cols;        // MFMA columns per unit (partials, merge): r, or chunk x r
     int32_t W;           // wavefronts launched
     float score_scale;   // softmax_scale * log2(e)
     // KV-head subset (per-head mixed precision): the pool's head h is KV
     // head head_ids[h] of the model; q / out rows have Hq query heads, of
     // which KV head g serves g * r .. g * r + r - 1.  Null: the identity.
     const int32_t *head_ids;
-    // chunked prefill only
-    const int32_t *q_start;  // [B + 1] chunk offsets in q / out
+    // chunks: [B + 1] offsets in q / out (chunked prefill, and short chunks
+    // walked by the decode partition); null for decode
+    const int32_t *q_start;
     int32_t qpc;             // chunk tokens per wavefront (16 / r)
     int32_t groups;          // ceil(max chunk length / qpc)
 };
@@ -558,7 +565,7 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
 #pragma unroll
             for (int i = 0; i < DT; ++i)
                 o[q][i] = f32x4{0.f, 0.f, 0.f, 0.f};
-            m[q] = -INFINITY;
+            m[q] = kNoMax;
             l[q] = 0.0f;
 #pragma unroll
             for (int j = 0; j < NA; ++j)
@@ -871,7 +878,7 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
             // a piece of a unit: slot 0 if it continues a unit, slot 1 if it
             // starts one (decode only: one column group)
             const int slot = t0 > 0 ? 0 : 1;
-            const int64_t idx = ((int64_t)w * 2 + slot) * p.r + col;
+            const int64_t idx = ((int64_t)w * 2 + slot) * p.cols + col;
             float *wacc = p.ws_acc + idx * D + 16 * grp;
 #pragma unroll
             for (int g4 = 0; g4 < D / 64; ++g4)
@@ -940,8 +947,12 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
         return;
     }
 
-    // ---- decode: walk the run [g0, g1) unit by unit (values wave-uniform)
-    const bool head_ok = col < p.r;
+    // ---- decode: walk the run [g0, g1) unit by unit (values wave-uniform).
+    // Column col is query head col of the unit's KV head; with short chunks
+    // (q_start set: every chunk at most cols / r tokens, chunk token i at
+    // position ctx - nq + i) it is chunk token col / r, query head col % r,
+    // and it takes the tokens at or before its position.
+    const int ci = col / p.r, cj = col % p.r;
     int b = rec.b;
     int g = rec.g0;
     int n = ctx_tiles(p.context_lens, b, p.max_ctx);
@@ -959,10 +970,19 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
         const int t1 = min(n, t0 + (rec.g1 - g));
         const int ctx = min(p.context_lens[b], p.max_ctx);
         const int gh = model_head(p, h);
-        const int64_t row = (int64_t)b * p.Hq + gh * p.r + (head_ok ? col : 0);
+        int qs = b, nq = 1, tcol = 1 << 30;
+        if (p.q_start) {
+            qs = p.q_start[b];
+            nq = min(p.q_start[b + 1] - qs, max(ctx, 0));
+            tcol = ctx - nq + ci + 1;
+        }
         run_after = rec.g1 - g - (t1 - t0);
-        const Cols cg[NQ] = {Cols{p.q + row * D, p.out + row * D, 1 << 30, head_ok}};
-        attend(b, h, ctx, n, t0, t1, cg);
+        if (nq > 0) {  // (an empty chunk has nothing to attend)
+            const bool act = col < p.cols && ci < nq;
+            const int64_t row = (int64_t)(qs + (act ? ci : 0)) * p.Hq + gh * p.r + (act ? cj : 0);
+            const Cols cg[NQ] = {Cols{p.q + row * D, p.out + row * D, tcol, act}};
+            attend(b, h, ctx, n, t0, t1, cg);
+        }
         g += t1 - t0;
     }
 }
@@ -998,7 +1018,7 @@ __global__ __launch_bounds__(64) void merge_runs_kernel(DecodeParams p)
     const int lane = threadIdx.x;
     // pieces: j = 0 is run k-1 (slot 1), j >= 1 is run k-1+j (slot 0)
     auto piece = [&](int j) -> int64_t {
-        return ((int64_t)(k - 1 + j) * 2 + (j == 0 ? 1 : 0)) * p.r + col;
+        return ((int64_t)(k - 1 + j) * 2 + (j == 0 ? 1 : 0)) * p.cols + col;
     };
     // number of pieces: runs k-1 .. kl with g0 < ue
     int np = 1;
@@ -1033,7 +1053,15 @@ __global__ __launch_bounds__(64) void merge_runs_kernel(DecodeParams p)
             acc[i] += a[i] * wgt;
     }
     const float inv = 1.0f / ls;
-    f16 *orow = p.out + ((int64_t)b * p.Hq + model_head(p, h) * p.r + col) * D + PER * lane;
+    int64_t row = (int64_t)b * p.Hq + model_head(p, h) * p.r + col;
+    if (p.q_start) {  // short chunks: column col is chunk token col / r, head col % r
+        const int qs = p.q_start[b];
+        const int nq = min(p.q_start[b + 1] - qs, min(max(p.context_lens[b], 0), p.max_ctx));
+        if (col / p.r >= nq)
+            return;
+        row = (int64_t)(qs + col / p.r) * p.Hq + model_head(p, h) * p.r + col % p.r;
+    }
+    f16 *orow = p.out + row * D + PER * lane;
 #pragma unroll
     for (int i = 0; i < PER; ++i)
         orow[i] = (f16)(acc[i] * inv);

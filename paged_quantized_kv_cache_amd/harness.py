@@ -164,7 +164,7 @@ class DecodeCase:
         return q.to(torch.float16).to(self.device)
 
     def prefill_attention(self, layer: int, chunk_lens, q: torch.Tensor,
-                          out=None) -> torch.Tensor:
+                          out=None, workspace=None) -> torch.Tensor:
         """Chunked prefill: sequence b's last chunk_lens[b] tokens attend
         causally (their K/V are already in the pool)."""
         p, s = self.pools[layer], self.spec
@@ -175,7 +175,8 @@ class DecodeCase:
         return kvq.kvq_paged_prefill(q, query_start, int(n.max()) if n.size else 0,
                                      p.k_pool, p.v_pool, p.k_scale, p.v_scale,
                                      self.block_tables, self.context_lens,
-                                     self.max_context_len, p.fmt, s.G, out=out)
+                                     self.max_context_len, p.fmt, s.G, out=out,
+                                     workspace=workspace)
 
     # ------------------------------------------------------------ readback
     def gather_codes(self, layer: int, seqs=None):

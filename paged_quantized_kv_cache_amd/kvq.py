@@ -48,7 +48,7 @@ STATUS = {0: "KVQ_OK", -1: "KVQ_ERR_INVALID_ARG", -2: "KVQ_ERR_UNSUPPORTED",
 EXPORTS = ("kvq_status_string", "kvq_version", "kvq_cache_write",
            "kvq_paged_decode", "kvq_decode_workspace_size", "kvq_copy_blocks",
            "kvq_swap_block_bytes", "kvq_swap_out", "kvq_swap_in", "kvq_paged_prefill",
-           "kvq_cache_write_heads", "kvq_paged_decode_heads")
+           "kvq_prefill_workspace_size", "kvq_cache_write_heads", "kvq_paged_decode_heads")
 
 
 class KvqError(RuntimeError):
@@ -96,7 +96,9 @@ def lib() -> ctypes.CDLL:
             L.kvq_paged_prefill.restype = i32
             L.kvq_paged_prefill.argtypes = [P, P, i32, P, P, P, P, P, i32, P, i32, i32,
                                             i32, i32, i32, i32, i32, i32, i32,
-                                            ctypes.c_float, P, P]
+                                            ctypes.c_float, P, P, ctypes.c_size_t, P]
+            L.kvq_prefill_workspace_size.restype = ctypes.c_size_t
+            L.kvq_prefill_workspace_size.argtypes = [i32] * 7
             L.kvq_decode_workspace_size.restype = ctypes.c_size_t
             L.kvq_decode_workspace_size.argtypes = [i32] * 7
             L.kvq_copy_blocks.restype = i32
@@ -208,6 +210,16 @@ def kvq_decode_workspace_size(num_seqs: int, num_q_heads: int, num_kv_heads: int
     n = int(lib().kvq_decode_workspace_size(num_seqs, num_q_heads, num_kv_heads,
                                             head_dim, block_size, max_context_len,
                                             split_tokens))
+    if n == ctypes.c_size_t(-1).value:
+        raise ValueError("invalid workspace arguments")
+    return n
+
+
+def kvq_prefill_workspace_size(num_seqs: int, num_q_heads: int, num_kv_heads: int,
+                               head_dim: int, block_size: int, max_context_len: int,
+                               max_query_len: int) -> int:
+    n = int(lib().kvq_prefill_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                             block_size, max_context_len, max_query_len))
     if n == ctypes.c_size_t(-1).value:
         raise ValueError("invalid workspace arguments")
     return n
@@ -328,10 +340,12 @@ def kvq_paged_prefill(q: torch.Tensor, query_start: torch.Tensor, max_query_len:
                       block_tables: torch.Tensor, context_lens: torch.Tensor,
                       max_context_len: int, fmt: str, group_size: int = 0,
                       softmax_scale: float = 0.0, out: Optional[torch.Tensor] = None,
+                      workspace: Optional[torch.Tensor] = None,
                       stream=None) -> torch.Tensor:
     """Causal attention of each sequence's chunk (its last n_b tokens, already
     in the pool) over its cached tokens.  q: fp16 [sum n][Hq][D];
-    query_start: int32 [B + 1] on the device."""
+    query_start: int32 [B + 1] on the device.  ``workspace`` (allocated here
+    when None) is only used for short chunks (see kvq.h)."""
     num_blocks, hkv, bs, d = _pool_geometry(k_pool, fmt)
     T, hq, dq = q.shape
     B = context_lens.numel()
@@ -341,12 +355,16 @@ def kvq_paged_prefill(q: torch.Tensor, query_start: torch.Tensor, max_query_len:
         raise ValueError("query_start must be int32 [B + 1]")
     if out is None:
         out = torch.empty_like(q)
+    if workspace is None and B > 0 and max_query_len > 0:
+        workspace = alloc_workspace(kvq_prefill_workspace_size(
+            B, hq, hkv, d, bs, max_context_len, max_query_len), q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib().kvq_paged_prefill(_ptr(q), _ptr(query_start), max_query_len, _ptr(k_pool),
                                  _ptr(v_pool), _ptr(k_scale), _ptr(v_scale),
                                  _ptr(block_tables), block_tables.shape[1],
                                  _ptr(context_lens), max_context_len, B, hq, hkv, d, bs,
                                  num_blocks, _fmt(fmt), group_size, softmax_scale, _ptr(out),
-                                 _stream(stream))
+                                 _ptr(workspace), ws_bytes, _stream(stream))
     _check(st, "kvq_paged_prefill")
     return out
 

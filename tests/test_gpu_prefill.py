@@ -3,9 +3,12 @@
 
 Each sequence's chunk is its last n_b tokens (already written by
 kvq_cache_write); chunk token i attends to every token up to its position.
-Chunks: whole prompts, a fixed-size tail chunk after cached tokens, and one
-token (where prefill must agree with decode).  Tolerance as for decode:
-|gpu - oracle| <= 2e-3 + 1e-3 |oracle|.
+Chunks: whole prompts, a fixed-size tail chunk after cached tokens, one
+token (where prefill must agree with decode), and short ragged chunks of at
+most 16 / (Hq / Hkv) tokens (empty ones included), which are walked by the
+decode partition: runs over every wavefront, one MFMA column per (chunk
+token, query head) with its own causal bound, cut units merged.  Tolerance
+as for decode: |gpu - oracle| <= 2e-3 + 1e-3 |oracle|.
 """
 import numpy as np
 import pytest
@@ -43,22 +46,26 @@ def _quantized(case, layer, seqs):
     return kq, vq, toks
 
 
-def _chunks(lens, mode):
+def _chunks(lens, mode, r=1):
     if mode == "whole":
         return lens.copy()
     if mode == "tail":
         return np.minimum(lens, 37)
+    if mode == "short":  # at most 16 / r tokens, ragged, one empty chunk
+        qpc = 16 // r
+        pat = [qpc, 1, max(qpc - 1, 1), 0, min(2, qpc)]
+        return np.minimum(lens, [pat[b % len(pat)] for b in range(lens.size)])
     return np.ones_like(lens)
 
 
-@pytest.mark.parametrize("mode", ["whole", "tail", "one"])
+@pytest.mark.parametrize("mode", ["whole", "tail", "one", "short"])
 @pytest.mark.parametrize("name", CASES)
 def test_prefill_within_tolerance(name, mode, gpu):
     print("case", name, mode, flush=True)
     spec = SMALL_CASES[name]
     case = DecodeCase(spec, device=gpu, gen_device="cpu")
     case.setup_layer(0)
-    n = _chunks(case.lens, mode)
+    n = _chunks(case.lens, mode, spec.Hq // spec.Hkv)
     q = case.chunk_queries(n)
     got = case.prefill_attention(0, n, q).float().cpu().numpy()
     assert np.isfinite(got).all()
@@ -106,3 +113,32 @@ def test_full_size_prefill_sampled_rows(gpu):
     ref = E.attention(np.stack(qrows), kq, vq, ctx)
     ok, mabs, mrel, excess = E.tolerance_ok(got[rows], ref, ATOL, RTOL)
     assert ok, "max_abs %.3g max_rel %.3g excess %.3g" % (mabs, mrel, excess)
+
+
+@pytest.mark.parametrize("name", ["c3_gqa", "c3_gqa_fp16"])
+def test_short_chunks_long_context(name, gpu):
+    """A few new tokens per sequence (e.g. draft tokens to verify) over long
+    cached contexts: every unit is cut into many pieces.  Lengths one or two
+    past a block boundary leave last tiles whose tokens all lie beyond the
+    first chunk tokens' causal bounds, so some pieces hold columns with no
+    token to attend (they must weigh nothing in the merge)."""
+    lens = (16 * 600 + 1, 16 * 900 + 2, 4097, 16 * 1200 + 1, 5000, 16 * 800 + 2)
+    spec = W.spec(name, B=len(lens), lens="fixed", lens_args=lens)
+    print("workload", spec.name, lens, flush=True)
+    case = DecodeCase(spec, device=gpu, gen_device="cpu")
+    case.setup_layer(0)
+    n = np.array([4, 3, 4, 1, 4, 2])
+    assert kvq.kvq_prefill_workspace_size(spec.B, spec.Hq, spec.Hkv, spec.D, spec.BS,
+                                          case.max_context_len, int(n.max())) > 0
+    q = case.chunk_queries(n)
+    got = case.prefill_attention(0, n, q).float().cpu().numpy()
+    assert np.isfinite(got).all()
+    kq, vq, toks = _quantized(case, 0, range(spec.B))
+    ref = E.prefill(q.cpu().numpy(), kq, vq, toks, n)
+    ok, mabs, mrel, excess = E.tolerance_ok(got, ref, ATOL, RTOL)
+    assert ok, "max_abs %.3g max_rel %.3g excess %.3g" % (mabs, mrel, excess)
+    # the last chunk token of each sequence is its decode row
+    last = np.cumsum(n) - 1
+    qd = q[torch.from_numpy(last).to(q.device)].contiguous()
+    dec = case.decode(0, q=qd).float().cpu().numpy()
+    assert np.all(np.abs(dec - got[last]) <= 2 * (ATOL + RTOL * np.abs(ref[last])))
