@@ -264,6 +264,7 @@ def run_short_chunks(args, spec) -> int:
     slots = torch.from_numpy(slot_of[ids]).to(dev)
     q = case.chunk_queries(chunk)
     out = torch.empty_like(q)
+    qstart = case.query_start(chunk)
     ws = kvq.alloc_workspace(kvq.kvq_prefill_workspace_size(
         spec.B, spec.Hq, spec.Hkv, spec.D, spec.BS, case.max_context_len,
         int(chunk.max())), dev)
@@ -280,7 +281,7 @@ def run_short_chunks(args, spec) -> int:
                             spec.G)
         if ev is not None:
             ev[0].record(stream)
-        case.prefill_attention(0, chunk, q, out=out, workspace=ws)
+        case.prefill_attention(0, chunk, q, out=out, workspace=ws, query_start=qstart)
         if ev is not None:
             ev[1].record(stream)
 
@@ -440,6 +441,7 @@ def run_prefill(args, spec) -> int:
         raise SystemExit("prefill workloads here write whole prompts (chunk >= every length)")
     q = case.chunk_queries(chunk)
     out = torch.empty_like(q)
+    qstart = case.query_start(chunk)
     flops = W.prefill_flops(spec, case.lens, chunk)
     stream = torch.cuda.current_stream()
 
@@ -448,7 +450,7 @@ def run_prefill(args, spec) -> int:
         case.append(0)
         if ev is not None:
             ev[0].record(stream)
-        case.prefill_attention(0, chunk, q, out=out)
+        case.prefill_attention(0, chunk, q, out=out, query_start=qstart)
         if ev is not None:
             ev[1].record(stream)
 

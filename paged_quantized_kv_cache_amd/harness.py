@@ -163,15 +163,22 @@ class DecodeCase:
         q = torch.randn((n, s.Hq, s.D), generator=g, dtype=torch.float32)
         return q.to(torch.float16).to(self.device)
 
-    def prefill_attention(self, layer: int, chunk_lens, q: torch.Tensor,
-                          out=None, workspace=None) -> torch.Tensor:
-        """Chunked prefill: sequence b's last chunk_lens[b] tokens attend
-        causally (their K/V are already in the pool)."""
-        p, s = self.pools[layer], self.spec
+    def query_start(self, chunk_lens) -> torch.Tensor:
+        """Chunk offsets ``int32 [B + 1]`` on the device."""
         n = np.asarray(chunk_lens, np.int64)
         qs = np.zeros(n.size + 1, np.int32)
         qs[1:] = np.cumsum(n)
-        query_start = torch.from_numpy(qs).to(self.device)
+        return torch.from_numpy(qs).to(self.device)
+
+    def prefill_attention(self, layer: int, chunk_lens, q: torch.Tensor,
+                          out=None, workspace=None, query_start=None) -> torch.Tensor:
+        """Chunked prefill: sequence b's last chunk_lens[b] tokens attend
+        causally (their K/V are already in the pool).  ``query_start``: the
+        offsets from query_start(chunk_lens), made here when None."""
+        p, s = self.pools[layer], self.spec
+        n = np.asarray(chunk_lens, np.int64)
+        if query_start is None:
+            query_start = self.query_start(n)
         return kvq.kvq_paged_prefill(q, query_start, int(n.max()) if n.size else 0,
                                      p.k_pool, p.v_pool, p.k_scale, p.v_scale,
                                      self.block_tables, self.context_lens,
