@@ -161,6 +161,40 @@ def test_workspace_size(lib):
         kvq.kvq_decode_workspace_size(2, 6, 4, 64, 16, 100)
 
 
+def test_prefill_workspace_size(lib):
+    from paged_quantized_kv_cache_amd import kvq
+    # short chunks (chunk x Hq/Hkv <= 16) take the decode partition: partial
+    # slots of chunk x r columns per run
+    r4 = kvq.kvq_prefill_workspace_size(16, 32, 8, 128, 16, 32768, 4)
+    assert r4 > 0
+    assert r4 > kvq.kvq_prefill_workspace_size(16, 32, 8, 128, 16, 32768, 1)
+    assert kvq.kvq_prefill_workspace_size(16, 32, 8, 128, 16, 32768, 1) == \
+        kvq.kvq_decode_workspace_size(16, 32, 8, 128, 16, 32768)
+    # longer chunks walk per (sequence, KV head, group): no workspace
+    assert kvq.kvq_prefill_workspace_size(16, 32, 8, 128, 16, 32768, 5) == 0
+    assert kvq.kvq_prefill_workspace_size(4, 8, 8, 64, 16, 100, 17) == 0
+    assert kvq.kvq_prefill_workspace_size(4, 8, 8, 64, 16, 100, 16) > 0
+    assert kvq.kvq_prefill_workspace_size(4, 8, 8, 64, 16, 100, 0) == 0
+    with pytest.raises(ValueError):
+        kvq.kvq_prefill_workspace_size(4, 8, 8, 64, 16, 10, 11)   # chunk > context bound
+    with pytest.raises(ValueError):
+        kvq.kvq_prefill_workspace_size(4, 6, 4, 64, 16, 100, 2)   # Hq % Hkv != 0
+
+
+def test_prefill_arguments_rejected_before_any_device_work(lib):
+    dummy = ctypes.c_void_p(16)
+
+    def pre(mq=4, ws=None, mcl=60, Hq=8, Hkv=2, D=64):
+        return lib.kvq_paged_prefill(dummy, dummy, mq, dummy, dummy, dummy, dummy, dummy, 4,
+                                     dummy, mcl, 2, Hq, Hkv, D, 16, 8, 1, 64, 0.0, dummy,
+                                     ws, 0, None)
+    assert pre(mq=4) == -3                       # short chunks need a workspace
+    assert pre(mq=0) == 0                        # nothing to do
+    assert pre(mq=61) == -1                      # chunk longer than the context bound
+    assert pre(Hq=6, Hkv=4) == -1
+    assert pre(D=96) == -2
+
+
 def test_bad_arguments_rejected_before_any_device_work(lib):
     P = ctypes.c_void_p
     dummy = P(16)
