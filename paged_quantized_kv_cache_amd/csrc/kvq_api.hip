@@ -266,8 +266,9 @@ kvq_status launch_decode(DecodeParams p, const LaunchPlan &lp, hipStream_t s)
     hipLaunchKernelGGL((paged_decode_kernel<FMT, D, BS, NG>), dim3((unsigned)runs), dim3(64), 0,
                        s, p);
     if (runs > 1)
-        hipLaunchKernelGGL((merge_runs_kernel<D>), dim3((unsigned)(runs - 1), (unsigned)p.cols),
-                           dim3(64), 0, s, p);
+        hipLaunchKernelGGL((merge_runs_kernel<D>),
+                           dim3((unsigned)(runs - 1), (unsigned)((p.cols + kMergeCols - 1) / kMergeCols)),
+                           dim3(64 * std::min(p.cols, kMergeCols)), 0, s, p);
     return launch_status();
 }
 

@@ -73,6 +73,9 @@ struct PlanRecord {
     int32_t g0;    // first tile of the run
     int32_t g1;    // one past the last tile
     int32_t base;  // first tile of sequence b (Hkv * tiles before b)
+    int32_t us;    // first tile of the unit holding g0
+    int32_t ue;    // one past its last tile
+    int32_t pad[2];
 };
 
 // Batches of at most 64 * kInlineSeqs sequences are planned inside the
@@ -223,7 +226,8 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanParams p)
                 for (int k = 0; k < m; ++k) {
                     const int g0 = lo + h * n + k * p.span_tiles;
                     p.rec[p.Hkv * off_i + h * m + k] =
-                        PlanRecord{b, g0, min(lo + (h + 1) * n, g0 + p.span_tiles), lo};
+                        PlanRecord{b, g0, min(lo + (h + 1) * n, g0 + p.span_tiles), lo,
+                                   lo + h * n, lo + (h + 1) * n, {0, 0}};
                 }
             off_i += m;
         }
@@ -253,7 +257,10 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanParams p)
             else
                 hi = mid - 1;
         }
-        p.rec[w] = PlanRecord{lo, g0, g1, p.Hkv * S[lo]};
+        const int base = p.Hkv * S[lo];
+        const int n = S[lo + 1] - S[lo];  // > 0: tile g0 lies in sequence lo
+        const int us = base + (g0 - base) / n * n;
+        p.rec[w] = PlanRecord{lo, g0, g1, base, us, us + n, {0, 0}};
     }
 }
 
@@ -410,18 +417,22 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
                 return;
             const int g0 = (int)((int64_t)w * T / W);
             const int g1 = (int)((int64_t)(w + 1) * T / W);
-            int s0 = incl - sum, found = -1, fbase = 0;
+            int s0 = incl - sum, found = -1, fbase = 0, fn = 1;
     #pragma unroll
             for (int j = 0; j < kInlineSeqs; ++j) {
                 if (p.Hkv * s0 <= g0 && g0 < p.Hkv * (s0 + tl[j])) {
                     found = lane * per + j;
                     fbase = p.Hkv * s0;
+                    fn = tl[j];
                 }
                 s0 += tl[j];
             }
             const int src = __builtin_ctzll(__builtin_amdgcn_ballot_w64(found >= 0));
-            rec = PlanRecord{__builtin_amdgcn_readlane(found, src), g0, g1,
-                             __builtin_amdgcn_readlane(fbase, src)};
+            const int base = __builtin_amdgcn_readlane(fbase, src);
+            const int n0 = __builtin_amdgcn_readlane(fn, src);
+            const int us = base + (g0 - base) / n0 * n0;
+            rec = PlanRecord{__builtin_amdgcn_readlane(found, src), g0, g1, base, us, us + n0,
+                             {0, 0}};
             if (lane == 0)
                 p.plan_rec[w] = rec;  // for the merge launch
         } else {
@@ -989,46 +1000,82 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
 
 // Log-sum-exp merge of the pieces of a unit cut by run boundaries:
 //   M = max_i m_i,  L = sum_i l_i 2^(m_i - M),  out = sum_i acc_i 2^(m_i - M) / L.
-// Workgroup (k, head) looks at the boundary between runs k-1 and k; it merges
-// that query head of the unit holding tile g0(k) when that boundary is the
-// unit's first one.  The pieces are run k-1's slot 1 (the unit's start) and
-// slot 0 of runs k, k+1, ... up to the unit's end.  It runs as its own
+// Workgroup (k, y) looks at the boundary between runs k-1 and k; when that
+// boundary is the first one of the unit holding tile g0(k), its wavefront c
+// merges column kMergeCols * y + c of that unit (up to kMergeCols wavefronts
+// per workgroup: one per column was 20 % slower on C3, sixteen per workgroup
+// made the 16-column merge of short chunks 2.6x slower).  The pieces are run k-1's slot 1 (the unit's start)
+// and slot 0 of runs k, k+1, ... up to the unit's end.  It runs as its own
 // launch, so the partials written by wavefronts on any XCD are visible
-// without device-wide fences.
+// without device-wide fences.  Loads go in two rounds: the run records
+// (each carries its unit's bounds), then every piece's (m, l) together with
+// the first pieces' partial outputs.
+constexpr int kMergeCols = 4;
+
 template <int D>
-__global__ __launch_bounds__(64) void merge_runs_kernel(DecodeParams p)
+__global__ __launch_bounds__(64 * kMergeCols) void merge_runs_kernel(DecodeParams p)
 {
+    constexpr int PER = D / 64;   // output dims per lane
+    constexpr int kAhead = 8;     // pieces whose partials load with (m, l)
     const int k = blockIdx.x + 1;
-    const int col = blockIdx.y;
+    const int col = kMergeCols * blockIdx.y + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (col >= p.cols)
+        return;
+    // round 1: the runs in use, and the records of runs k - 1 .. k + 62
+    // (lane j: run k - 1 + j; p.W records are allocated)
     const int nrec = p.plan_meta[0];
+    const int rj = k - 1 + lane;
+    PlanRecord rr{};
+    if (rj < p.W)
+        rr = p.plan_rec[rj];
     if (k >= nrec)
         return;
-    const PlanRecord rk = p.plan_rec[k];
-    const int b = rk.b;
-    const int n = ctx_tiles(p.context_lens, b, p.max_ctx);
-    if (n == 0)
-        return;
-    const int base = rk.base;
-    const int h = (rk.g0 - base) / n;
-    const int us = base + h * n, ue = us + n;
-    if (us == rk.g0)
+    const int g0k = __builtin_amdgcn_readlane(rr.g0, 1);
+    const int us = __builtin_amdgcn_readlane(rr.us, 1);
+    const int ue = __builtin_amdgcn_readlane(rr.ue, 1);
+    if (us == g0k)
         return;                           // the boundary is a unit start
-    if (p.plan_rec[k - 1].g0 > us)
+    if (__builtin_amdgcn_readlane(rr.g0, 0) > us)
         return;                           // an earlier boundary cuts this unit
-    const int lane = threadIdx.x;
-    // pieces: j = 0 is run k-1 (slot 1), j >= 1 is run k-1+j (slot 0)
+    const int b = __builtin_amdgcn_readlane(rr.b, 1);
+    const int base = __builtin_amdgcn_readlane(rr.base, 1);
+    const int h = (us - base) / (ue - us);
+    // pieces: j = 0 is run k-1 (slot 1), j >= 1 is run k-1+j (slot 0): the
+    // runs from k on that start before the unit's end (a prefix of them)
+    int np = 1 + __builtin_popcountll(
+                     __builtin_amdgcn_ballot_w64(lane >= 1 && rj < nrec && rr.g0 < ue));
+    if (np == 64) {  // a unit over more than 63 runs: count the rest
+        for (int j0 = 64;; j0 += 64) {
+            const int r2 = k - 1 + j0 + lane;
+            const uint64_t m = __builtin_amdgcn_ballot_w64(r2 < nrec && p.plan_rec[r2].g0 < ue);
+            np += __builtin_popcountll(m);
+            if (m != ~0ull)
+                break;
+        }
+    }
     auto piece = [&](int j) -> int64_t {
         return ((int64_t)(k - 1 + j) * 2 + (j == 0 ? 1 : 0)) * p.cols + col;
     };
-    // number of pieces: runs k-1 .. kl with g0 < ue
-    int np = 1;
-    for (int j0 = 0;; j0 += 64) {
-        const int rj = k + j0 + lane;
-        const bool in = rj < nrec && p.plan_rec[rj].g0 < ue;
-        const uint64_t mask = __builtin_amdgcn_ballot_w64(in);
-        np += __builtin_popcountll(mask);
-        if (mask != ~0ull)
-            break;
+    // output row (short chunks: column col is chunk token col / r)
+    int64_t row = (int64_t)b * p.Hq + model_head(p, h) * p.r + col;
+    if (p.q_start) {
+        const int qs = p.q_start[b];
+        const int nq = min(p.q_start[b + 1] - qs, min(max(p.context_lens[b], 0), p.max_ctx));
+        if (col / p.r >= nq)
+            return;
+        row = (int64_t)(qs + col / p.r) * p.Hq + model_head(p, h) * p.r + col % p.r;
+    }
+    // round 2: (m, l) of every piece, the partials of the first kAhead
+    float ahead[kAhead][PER];
+#pragma unroll
+    for (int j = 0; j < kAhead; ++j) {
+        if (j < np) {
+            const float *a = p.ws_acc + piece(j) * D + PER * lane;
+#pragma unroll
+            for (int i = 0; i < PER; ++i)
+                ahead[j][i] = a[i];
+        }
     }
     float mx = -INFINITY;
     for (int j = lane; j < np; j += 64)
@@ -1038,13 +1085,21 @@ __global__ __launch_bounds__(64) void merge_runs_kernel(DecodeParams p)
     for (int j = lane; j < np; j += 64)
         ls += p.ws_ml[2 * piece(j) + 1] * __builtin_amdgcn_exp2f(p.ws_ml[2 * piece(j)] - mx);
     ls = wave_sum(ls);
-    constexpr int PER = D / 64;
     float acc[PER];
 #pragma unroll
     for (int i = 0; i < PER; ++i)
         acc[i] = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kAhead; ++j) {
+        if (j < np) {
+            const float wgt = __builtin_amdgcn_exp2f(p.ws_ml[2 * piece(j)] - mx);
+#pragma unroll
+            for (int i = 0; i < PER; ++i)
+                acc[i] += ahead[j][i] * wgt;
+        }
+    }
 #pragma unroll 4
-    for (int j = 0; j < np; ++j) {
+    for (int j = kAhead; j < np; ++j) {
         const int64_t ix = piece(j);
         const float wgt = __builtin_amdgcn_exp2f(p.ws_ml[2 * ix] - mx);
         const float *a = p.ws_acc + ix * D + PER * lane;
@@ -1053,14 +1108,6 @@ __global__ __launch_bounds__(64) void merge_runs_kernel(DecodeParams p)
             acc[i] += a[i] * wgt;
     }
     const float inv = 1.0f / ls;
-    int64_t row = (int64_t)b * p.Hq + model_head(p, h) * p.r + col;
-    if (p.q_start) {  // short chunks: column col is chunk token col / r, head col % r
-        const int qs = p.q_start[b];
-        const int nq = min(p.q_start[b + 1] - qs, min(max(p.context_lens[b], 0), p.max_ctx));
-        if (col / p.r >= nq)
-            return;
-        row = (int64_t)(qs + col / p.r) * p.Hq + model_head(p, h) * p.r + col % p.r;
-    }
     f16 *orow = p.out + row * D + PER * lane;
 #pragma unroll
     for (int i = 0; i < PER; ++i)
