@@ -297,3 +297,28 @@ def test_extreme_magnitudes_stay_finite(fmt, G, gpu):
         got = _host(case.decode(0, split_tokens=split)).astype(np.float64)
         assert np.isfinite(got).all()
         _check_out(got, ref, "%s g%d x-large split=%d" % (fmt, G, split))
+
+
+@pytest.mark.parametrize("B,hi", [(1500, 200), (9000, 40)])
+def test_large_batches_planned_by_the_plan_kernel(B, hi, gpu):
+    """More than 1024 sequences: the balanced runs come from plan_kernel (one
+    workgroup scanning the lengths; past 8192 sequences its prefix sums stay
+    in global memory instead of LDS), for decode and for short chunks."""
+    # N(0,1) data: the test is about the plan; C1's x8 outlier channels on
+    # Q, K and V at this scale put ~1e-5 of the outputs past the bound in
+    # every partition (fp16 P operands times |V| up to ~30, see the parity
+    # notes of the design), while the four-sequence C1 workload stays within
+    spec = small("c2_mha", B=B, Hq=8, Hkv=2, D=64, G=64, lens="uniform",
+                 lens_args=(1, hi))
+    print("batch", B, flush=True)
+    case = _build(spec, gpu)
+    _, _, _, ref = _expected(case, 0)
+    got = _host(case.decode(0)).astype(np.float64)
+    _check_out(got, ref, "B=%d decode" % B)
+    # the same batch as short chunks of up to 16 / r = 4 tokens (some empty)
+    n = np.minimum(case.lens, np.arange(B) % 5)
+    q = case.chunk_queries(n)
+    pre = case.prefill_attention(0, n, q).float().cpu().numpy()
+    kq, vq, toks, _ = _expected(case, 0)
+    ref_p = E.prefill(q.cpu().numpy(), kq, vq, toks, n)
+    _check_out(pre, ref_p, "B=%d short chunks" % B)
