@@ -250,8 +250,8 @@ def run_short_chunks(args, spec) -> int:
     case.setup_layer(0)              # every token written, the chunks' included
     L = case.layout
     chunk = np.minimum(case.lens, spec.chunk)
-    if chunk.max() * spec.r > 16 or L.cow_pairs.size:
-        raise SystemExit("short-chunk workloads: chunk x (Hq / Hkv) <= 16, no shared blocks")
+    if chunk.max() * spec.r > 32 or L.cow_pairs.size:
+        raise SystemExit("short-chunk workloads: chunk x (Hq / Hkv) <= 32, no shared blocks")
     slot_of = np.full(L.n_unique, -1, np.int64)
     slot_of[L.prefill_ids] = L.prefill_slots
     slot_of[L.append_ids] = L.append_slots
@@ -526,7 +526,7 @@ def main(argv=None) -> int:
     dev = torch.device("cuda:0")
     spec = W.spec(args.workload)
     if spec.chunk > 0:
-        if spec.chunk * spec.r <= 16:
+        if spec.chunk * spec.r <= 32:
             return run_short_chunks(args, spec)
         return run_prefill(args, spec)
     if spec.fp16_heads:

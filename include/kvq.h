@@ -227,12 +227,13 @@ KVQ_API kvq_status kvq_paged_decode(const void *q, const void *k_pool,
  *                 calls sharing it must be ordered).  That size is 0, and
  *                 workspace may be NULL, unless the chunks are short:
  *   How the work is cut:
- *     max_query_len * (Hq / Hkv) <= 16 (short chunks, e.g. a few draft
+ *     max_query_len * (Hq / Hkv) <= 32 (short chunks, e.g. a few draft
  *       tokens of speculative decoding over long contexts): the decode
  *       partition -- the batch's 16-token tiles dealt in equal runs over
  *       every wavefront the GPU holds, an MFMA column per (chunk token,
- *       query head) of a KV head with its own causal bound, cut units merged
- *       by log-sum-exp -- so a handful of sequences still fills the GPU;
+ *       query head) of a KV head with its own causal bound (one or two
+ *       groups of 16 columns per wavefront), cut units merged by
+ *       log-sum-exp -- so a handful of sequences still fills the GPU;
  *     otherwise: one wavefront per (sequence, KV head, group of
  *       16 / (Hq / Hkv) chunk tokens) walks the tokens it needs.
  *   The other arguments are those of kvq_paged_decode.
@@ -252,7 +253,7 @@ KVQ_API kvq_status kvq_paged_prefill(const void *q, const int32_t *query_start,
                              size_t workspace_bytes, void *stream);
 
 /* Workspace bytes kvq_paged_prefill needs for these arguments on the current
- * device: 0 unless max_query_len * (num_q_heads / num_kv_heads) <= 16.
+ * device: 0 unless max_query_len * (num_q_heads / num_kv_heads) <= 32.
  * Returns SIZE_MAX for invalid arguments. */
 KVQ_API size_t kvq_prefill_workspace_size(int32_t num_seqs, int32_t num_q_heads,
                                   int32_t num_kv_heads, int32_t head_dim,

@@ -203,7 +203,7 @@ kvq_status dispatch_write_d(const WriteParams &p, int D, int G, hipStream_t s)
 }
 
 // Resident 64-lane workgroups per CU for a kernel instance (cached per device).
-template <int FMT, int D, int BS, int NG>
+template <int FMT, int D, int BS, int NG, int QG = 1>
 int waves_per_cu()
 {
     static std::atomic<int> cache[kMaxDevices];
@@ -214,7 +214,7 @@ int waves_per_cu()
     if (v == 0) {
         int n = 0;
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                &n, reinterpret_cast<const void *>(&paged_decode_kernel<FMT, D, BS, NG>), 64,
+                &n, reinterpret_cast<const void *>(&paged_decode_kernel<FMT, D, BS, NG, false, QG>), 64,
                 0) != hipSuccess || n <= 0)
             n = 4;
         v = std::min(n, run_waves_per_cu(FMT));
@@ -224,16 +224,17 @@ int waves_per_cu()
 }
 
 struct LaunchPlan {
+    int32_t groups;        // MFMA column groups per wavefront (1, or 2 for > 16 columns)
     int32_t split_tokens;
     int32_t max_ctx;
     size_t ws_bytes;
     uint8_t *ws;
 };
 
-template <int FMT, int D, int BS, int NG>
+template <int FMT, int D, int BS, int NG, int QG>
 kvq_status launch_decode(DecodeParams p, const LaunchPlan &lp, hipStream_t s)
 {
-    const int64_t balanced = (int64_t)device_cus() * waves_per_cu<FMT, D, BS, NG>();
+    const int64_t balanced = (int64_t)device_cus() * waves_per_cu<FMT, D, BS, NG, QG>();
     const int64_t runs = runs_bound(p.B, p.Hkv, lp.max_ctx, lp.split_tokens, balanced);
     if (runs > (1 << 30))
         return KVQ_ERR_UNSUPPORTED;
@@ -263,8 +264,8 @@ kvq_status launch_decode(DecodeParams p, const LaunchPlan &lp, hipStream_t s)
     pp.span_tiles = lp.split_tokens / 16;
     if (!p.inline_plan)
         hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, pp);
-    hipLaunchKernelGGL((paged_decode_kernel<FMT, D, BS, NG>), dim3((unsigned)runs), dim3(64), 0,
-                       s, p);
+    hipLaunchKernelGGL((paged_decode_kernel<FMT, D, BS, NG, false, QG>), dim3((unsigned)runs),
+                       dim3(64), 0, s, p);
     if (runs > 1)
         hipLaunchKernelGGL((merge_runs_kernel<D>),
                            dim3((unsigned)(runs - 1), (unsigned)((p.cols + kMergeCols - 1) / kMergeCols)),
@@ -293,7 +294,10 @@ kvq_status launch_prefill(const DecodeParams &p, hipStream_t s)
 template <int FMT, int D, int BS, int NG>
 kvq_status launch_attention(const DecodeParams &p, const LaunchPlan *lp, hipStream_t s)
 {
-    return lp ? launch_decode<FMT, D, BS, NG>(p, *lp, s) : launch_prefill<FMT, D, BS, NG>(p, s);
+    if (!lp)
+        return launch_prefill<FMT, D, BS, NG>(p, s);
+    return lp->groups == 2 ? launch_decode<FMT, D, BS, NG, 2>(p, *lp, s)
+                           : launch_decode<FMT, D, BS, NG, 1>(p, *lp, s);
 }
 
 // Kernel instances: NG = head_dim / group_size for per-group scales, 0 for
@@ -454,13 +458,15 @@ size_t kvq_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t 
     return w.total;
 }
 
-// Short chunks (at most 16 / r tokens each) are walked by the decode
-// partition: its runs and merge cover every wavefront however few
-// sequences and chunk tokens there are.  Longer chunks take the prefill
-// kernel (one wavefront per sequence, KV head and group of chunk tokens).
+// Short chunks (at most 32 / r tokens each: up to 32 MFMA columns of chunk
+// tokens x query heads, in one or two column groups per wavefront) are
+// walked by the decode partition: its runs and merge cover every wavefront
+// however few sequences and chunk tokens there are.  Longer chunks take the
+// prefill kernel (one wavefront per sequence, KV head and two groups of
+// 16 / r chunk tokens).
 static bool short_chunks(int32_t num_q_heads, int32_t num_kv_heads, int32_t max_query_len)
 {
-    return max_query_len >= 1 && (int64_t)max_query_len * (num_q_heads / num_kv_heads) <= 16;
+    return max_query_len >= 1 && (int64_t)max_query_len * (num_q_heads / num_kv_heads) <= 32;
 }
 
 size_t kvq_prefill_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
@@ -553,6 +559,7 @@ static kvq_status decode_impl(const void *q, const void *k_pool, const void *v_p
     const float sm = softmax_scale > 0.0f ? softmax_scale : 1.0f / std::sqrt((float)head_dim);
     p.score_scale = sm * 1.4426950408889634f;  // log2(e): softmax in base 2
     LaunchPlan lp;
+    lp.groups = 1;
     lp.split_tokens = split_tokens;
     lp.max_ctx = max_context_len;
     lp.ws_bytes = workspace_bytes;
@@ -667,6 +674,7 @@ kvq_status kvq_paged_prefill(const void *q, const int32_t *query_start, int32_t 
     if (split) {  // the decode partition, columns = (chunk token, query head)
         p.cols = max_query_len * r;
         LaunchPlan lp;
+        lp.groups = p.cols > 16 ? 2 : 1;
         lp.split_tokens = 0;
         lp.max_ctx = max_context_len;
         lp.ws_bytes = workspace_bytes;

@@ -362,7 +362,9 @@ struct Cols {
 constexpr int kPrefillGroups = 2;
 
 // kPrefill: chunked prefill instead of decode (see the end of the kernel).
-template <int FMT, int D, int BS, int NG, bool kPrefill = false>
+// kDecodeGroups: MFMA column groups per wavefront in the decode walk (2 for
+// short chunks of more than 16 columns: chunk tokens x query heads).
+template <int FMT, int D, int BS, int NG, bool kPrefill = false, int kDecodeGroups = 1>
 __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
 {
     constexpr int KS = D / 16;   // MFMA k-steps over head_dim
@@ -373,7 +375,7 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
     // one per (KV head, channel) (INT8), none (fp16).
     constexpr bool kGroup = NG > 0;
     constexpr int NA = kGroup ? NG : 1;        // score accumulators per tile
-    constexpr int NQ = kPrefill ? kPrefillGroups : 1;  // column groups per wavefront
+    constexpr int NQ = kPrefill ? kPrefillGroups : kDecodeGroups;  // column groups per wavefront
     constexpr int G = kGroup ? D / NG : D;     // group size
     // INT8 and INT4 codes enter the MFMAs biased (c + kBias)
     constexpr bool kInt8 = FMT == FMT_INT8 || FMT == FMT_INT4;
@@ -887,9 +889,9 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
                 continue;
             }
             // a piece of a unit: slot 0 if it continues a unit, slot 1 if it
-            // starts one (decode only: one column group)
+            // starts one (decode walk only); unit column 16 q + col
             const int slot = t0 > 0 ? 0 : 1;
-            const int64_t idx = ((int64_t)w * 2 + slot) * p.cols + col;
+            const int64_t idx = ((int64_t)w * 2 + slot) * p.cols + 16 * q + col;
             float *wacc = p.ws_acc + idx * D + 16 * grp;
 #pragma unroll
             for (int g4 = 0; g4 < D / 64; ++g4)
@@ -959,11 +961,11 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
     }
 
     // ---- decode: walk the run [g0, g1) unit by unit (values wave-uniform).
-    // Column col is query head col of the unit's KV head; with short chunks
-    // (q_start set: every chunk at most cols / r tokens, chunk token i at
-    // position ctx - nq + i) it is chunk token col / r, query head col % r,
-    // and it takes the tokens at or before its position.
-    const int ci = col / p.r, cj = col % p.r;
+    // Unit column c = 16 q + col (column group q) is query head c of the
+    // unit's KV head; with short chunks (q_start set: every chunk at most
+    // cols / r tokens, chunk token i at position ctx - nq + i) it is chunk
+    // token c / r, query head c % r, and it takes the tokens at or before its
+    // position.
     int b = rec.b;
     int g = rec.g0;
     int n = ctx_tiles(p.context_lens, b, p.max_ctx);
@@ -981,17 +983,24 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
         const int t1 = min(n, t0 + (rec.g1 - g));
         const int ctx = min(p.context_lens[b], p.max_ctx);
         const int gh = model_head(p, h);
-        int qs = b, nq = 1, tcol = 1 << 30;
+        int qs = b, nq = 1, tcol = 1 << 30;  // tcol: causal bound of chunk token 0
         if (p.q_start) {
             qs = p.q_start[b];
             nq = min(p.q_start[b + 1] - qs, max(ctx, 0));
-            tcol = ctx - nq + ci + 1;
+            tcol = ctx - nq + 1;
         }
         run_after = rec.g1 - g - (t1 - t0);
         if (nq > 0) {  // (an empty chunk has nothing to attend)
-            const bool act = col < p.cols && ci < nq;
-            const int64_t row = (int64_t)(qs + (act ? ci : 0)) * p.Hq + gh * p.r + (act ? cj : 0);
-            const Cols cg[NQ] = {Cols{p.q + row * D, p.out + row * D, tcol, act}};
+            Cols cg[NQ];
+#pragma unroll
+            for (int q = 0; q < NQ; ++q) {
+                const int c = 16 * q + col;
+                const int ci = c / p.r, cj = c % p.r;
+                const bool act = c < p.cols && ci < nq;
+                const int64_t row =
+                    (int64_t)(qs + (act ? ci : 0)) * p.Hq + gh * p.r + (act ? cj : 0);
+                cg[q] = Cols{p.q + row * D, p.out + row * D, p.q_start ? tcol + ci : tcol, act};
+            }
             attend(b, h, ctx, n, t0, t1, cg);
         }
         g += t1 - t0;

@@ -5,9 +5,10 @@ Each sequence's chunk is its last n_b tokens (already written by
 kvq_cache_write); chunk token i attends to every token up to its position.
 Chunks: whole prompts, a fixed-size tail chunk after cached tokens, one
 token (where prefill must agree with decode), and short ragged chunks of at
-most 16 / (Hq / Hkv) tokens (empty ones included), which are walked by the
-decode partition: runs over every wavefront, one MFMA column per (chunk
-token, query head) with its own causal bound, cut units merged.  Tolerance
+most 16 / (Hq / Hkv) or 32 / (Hq / Hkv) tokens (empty ones included), which
+are walked by the decode partition: runs over every wavefront, one MFMA
+column per (chunk token, query head) with its own causal bound (one or two
+groups of 16 columns per wavefront), cut units merged.  Tolerance
 as for decode: |gpu - oracle| <= 2e-3 + 1e-3 |oracle|.
 """
 import numpy as np
@@ -51,14 +52,14 @@ def _chunks(lens, mode, r=1):
         return lens.copy()
     if mode == "tail":
         return np.minimum(lens, 37)
-    if mode == "short":  # at most 16 / r tokens, ragged, one empty chunk
-        qpc = 16 // r
+    if mode in ("short", "short2"):  # at most 16 (32) / r tokens, ragged, one empty
+        qpc = (16 if mode == "short" else 32) // r
         pat = [qpc, 1, max(qpc - 1, 1), 0, min(2, qpc)]
         return np.minimum(lens, [pat[b % len(pat)] for b in range(lens.size)])
     return np.ones_like(lens)
 
 
-@pytest.mark.parametrize("mode", ["whole", "tail", "one", "short"])
+@pytest.mark.parametrize("mode", ["whole", "tail", "one", "short", "short2"])
 @pytest.mark.parametrize("name", CASES)
 def test_prefill_within_tolerance(name, mode, gpu):
     print("case", name, mode, flush=True)
@@ -115,8 +116,9 @@ def test_full_size_prefill_sampled_rows(gpu):
     assert ok, "max_abs %.3g max_rel %.3g excess %.3g" % (mabs, mrel, excess)
 
 
+@pytest.mark.parametrize("chunks", [(4, 3, 4, 1, 4, 2), (8, 5, 8, 1, 6, 2)])
 @pytest.mark.parametrize("name", ["c3_gqa", "c3_gqa_fp16"])
-def test_short_chunks_long_context(name, gpu):
+def test_short_chunks_long_context(name, chunks, gpu):
     """A few new tokens per sequence (e.g. draft tokens to verify) over long
     cached contexts: every unit is cut into many pieces.  Lengths one or two
     past a block boundary leave last tiles whose tokens all lie beyond the
@@ -127,7 +129,7 @@ def test_short_chunks_long_context(name, gpu):
     print("workload", spec.name, lens, flush=True)
     case = DecodeCase(spec, device=gpu, gen_device="cpu")
     case.setup_layer(0)
-    n = np.array([4, 3, 4, 1, 4, 2])
+    n = np.array(chunks)
     assert kvq.kvq_prefill_workspace_size(spec.B, spec.Hq, spec.Hkv, spec.D, spec.BS,
                                           case.max_context_len, int(n.max())) > 0
     q = case.chunk_queries(n)

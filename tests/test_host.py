@@ -179,7 +179,7 @@ def test_workspace_size(lib):
 
 def test_prefill_workspace_size(lib):
     from paged_quantized_kv_cache_amd import kvq
-    # short chunks (chunk x Hq/Hkv <= 16) take the decode partition: partial
+    # short chunks (chunk x Hq/Hkv <= 32) take the decode partition: partial
     # slots of chunk x r columns per run
     r4 = kvq.kvq_prefill_workspace_size(16, 32, 8, 128, 16, 32768, 4)
     assert r4 > 0
@@ -187,9 +187,10 @@ def test_prefill_workspace_size(lib):
     assert kvq.kvq_prefill_workspace_size(16, 32, 8, 128, 16, 32768, 1) == \
         kvq.kvq_decode_workspace_size(16, 32, 8, 128, 16, 32768)
     # longer chunks walk per (sequence, KV head, group): no workspace
-    assert kvq.kvq_prefill_workspace_size(16, 32, 8, 128, 16, 32768, 5) == 0
-    assert kvq.kvq_prefill_workspace_size(4, 8, 8, 64, 16, 100, 17) == 0
-    assert kvq.kvq_prefill_workspace_size(4, 8, 8, 64, 16, 100, 16) > 0
+    assert kvq.kvq_prefill_workspace_size(16, 32, 8, 128, 16, 32768, 8) > r4
+    assert kvq.kvq_prefill_workspace_size(16, 32, 8, 128, 16, 32768, 9) == 0
+    assert kvq.kvq_prefill_workspace_size(4, 8, 8, 64, 16, 100, 33) == 0
+    assert kvq.kvq_prefill_workspace_size(4, 8, 8, 64, 16, 100, 32) > 0
     assert kvq.kvq_prefill_workspace_size(4, 8, 8, 64, 16, 100, 0) == 0
     with pytest.raises(ValueError):
         kvq.kvq_prefill_workspace_size(4, 8, 8, 64, 16, 10, 11)   # chunk > context bound
