@@ -108,15 +108,16 @@ kvq_status launch_status()
 // at run_waves_per_cu), at most one run per 4 tiles of the largest possible
 // batch.  With the wavefront priorities, two waves per SIMD keep HBM as busy
 // as three for 1-byte and fp16 codes (and make fewer partials: measured equal
-// on C3 / C5 / fp16, 1-3 % faster on C2 / C4); INT4 tiles carry half the
-// bytes, so INT4 needs three per SIMD for the same bytes in flight (two were
-// 12 % slower).  A fourth wave per SIMD was 1-5 % slower.
+// on C3 / C5 / fp16, 1-3 % faster on C2 / C4; a fourth was 1-5 % slower).
+// INT4 tiles carry half the bytes, so INT4 needs more waves per SIMD for the
+// same bytes in flight: four where its registers allow it (126 VGPRs: C3
+// shape 0.140 ms, against 0.152 ms with three and 12 % more with two).
 // split_tokens > 0: one run per span; the launch covers the largest
 // possible count.
 constexpr int kMaxWavesPerCU = 32;  // hardware bound used for workspace sizing
 constexpr int run_waves_per_cu(int fmt)
 {
-    return fmt == FMT_INT4 ? 12 : 8;  // 3 / 2 per SIMD
+    return fmt == FMT_INT4 ? 16 : 8;  // 4 / 2 per SIMD
 }
 
 bool valid_split(int32_t split_tokens)
