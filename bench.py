@@ -591,6 +591,7 @@ def main(argv=None) -> int:
     if spec.shared_prefix:
         uniq = case.layout.n_unique  # shared blocks counted once
     layer_bytes = [W.algorithmic_bytes(spec, case.lens, f, unique_tokens=uniq) for f in fmts]
+    logical_bytes = [W.algorithmic_bytes(spec, case.lens, f) for f in fmts]
     # dominant kernel: the INT8 decode (all layers of that format)
     dom = [l for l in range(nl) if fmts[l] == "int8"] or list(range(nl))
     dom_ms = float(np.mean(per_layer_ms[dom]))
@@ -645,6 +646,15 @@ def main(argv=None) -> int:
             "avg_launch_ms": round(dom_ms, 5),
         },
         "decode_ms_per_layer": [round(float(x), 5) for x in per_layer_ms] if nl > 1 else None,
+        # whole step, every layer's decode call: unique bytes (shared blocks
+        # once) and logical bytes (every sequence's own reads)
+        "decode_all_layers": {
+            "ms": round(float(per_layer_ms.sum()), 5),
+            "unique_bytes": int(sum(layer_bytes)),
+            "unique_GBps": round(sum(layer_bytes) / (per_layer_ms.sum() * 1e-3) / 1e9, 1),
+            "logical_bytes": int(sum(logical_bytes)),
+            "logical_GBps": round(sum(logical_bytes) / (per_layer_ms.sum() * 1e-3) / 1e9, 1),
+        } if nl > 1 or spec.shared_prefix else None,
         # spread of the timed calls of the dominant format (event times)
         "decode_ms_p10_p50_p90": [round(float(x), 5) for x in
                                   np.percentile(dec_ms[:, dom].ravel(), [10, 50, 90])],
