@@ -214,9 +214,10 @@ int waves_per_cu()
     int v = cache[dev].load(std::memory_order_relaxed);
     if (v == 0) {
         int n = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                &n, reinterpret_cast<const void *>(&paged_decode_kernel<FMT, D, BS, NG, false, QG>), 64,
-                0) != hipSuccess || n <= 0)
+        const void *kernel =
+            reinterpret_cast<const void *>(&paged_decode_kernel<FMT, D, BS, NG, false, QG>);
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, 64, 0) != hipSuccess ||
+            n <= 0)
             n = 4;
         v = std::min(n, run_waves_per_cu(FMT));
         cache[dev].store(v, std::memory_order_relaxed);
@@ -269,7 +270,8 @@ kvq_status launch_decode(DecodeParams p, const LaunchPlan &lp, hipStream_t s)
                        dim3(64), 0, s, p);
     if (runs > 1)
         hipLaunchKernelGGL((merge_runs_kernel<D>),
-                           dim3((unsigned)(runs - 1), (unsigned)((p.cols + kMergeCols - 1) / kMergeCols)),
+                           dim3((unsigned)(runs - 1),
+                                (unsigned)((p.cols + kMergeCols - 1) / kMergeCols)),
                            dim3(64 * std::min(p.cols, kMergeCols)), 0, s, p);
     return launch_status();
 }

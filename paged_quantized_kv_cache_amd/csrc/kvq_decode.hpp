@@ -1013,12 +1013,12 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
 // boundary is the first one of the unit holding tile g0(k), its wavefront c
 // merges column kMergeCols * y + c of that unit (up to kMergeCols wavefronts
 // per workgroup: one per column was 20 % slower on C3, sixteen per workgroup
-// made the 16-column merge of short chunks 2.6x slower).  The pieces are run k-1's slot 1 (the unit's start)
-// and slot 0 of runs k, k+1, ... up to the unit's end.  It runs as its own
-// launch, so the partials written by wavefronts on any XCD are visible
-// without device-wide fences.  Loads go in two rounds: the run records
-// (each carries its unit's bounds), then every piece's (m, l) together with
-// the first pieces' partial outputs.
+// made the 16-column merge of short chunks 2.6x slower).  The pieces are run
+// k-1's slot 1 (the unit's start) and slot 0 of runs k, k+1, ... up to the
+// unit's end.  It runs as its own launch, so the partials written by
+// wavefronts on any XCD are visible without device-wide fences.  Loads go in
+// two rounds: the run records (each carries its unit's bounds), then every
+// piece's (m, l) together with the first pieces' partial outputs.
 constexpr int kMergeCols = 4;
 
 template <int D>
