@@ -502,6 +502,14 @@ def main(argv=None) -> int:
     ap.add_argument("--cpu-seqs", type=int, default=256,
                     help="sequences in the CPU-oracle sample (0 = skip)")
     ap.add_argument("--cpu-min-seconds", type=float, default=10.0)
+    ap.add_argument("--kv-copies", type=int, default=4,
+                    help="single-layer workloads: independent caches the steps rotate "
+                         "over (1 = every step on the same cache)")
+    ap.add_argument("--flush-bytes", type=int, default=0,
+                    help="copy this many bytes between steps, outside the timed decode "
+                         "calls (last-level-cache check; off by default)")
+    ap.add_argument("--flush-mode", choices=("read", "copy"), default="read",
+                    help="read the flush buffer, or copy it (which also leaves dirty lines)")
     ap.add_argument("--copy-calib-bytes", type=int, default=0,
                     help="also run one plain copy of this many bytes (counter calibration)")
     ap.add_argument("--swap", action="store_true",
@@ -532,9 +540,18 @@ def main(argv=None) -> int:
     if spec.fp16_heads:
         return run_mixed_heads(args, spec)
     t_setup = time.perf_counter()
-    case = DecodeCase(spec, device=dev, poison=False)
+    # A single-layer workload keeps `copies` independent caches of its layer
+    # (the per-layer draws of the same recipe) and step i runs on copy
+    # i % copies: consecutive steps touch different K/V, as consecutive layers
+    # of a model do, so no step reads what the previous one left in the
+    # 256 MB last-level cache.  (Back to back on one cache, C3 ran ~3.5 %
+    # faster than with a 2 GiB read between steps.)
+    copies = max(1, args.kv_copies) if spec.layers == 1 else 1
+    import dataclasses
+    case_spec = dataclasses.replace(spec, layers=copies) if copies > 1 else spec
+    case = DecodeCase(case_spec, device=dev, poison=False)
     inputs = []
-    for layer in range(spec.layers):
+    for layer in range(case_spec.layers):
         # prefill every cached token of the layer (untimed), keep only what a
         # decode step needs: the appended tokens' K/V and the queries
         case.gen(layer)
@@ -544,7 +561,7 @@ def main(argv=None) -> int:
         k, v = case.append_inputs(layer)
         q = case.data[layer].q.contiguous()
         case.append(layer, (k, v))
-        if spec.layers > 1:
+        if layer > 0 or spec.layers > 1:   # (copy 0's data feeds the CPU baseline)
             case.data[layer] = None
         inputs.append((k, v, q, torch.empty_like(q)))
     ws = case.workspace(0)
@@ -557,18 +574,34 @@ def main(argv=None) -> int:
     stream = torch.cuda.current_stream()
     nl = spec.layers
 
-    def step(events=None):
-        for layer in range(nl):
+    # optional: stream flush_bytes through a scratch copy before every step
+    # (outside the decode events) so that no K/V can be served from the
+    # last-level cache left by the previous step; a check of that effect,
+    # not the default (the wall-clock step time then includes the copies)
+    flush = None
+    if args.flush_bytes:
+        flush = (torch.empty(args.flush_bytes, dtype=torch.uint8, device=dev),
+                 torch.empty(args.flush_bytes, dtype=torch.uint8, device=dev))
+        flush[0].fill_(1)
+
+    def step(i, events=None):
+        if flush is not None:
+            if args.flush_mode == "copy":
+                flush[1].copy_(flush[0])
+            else:  # read only: no dirty lines left behind
+                torch.amax(flush[0])
+        for li in range(nl):
+            layer = i % copies if copies > 1 else li
             k, v, q, out = inputs[layer]
             case.append(layer, (k, v))
             if events is not None:
-                events[layer][0].record(stream)
+                events[li][0].record(stream)
             case.decode(layer, q=q, out=out, workspace=ws)
             if events is not None:
-                events[layer][1].record(stream)
+                events[li][1].record(stream)
 
-    for _ in range(args.warmup):
-        step()
+    for i in range(args.warmup):
+        step(i)
     torch.cuda.synchronize()
 
     # timed region: exactly `steps` steps, synchronized on both sides
@@ -577,7 +610,7 @@ def main(argv=None) -> int:
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(ev[i])
+        step(args.warmup + i, ev[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
@@ -632,6 +665,7 @@ def main(argv=None) -> int:
             "mean_context": float(case.lens.mean()),
             "max_context": int(case.lens.max()),
             "partition": "balanced runs over the GPU's resident wavefronts",
+            "kv_copies": copies,
         },
         "roofline": {
             "bound": "hbm",
@@ -659,6 +693,8 @@ def main(argv=None) -> int:
         "decode_ms_p10_p50_p90": [round(float(x), 5) for x in
                                   np.percentile(dec_ms[:, dom].ravel(), [10, 50, 90])],
         "measured_copy_gbps": round(copy_gbps, 1),
+        "flush_bytes_between_steps": args.flush_bytes,
+        "flush_mode": args.flush_mode if args.flush_bytes else None,
         "swap": swap,
         "setup_s": round(setup_s, 1),
     }
