@@ -225,6 +225,65 @@ def kvq_prefill_workspace_size(num_seqs: int, num_q_heads: int, num_kv_heads: in
     return n
 
 
+BLOCK_ID_MASK = 0x3FFFFFFF      # table entry bits 0..29: physical block id
+SHARED_HINT_BIT = 1 << 30       # bit 30: shared-block cache hint
+
+
+def _validate_wanted(validate: Optional[bool]) -> bool:
+    if validate is not None:
+        return validate
+    return os.environ.get("KVQ_VALIDATE", "0") not in ("", "0")
+
+
+def validate_decode_inputs(block_tables: torch.Tensor, context_lens: torch.Tensor,
+                           max_context_len: int, block_size: int, num_blocks: int,
+                           query_start: Optional[torch.Tensor] = None) -> None:
+    """Check the device metadata of a decode or prefill call on host copies
+    (synchronizes; a debugging aid, off by default).  The kernels never read
+    outside the pools whatever these hold -- block ids are clamped into the
+    pool and lengths into max_context_len -- but wrong metadata gives wrong
+    attention; this names the first offending sequence instead.
+
+    Checks: every context length in [1, max_context_len]; every table entry
+    a sequence uses (its first ceil(ctx / block_size)) has bit 31 clear and a
+    block id below num_blocks (bit 30, the shared-block hint, is allowed);
+    max_context_len fits the table width; chunk offsets (prefill) are
+    non-decreasing with each chunk no longer than its context."""
+    bt = block_tables.detach().to("cpu", torch.int64)
+    cl = context_lens.detach().to("cpu", torch.int64).reshape(-1)
+    B, width = bt.shape
+    if cl.numel() != B:
+        raise ValueError("context_lens has %d entries for %d table rows" % (cl.numel(), B))
+    if max_context_len > width * block_size:
+        raise ValueError("max_context_len %d exceeds the table width (%d blocks of %d)"
+                         % (max_context_len, width, block_size))
+    bad = ((cl < 1) | (cl > max_context_len)).nonzero()
+    if bad.numel():
+        b = int(bad[0])
+        raise ValueError("sequence %d: context length %d outside [1, %d]"
+                         % (b, int(cl[b]), max_context_len))
+    used = (torch.arange(width)[None, :] * block_size) < cl[:, None]
+    neg = (bt < 0) & used           # int32 entries with bit 31 set
+    ids = bt & BLOCK_ID_MASK
+    over = (ids >= num_blocks) & used
+    for what, m in (("has bit 31 set", neg), ("names a block outside the pool", over)):
+        hit = m.nonzero()
+        if hit.numel():
+            b, i = int(hit[0, 0]), int(hit[0, 1])
+            raise ValueError("sequence %d: table entry %d (%#x) %s (%d blocks)"
+                             % (b, i, int(bt[b, i]) & 0xFFFFFFFF, what, num_blocks))
+    if query_start is not None:
+        qs = query_start.detach().to("cpu", torch.int64).reshape(-1)
+        if qs.numel() != B + 1:
+            raise ValueError("query_start has %d entries for %d sequences" % (qs.numel(), B))
+        n = qs[1:] - qs[:-1]
+        bad = ((n < 0) | (n > cl)).nonzero()
+        if bad.numel():
+            b = int(bad[0])
+            raise ValueError("sequence %d: chunk of %d tokens for a context of %d"
+                             % (b, int(n[b]), int(cl[b])))
+
+
 def alloc_workspace(nbytes: int, device="cuda") -> Optional[torch.Tensor]:
     """Decode workspace (contents on entry do not matter)."""
     if nbytes == 0:
@@ -239,8 +298,10 @@ def kvq_paged_decode(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor
                      softmax_scale: float = 0.0, split_tokens: int = 0,
                      out: Optional[torch.Tensor] = None,
                      workspace: Optional[torch.Tensor] = None,
-                     stream=None) -> torch.Tensor:
-    """One decode step of paged attention (see kvq.h).  Returns ``out``."""
+                     stream=None, validate: Optional[bool] = None) -> torch.Tensor:
+    """One decode step of paged attention (see kvq.h).  Returns ``out``.
+    ``validate`` (default: the KVQ_VALIDATE environment variable) checks the
+    tables and lengths on the host first (validate_decode_inputs)."""
     num_blocks, hkv, bs, d = _pool_geometry(k_pool, fmt)
     B, hq, dq = q.shape
     if q.dtype != torch.float16 or dq != d:
@@ -249,6 +310,8 @@ def kvq_paged_decode(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor
         raise ValueError("block_tables must be int32 [B][max_blocks]")
     if context_lens.dtype != torch.int32 or context_lens.numel() != B:
         raise ValueError("context_lens must be int32 [B]")
+    if _validate_wanted(validate) and B > 0:
+        validate_decode_inputs(block_tables, context_lens, max_context_len, bs, num_blocks)
     if out is None:
         out = torch.empty_like(q)
     for t in (q, k_pool, v_pool, block_tables, context_lens, out):
@@ -341,7 +404,7 @@ def kvq_paged_prefill(q: torch.Tensor, query_start: torch.Tensor, max_query_len:
                       max_context_len: int, fmt: str, group_size: int = 0,
                       softmax_scale: float = 0.0, out: Optional[torch.Tensor] = None,
                       workspace: Optional[torch.Tensor] = None,
-                      stream=None) -> torch.Tensor:
+                      stream=None, validate: Optional[bool] = None) -> torch.Tensor:
     """Causal attention of each sequence's chunk (its last n_b tokens, already
     in the pool) over its cached tokens.  q: fp16 [sum n][Hq][D];
     query_start: int32 [B + 1] on the device.  ``workspace`` (allocated here
@@ -353,6 +416,9 @@ def kvq_paged_prefill(q: torch.Tensor, query_start: torch.Tensor, max_query_len:
         raise ValueError("q must be contiguous fp16 [tokens][Hq][head_dim]")
     if query_start.dtype != torch.int32 or query_start.numel() != B + 1:
         raise ValueError("query_start must be int32 [B + 1]")
+    if _validate_wanted(validate) and B > 0:
+        validate_decode_inputs(block_tables, context_lens, max_context_len, bs, num_blocks,
+                               query_start)
     if out is None:
         out = torch.empty_like(q)
     if workspace is None and B > 0 and max_query_len > 0:
@@ -395,11 +461,13 @@ def kvq_paged_decode_heads(q: torch.Tensor, num_kv_heads: int, kv_head_ids: torc
                            max_context_len: int, fmt: str, group_size: int = 0,
                            out: Optional[torch.Tensor] = None, workspace=None,
                            softmax_scale: float = 0.0, split_tokens: int = 0,
-                           stream=None) -> torch.Tensor:
+                           stream=None, validate: Optional[bool] = None) -> torch.Tensor:
     """kvq_paged_decode over a pool holding the model KV heads
     ``kv_head_ids``; writes only their query heads' rows of ``out``."""
     num_blocks, hkv, bs, d = _pool_geometry(k_pool, fmt)
     B, hq, _ = q.shape
+    if _validate_wanted(validate) and B > 0:
+        validate_decode_inputs(block_tables, context_lens, max_context_len, bs, num_blocks)
     if out is None:
         out = torch.zeros_like(q)
     if workspace is None:

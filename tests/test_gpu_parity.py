@@ -322,3 +322,19 @@ def test_large_batches_planned_by_the_plan_kernel(B, hi, gpu):
     kq, vq, toks, _ = _expected(case, 0)
     ref_p = E.prefill(q.cpu().numpy(), kq, vq, toks, n)
     _check_out(pre, ref_p, "B=%d short chunks" % B)
+
+
+def test_validation_flag_checks_device_metadata(gpu, monkeypatch):
+    """KVQ_VALIDATE=1: the binding checks tables and lengths on host copies
+    before the launch; a corrupt entry is named instead of silently clamped."""
+    spec = SMALL_CASES["gqa_int8_g64_outliers"]
+    case = _build(spec, gpu)
+    monkeypatch.setenv("KVQ_VALIDATE", "1")
+    _, _, _, ref = _expected(case, 0)
+    _check_out(_host(case.decode(0)).astype(np.float64), ref, "validated decode")
+    bt = case.block_tables.clone()
+    bt[3, 2] = case.layout.num_blocks + 5            # sequence 3 uses 7 blocks
+    case.block_tables, good = bt, case.block_tables
+    with pytest.raises(ValueError, match="sequence 3: table entry 2"):
+        case.decode(0)
+    case.block_tables = good

@@ -124,6 +124,35 @@ def test_generated_inputs_are_reproducible():
     assert np.array_equal(l1, l2)
 
 
+def test_host_validation_of_decode_metadata():
+    from paged_quantized_kv_cache_amd import kvq
+    bt = torch.tensor([[3, 5, 7, 0], [1 | kvq.SHARED_HINT_BIT, 2, 99, -1]], dtype=torch.int32)
+    cl = torch.tensor([40, 20], dtype=torch.int32)   # 3 and 2 blocks of 16 in use
+    kvq.validate_decode_inputs(bt, cl, 64, 16, 8)      # unused entries are not read
+    with pytest.raises(ValueError, match="sequence 1: context length 0"):
+        kvq.validate_decode_inputs(bt, torch.tensor([40, 0], dtype=torch.int32), 64, 16, 8)
+    with pytest.raises(ValueError, match=r"context length 70 outside \[1, 64\]"):
+        kvq.validate_decode_inputs(bt, torch.tensor([70, 20], dtype=torch.int32), 64, 16, 8)
+    with pytest.raises(ValueError, match="outside the pool"):
+        kvq.validate_decode_inputs(bt, torch.tensor([40, 33], dtype=torch.int32), 64, 16, 8)
+    with pytest.raises(ValueError, match="bit 31"):
+        kvq.validate_decode_inputs(bt, torch.tensor([40, 64], dtype=torch.int32), 64, 16, 8)
+    with pytest.raises(ValueError, match="table width"):
+        kvq.validate_decode_inputs(bt, cl, 65, 16, 8)
+    qs = torch.tensor([0, 4, 4], dtype=torch.int32)
+    kvq.validate_decode_inputs(bt, cl, 64, 16, 8, qs)
+    with pytest.raises(ValueError, match="chunk of 25 tokens"):
+        kvq.validate_decode_inputs(bt, cl, 64, 16, 8, torch.tensor([0, 4, 29], dtype=torch.int32))
+    # the workloads' own tables pass
+    s = W.spec("c5_prefix_mixed", B=10, shared_prefix=64, lens_args=(3, 90), fork_pairs=3)
+    rng = np.random.default_rng(0)
+    lens = W.draw_lengths(s, rng)
+    L = W.build_layout(s, lens, rng)
+    t = torch.from_numpy(np.where(L.block_tables_hinted < 0, 0, L.block_tables_hinted))
+    kvq.validate_decode_inputs(t, torch.from_numpy(lens.astype(np.int32)), int(lens.max()),
+                               s.BS, L.num_blocks)
+
+
 # ------------------------------------------------------------------ library
 @pytest.fixture(scope="module")
 def lib():
