@@ -250,8 +250,8 @@ def run_short_chunks(args, spec) -> int:
     case.setup_layer(0)              # every token written, the chunks' included
     L = case.layout
     chunk = np.minimum(case.lens, spec.chunk)
-    if chunk.max() * spec.r > 32 or L.cow_pairs.size:
-        raise SystemExit("short-chunk workloads: chunk x (Hq / Hkv) <= 32, no shared blocks")
+    if L.cow_pairs.size:
+        raise SystemExit("chunk workloads: no shared blocks")
     slot_of = np.full(L.n_unique, -1, np.int64)
     slot_of[L.prefill_ids] = L.prefill_slots
     slot_of[L.append_ids] = L.append_slots
@@ -267,7 +267,7 @@ def run_short_chunks(args, spec) -> int:
     qstart = case.query_start(chunk)
     ws = kvq.alloc_workspace(kvq.kvq_prefill_workspace_size(
         spec.B, spec.Hq, spec.Hkv, spec.D, spec.BS, case.max_context_len,
-        int(chunk.max())), dev)
+        int(chunk.max()), args.prefill_split), dev)
     p = case.pools[0]
     nchunk = int(chunk.sum())
     # decode's algorithmic bytes with q / out for every chunk token, plus
@@ -281,7 +281,8 @@ def run_short_chunks(args, spec) -> int:
                             spec.G)
         if ev is not None:
             ev[0].record(stream)
-        case.prefill_attention(0, chunk, q, out=out, workspace=ws, query_start=qstart)
+        case.prefill_attention(0, chunk, q, out=out, workspace=ws, query_start=qstart,
+                               split_mode=args.prefill_split)
         if ev is not None:
             ev[1].record(stream)
 
@@ -313,7 +314,7 @@ def run_short_chunks(args, spec) -> int:
                    "num_seqs": spec.B, "num_q_heads": spec.Hq, "num_kv_heads": spec.Hkv,
                    "head_dim": spec.D, "block_size": spec.BS, "kv_format": spec.fmt,
                    "group_size": spec.G, "chunk_tokens": nchunk,
-                   "cached_tokens": int(case.lens.sum())},
+                   "cached_tokens": int(case.lens.sum()), "prefill_split": args.prefill_split},
         "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
                      "kernel": "kvq_paged_prefill, short chunks: paged_decode_kernel + "
@@ -502,6 +503,8 @@ def main(argv=None) -> int:
     ap.add_argument("--cpu-seqs", type=int, default=256,
                     help="sequences in the CPU-oracle sample (0 = skip)")
     ap.add_argument("--cpu-min-seconds", type=float, default=10.0)
+    ap.add_argument("--prefill-split", choices=("auto", "walk", "split"), default="auto",
+                    help="chunk workloads: how kvq_paged_prefill cuts the work")
     ap.add_argument("--kv-copies", type=int, default=4,
                     help="single-layer workloads: independent caches the steps rotate "
                          "over (1 = every step on the same cache)")
@@ -534,7 +537,7 @@ def main(argv=None) -> int:
     dev = torch.device("cuda:0")
     spec = W.spec(args.workload)
     if spec.chunk > 0:
-        if spec.chunk * spec.r <= 32:
+        if spec.chunk < max(spec.lens_args):   # chunks after cached tokens
             return run_short_chunks(args, spec)
         return run_prefill(args, spec)
     if spec.fp16_heads:

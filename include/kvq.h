@@ -96,6 +96,13 @@ enum {
     KVQ_INT4 = 4       /* symmetric, |code| <= 7, two per byte, per-group   */
 };
 
+/* How kvq_paged_prefill cuts the work (its split_mode argument). */
+enum {
+    KVQ_PREFILL_AUTO = 0,
+    KVQ_PREFILL_WALK = 1,   /* a wavefront per (sequence, KV head, token groups) */
+    KVQ_PREFILL_SPLIT = 2   /* the decode partition over every wavefront         */
+};
+
 typedef int32_t kvq_status;
 enum {
     KVQ_OK = 0,
@@ -222,20 +229,23 @@ KVQ_API kvq_status kvq_paged_decode(const void *q, const void *k_pool,
  *   query_start   int32 [num_seqs + 1] on the device, non-decreasing, with
  *                 n_b <= context_lens[b]; max_query_len >= every n_b is the
  *                 host-side bound that sizes the launch.
+ *   split_mode    how the work is cut (KVQ_PREFILL_*):
+ *     WALK: one wavefront per (sequence, KV head, two groups of
+ *       16 / (Hq / Hkv) chunk tokens) walks the tokens it needs;
+ *     SPLIT: the decode partition -- the batch's 16-token tiles dealt in
+ *       equal runs over every wavefront the GPU holds, an MFMA column per
+ *       (chunk token, query head) of a KV head with its own causal bound
+ *       (one or two groups of 16 columns per wavefront), cut units merged
+ *       by log-sum-exp.  Chunks of more than 32 / (Hq / Hkv) tokens are
+ *       first cut into virtual sequences of that many tokens (a small
+ *       launch writes their lengths into the workspace);
+ *     AUTO: SPLIT for chunks of at most 32 / (Hq / Hkv) tokens and
+ *       whenever WALK would launch fewer wavefronts than the GPU holds (a
+ *       few sequences with short chunks over long contexts), else WALK.
  *   workspace     device scratch of kvq_prefill_workspace_size(...) bytes
  *                 for these arguments (its contents on entry do not matter;
  *                 calls sharing it must be ordered).  That size is 0, and
- *                 workspace may be NULL, unless the chunks are short:
- *   How the work is cut:
- *     max_query_len * (Hq / Hkv) <= 32 (short chunks, e.g. a few draft
- *       tokens of speculative decoding over long contexts): the decode
- *       partition -- the batch's 16-token tiles dealt in equal runs over
- *       every wavefront the GPU holds, an MFMA column per (chunk token,
- *       query head) of a KV head with its own causal bound (one or two
- *       groups of 16 columns per wavefront), cut units merged by
- *       log-sum-exp -- so a handful of sequences still fills the GPU;
- *     otherwise: one wavefront per (sequence, KV head, group of
- *       16 / (Hq / Hkv) chunk tokens) walks the tokens it needs.
+ *                 workspace may be NULL, when the cut is WALK.
  *   The other arguments are those of kvq_paged_decode.
  */
 KVQ_API kvq_status kvq_paged_prefill(const void *q, const int32_t *query_start,
@@ -249,16 +259,16 @@ KVQ_API kvq_status kvq_paged_prefill(const void *q, const int32_t *query_start,
                              int32_t head_dim, int32_t block_size,
                              int32_t num_blocks, int32_t dtype,
                              int32_t group_size, float softmax_scale,
-                             void *out, void *workspace,
+                             int32_t split_mode, void *out, void *workspace,
                              size_t workspace_bytes, void *stream);
 
-/* Workspace bytes kvq_paged_prefill needs for these arguments on the current
- * device: 0 unless max_query_len * (num_q_heads / num_kv_heads) <= 32.
- * Returns SIZE_MAX for invalid arguments. */
+/* Workspace bytes kvq_paged_prefill needs for these arguments and split_mode
+ * on the current device (0 when the cut is WALK).  Returns SIZE_MAX for
+ * invalid arguments. */
 KVQ_API size_t kvq_prefill_workspace_size(int32_t num_seqs, int32_t num_q_heads,
                                   int32_t num_kv_heads, int32_t head_dim,
                                   int32_t block_size, int32_t max_context_len,
-                                  int32_t max_query_len);
+                                  int32_t max_query_len, int32_t split_mode);
 
 /*
  * Per-head mixed precision (xpshop.cn article 312, s6: the attention heads

@@ -461,33 +461,103 @@ size_t kvq_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t 
     return w.total;
 }
 
-// Short chunks (at most 32 / r tokens each: up to 32 MFMA columns of chunk
-// tokens x query heads, in one or two column groups per wavefront) are
-// walked by the decode partition: its runs and merge cover every wavefront
-// however few sequences and chunk tokens there are.  Longer chunks take the
-// prefill kernel (one wavefront per sequence, KV head and two groups of
-// 16 / r chunk tokens).
-static bool short_chunks(int32_t num_q_heads, int32_t num_kv_heads, int32_t max_query_len)
+// How kvq_paged_prefill cuts the work.
+//   walk:    one wavefront per (sequence, KV head, two groups of 16 / r chunk
+//            tokens) walks the tokens it needs (the prefill kernel);
+//   short:   chunks of at most 32 / r tokens (up to 32 MFMA columns of chunk
+//            tokens x query heads, one or two column groups per wavefront)
+//            go through the decode partition: balanced runs over every
+//            resident wavefront and the merge of cut units;
+//   virtual: longer chunks are cut into virtual sequences of 32 / r tokens
+//            (virtual_chunks_kernel), which the decode partition then walks.
+// Automatic choice: short chunks always split; longer ones split when the
+// walk would launch fewer wavefronts than the GPU holds (few sequences and
+// chunk tokens over long contexts), else walk (e.g. whole prompts).
+enum PrefillPath { kPathWalk, kPathShort, kPathVirtual };
+struct PrefillCut {
+    PrefillPath path;
+    int32_t qpg;    // chunk tokens per virtual sequence
+    int32_t J;      // virtual sequences per sequence
+    int32_t cols;   // MFMA columns per unit
+    int64_t V;      // sequences the decode partition sees
+};
+
+static bool valid_prefill_mode(int32_t mode)
 {
-    return max_query_len >= 1 && (int64_t)max_query_len * (num_q_heads / num_kv_heads) <= 32;
+    return mode == KVQ_PREFILL_AUTO || mode == KVQ_PREFILL_WALK || mode == KVQ_PREFILL_SPLIT;
+}
+
+static PrefillCut prefill_cut(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                              int32_t max_query_len, int32_t mode)
+{
+    const int32_t r = num_q_heads / num_kv_heads;
+    PrefillCut c{kPathWalk, 0, 1, r, num_seqs};
+    if (max_query_len < 1 || mode == KVQ_PREFILL_WALK)
+        return c;
+    const bool fits = (int64_t)max_query_len * r <= 32;
+    if (mode == KVQ_PREFILL_AUTO && !fits) {
+        const int64_t tokens_per_wave = 2 * (16 / r);
+        const int64_t walk_waves = (int64_t)num_seqs * num_kv_heads *
+                                   ((max_query_len + tokens_per_wave - 1) / tokens_per_wave);
+        if (walk_waves >= (int64_t)device_cus() * run_waves_per_cu(FMT_INT8))
+            return c;
+    }
+    if (fits) {
+        c.path = kPathShort;
+        c.cols = max_query_len * r;
+        return c;
+    }
+    c.path = kPathVirtual;
+    c.qpg = 32 / r;
+    c.J = (max_query_len + c.qpg - 1) / c.qpg;
+    c.cols = c.qpg * r;
+    c.V = (int64_t)num_seqs * c.J;
+    return c;
+}
+
+// Workspace of a split prefill: the virtual-sequence arrays (virtual path),
+// then the decode workspace for the sequences the partition sees.
+struct PrefillWs {
+    size_t vctx_off, vrow_off, vqs_off, decode_off, total;
+};
+
+static bool prefill_ws(const PrefillCut &c, int32_t num_kv_heads, int32_t head_dim,
+                       int32_t max_context_len, PrefillWs &w)
+{
+    auto up256 = [](size_t x) { return (x + 255) / 256 * 256; };
+    const int64_t nv = c.path == kPathVirtual ? c.V : 0;
+    w.vctx_off = 0;
+    w.vrow_off = up256((size_t)nv * 4);
+    w.vqs_off = w.vrow_off + up256((size_t)nv * 4);
+    w.decode_off = c.path == kPathVirtual ? w.vqs_off + up256((size_t)(nv + 1) * 4) : 0;
+    const int64_t balanced = (int64_t)device_cus() * kMaxWavesPerCU;
+    const int64_t runs = runs_bound((int32_t)c.V, num_kv_heads, max_context_len, 0, balanced);
+    WsLayout d;
+    if (!workspace_layout((int32_t)c.V, c.cols, head_dim, runs, d))
+        return false;
+    w.total = w.decode_off + d.total;
+    return true;
 }
 
 size_t kvq_prefill_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                   int32_t head_dim, int32_t block_size,
-                                  int32_t max_context_len, int32_t max_query_len)
+                                  int32_t max_context_len, int32_t max_query_len,
+                                  int32_t split_mode)
 {
     (void)block_size;
     if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
         num_q_heads % num_kv_heads != 0 || head_dim <= 0 || max_query_len < 0 ||
-        max_context_len < max_query_len)
+        max_context_len < max_query_len || !valid_prefill_mode(split_mode) ||
+        num_q_heads / num_kv_heads > 16)
         return SIZE_MAX;
-    if (!short_chunks(num_q_heads, num_kv_heads, max_query_len))
+    const PrefillCut c =
+        prefill_cut(num_seqs, num_q_heads, num_kv_heads, max_query_len, split_mode);
+    if (c.path == kPathWalk || num_seqs == 0)
         return 0;
-    const int64_t balanced = (int64_t)device_cus() * kMaxWavesPerCU;
-    const int64_t runs = runs_bound(num_seqs, num_kv_heads, max_context_len, 0, balanced);
-    WsLayout w;
-    if (!workspace_layout(num_seqs, max_query_len * (num_q_heads / num_kv_heads), head_dim,
-                          runs, w))
+    if (c.V > INT32_MAX)
+        return SIZE_MAX;
+    PrefillWs w;
+    if (!prefill_ws(c, num_kv_heads, head_dim, max_context_len, w))
         return SIZE_MAX;
     return w.total;
 }
@@ -615,8 +685,8 @@ kvq_status kvq_paged_prefill(const void *q, const int32_t *query_start, int32_t 
                              int32_t max_context_len, int32_t num_seqs, int32_t num_q_heads,
                              int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                              int32_t num_blocks, int32_t dtype, int32_t group_size,
-                             float softmax_scale, void *out, void *workspace,
-                             size_t workspace_bytes, void *stream)
+                             float softmax_scale, int32_t split_mode, void *out,
+                             void *workspace, size_t workspace_bytes, void *stream)
 {
     kvq_status st = check_format(dtype, head_dim, block_size, group_size);
     if (st != KVQ_OK)
@@ -634,7 +704,7 @@ kvq_status kvq_paged_prefill(const void *q, const int32_t *query_start, int32_t 
     if (max_context_len < max_query_len ||
         (int64_t)max_blocks_per_seq * block_size < max_context_len)
         return KVQ_ERR_INVALID_ARG;
-    if (!(softmax_scale >= 0.0f) || std::isinf(softmax_scale))
+    if (!(softmax_scale >= 0.0f) || std::isinf(softmax_scale) || !valid_prefill_mode(split_mode))
         return KVQ_ERR_INVALID_ARG;
     if (!q || !query_start || !k_pool || !v_pool || !block_tables || !context_lens || !out)
         return KVQ_ERR_INVALID_ARG;
@@ -644,11 +714,18 @@ kvq_status kvq_paged_prefill(const void *q, const int32_t *query_start, int32_t 
         (k_scale && !aligned16(k_scale)) || (v_scale && !aligned16(v_scale)) ||
         (workspace && !aligned16(workspace)))
         return KVQ_ERR_INVALID_ARG;
-    const bool split = short_chunks(num_q_heads, num_kv_heads, max_query_len);
-    if (split && max_tiles(num_seqs, num_kv_heads, max_context_len) >= (int64_t)1 << 30)
-        return KVQ_ERR_UNSUPPORTED;
-    if (split && !workspace)
-        return KVQ_ERR_WORKSPACE;
+    const PrefillCut cut =
+        prefill_cut(num_seqs, num_q_heads, num_kv_heads, max_query_len, split_mode);
+    PrefillWs pw{};
+    if (cut.path != kPathWalk) {
+        if (cut.V > INT32_MAX ||
+            max_tiles((int32_t)cut.V, num_kv_heads, max_context_len) >= (int64_t)1 << 30)
+            return KVQ_ERR_UNSUPPORTED;
+        if (!prefill_ws(cut, num_kv_heads, head_dim, max_context_len, pw))
+            return KVQ_ERR_INVALID_ARG;
+        if (!workspace || workspace_bytes < pw.total)
+            return KVQ_ERR_WORKSPACE;
+    }
     st = check_device();
     if (st != KVQ_OK)
         return st;
@@ -674,16 +751,36 @@ kvq_status kvq_paged_prefill(const void *q, const int32_t *query_start, int32_t 
     p.q_start = query_start;
     p.qpc = 16 / r;
     p.groups = (max_query_len + p.qpc - 1) / p.qpc;
-    if (split) {  // the decode partition, columns = (chunk token, query head)
-        p.cols = max_query_len * r;
+    if (cut.path != kPathWalk) {  // the decode partition, columns = (chunk token, query head)
+        hipStream_t s = static_cast<hipStream_t>(stream);
+        uint8_t *ws = static_cast<uint8_t *>(workspace);
+        if (cut.path == kPathVirtual) {
+            VirtualParams vp;
+            vp.q_start = query_start;
+            vp.context_lens = context_lens;
+            vp.vctx = reinterpret_cast<int32_t *>(ws + pw.vctx_off);
+            vp.vrow = reinterpret_cast<int32_t *>(ws + pw.vrow_off);
+            vp.vqs = reinterpret_cast<int32_t *>(ws + pw.vqs_off);
+            vp.B = num_seqs;
+            vp.J = cut.J;
+            vp.qpg = cut.qpg;
+            vp.max_ctx = max_context_len;
+            const int64_t threads = cut.V + 1;
+            hipLaunchKernelGGL(virtual_chunks_kernel, dim3((unsigned)((threads + 255) / 256)),
+                               dim3(256), 0, s, vp);
+            p.B = (int32_t)cut.V;
+            p.context_lens = vp.vctx;
+            p.q_start = vp.vqs;
+            p.seq_row = vp.vrow;
+        }
+        p.cols = cut.cols;
         LaunchPlan lp;
         lp.groups = p.cols > 16 ? 2 : 1;
         lp.split_tokens = 0;
         lp.max_ctx = max_context_len;
-        lp.ws_bytes = workspace_bytes;
-        lp.ws = static_cast<uint8_t *>(workspace);
-        return dispatch_attention(p, &lp, dtype, head_dim, block_size, group_size,
-                                  static_cast<hipStream_t>(stream));
+        lp.ws_bytes = workspace_bytes - pw.decode_off;
+        lp.ws = ws + pw.decode_off;
+        return dispatch_attention(p, &lp, dtype, head_dim, block_size, group_size, s);
     }
     p.cols = r;
     return dispatch_attention(p, nullptr, dtype, head_dim, block_size, group_size,

@@ -114,6 +114,9 @@ struct DecodeParams {
     // chunks: [B + 1] offsets in q / out (chunked prefill, and short chunks
     // walked by the decode partition); null for decode
     const int32_t *q_start;
+    // [B] table row of each (virtual) sequence when the chunks of longer
+    // prompts are cut into virtual sequences; null: row b is sequence b
+    const int32_t *seq_row;
     int32_t qpc;             // chunk tokens per wavefront (16 / r)
     int32_t groups;          // ceil(max chunk length / qpc)
 };
@@ -261,6 +264,50 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanParams p)
         const int n = S[lo + 1] - S[lo];  // > 0: tile g0 lies in sequence lo
         const int us = base + (g0 - base) / n * n;
         p.rec[w] = PlanRecord{lo, g0, g1, base, us, us + n, {0, 0}};
+    }
+}
+
+// Virtual sequences for chunks longer than one wavefront's columns: chunk
+// j of sequence b (tokens [j qpg, (j + 1) qpg) of its chunk, qpg = 32 / r)
+// becomes virtual sequence v = b J + j, whose context ends at its last chunk
+// token (so the causal bounds come out as for the whole chunk) and whose
+// chunk is those qpg tokens; chunks past the end of b's are empty (context
+// 0, no tiles).  The decode partition then runs over the B J virtual
+// sequences with seq_row[v] = b choosing the block-table row.
+struct VirtualParams {
+    const int32_t *q_start;       // [B + 1]
+    const int32_t *context_lens;  // [B]
+    int32_t *vctx;                // [B J]
+    int32_t *vrow;                // [B J]
+    int32_t *vqs;                 // [B J + 1]
+    int32_t B;
+    int32_t J;
+    int32_t qpg;
+    int32_t max_ctx;
+};
+
+__global__ __launch_bounds__(256) void virtual_chunks_kernel(VirtualParams p)
+{
+    const int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t nv = (int64_t)p.B * p.J;
+    if (v > nv)
+        return;
+    if (v == nv) {
+        p.vqs[v] = p.q_start[p.B];
+        return;
+    }
+    const int b = (int)(v / p.J), j = (int)(v % p.J);
+    const int ctx = min(max(p.context_lens[b], 0), p.max_ctx);
+    const int qs = p.q_start[b];
+    const int nb = max(min(p.q_start[b + 1] - qs, ctx), 0);
+    const int lo = j * p.qpg;
+    p.vrow[v] = b;
+    if (lo < nb) {
+        p.vctx[v] = ctx - nb + min(lo + p.qpg, nb);
+        p.vqs[v] = qs + lo;
+    } else {
+        p.vctx[v] = 0;
+        p.vqs[v] = qs + nb;
     }
 }
 
@@ -767,7 +814,8 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
         // sequence: the leading windows (among the three first loaded) that
         // hold a shared block are walked with ordinary loads, the rest with
         // nontemporal ones.
-        const int32_t *bt = p.block_tables + (int64_t)b * p.max_blocks;
+        const int32_t *bt =
+            p.block_tables + (int64_t)(p.seq_row ? p.seq_row[b] : b) * p.max_blocks;
         constexpr int TPB = BS / 16;                // tiles per block
         const int blk_last = (16 * t1 - 1) / BS;    // last block of the piece
         // (entries past the piece repeat its last block: never used, and the

@@ -171,7 +171,8 @@ class DecodeCase:
         return torch.from_numpy(qs).to(self.device)
 
     def prefill_attention(self, layer: int, chunk_lens, q: torch.Tensor,
-                          out=None, workspace=None, query_start=None) -> torch.Tensor:
+                          out=None, workspace=None, query_start=None,
+                          split_mode="auto") -> torch.Tensor:
         """Chunked prefill: sequence b's last chunk_lens[b] tokens attend
         causally (their K/V are already in the pool).  ``query_start``: the
         offsets from query_start(chunk_lens), made here when None."""
@@ -183,7 +184,7 @@ class DecodeCase:
                                      p.k_pool, p.v_pool, p.k_scale, p.v_scale,
                                      self.block_tables, self.context_lens,
                                      self.max_context_len, p.fmt, s.G, out=out,
-                                     workspace=workspace)
+                                     workspace=workspace, split_mode=split_mode)
 
     # ------------------------------------------------------------ readback
     def gather_codes(self, layer: int, seqs=None):

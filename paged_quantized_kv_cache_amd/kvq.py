@@ -24,6 +24,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libkvq.so")
 
 KVQ_FP16, KVQ_INT8, KVQ_FP8_E4M3, KVQ_FP8_E5M2, KVQ_INT4 = 0, 1, 2, 3, 4
+# kvq_paged_prefill split modes
+PREFILL_SPLIT_MODES = {"auto": 0, "walk": 1, "split": 2}
 FORMATS = {"fp16": KVQ_FP16, "int8": KVQ_INT8, "fp8": KVQ_FP8_E4M3, "e5m2": KVQ_FP8_E5M2,
            "int4": KVQ_INT4}
 # INT8 pools hold excess-128 bytes (code + 128), FP8 pools E4M3 / E5M2 bytes,
@@ -96,9 +98,9 @@ def lib() -> ctypes.CDLL:
             L.kvq_paged_prefill.restype = i32
             L.kvq_paged_prefill.argtypes = [P, P, i32, P, P, P, P, P, i32, P, i32, i32,
                                             i32, i32, i32, i32, i32, i32, i32,
-                                            ctypes.c_float, P, P, ctypes.c_size_t, P]
+                                            ctypes.c_float, i32, P, P, ctypes.c_size_t, P]
             L.kvq_prefill_workspace_size.restype = ctypes.c_size_t
-            L.kvq_prefill_workspace_size.argtypes = [i32] * 7
+            L.kvq_prefill_workspace_size.argtypes = [i32] * 8
             L.kvq_decode_workspace_size.restype = ctypes.c_size_t
             L.kvq_decode_workspace_size.argtypes = [i32] * 7
             L.kvq_copy_blocks.restype = i32
@@ -215,11 +217,16 @@ def kvq_decode_workspace_size(num_seqs: int, num_q_heads: int, num_kv_heads: int
     return n
 
 
+def _split_mode(mode) -> int:
+    return PREFILL_SPLIT_MODES[mode] if isinstance(mode, str) else int(mode)
+
+
 def kvq_prefill_workspace_size(num_seqs: int, num_q_heads: int, num_kv_heads: int,
                                head_dim: int, block_size: int, max_context_len: int,
-                               max_query_len: int) -> int:
+                               max_query_len: int, split_mode="auto") -> int:
     n = int(lib().kvq_prefill_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim,
-                                             block_size, max_context_len, max_query_len))
+                                             block_size, max_context_len, max_query_len,
+                                             _split_mode(split_mode)))
     if n == ctypes.c_size_t(-1).value:
         raise ValueError("invalid workspace arguments")
     return n
@@ -404,11 +411,13 @@ def kvq_paged_prefill(q: torch.Tensor, query_start: torch.Tensor, max_query_len:
                       max_context_len: int, fmt: str, group_size: int = 0,
                       softmax_scale: float = 0.0, out: Optional[torch.Tensor] = None,
                       workspace: Optional[torch.Tensor] = None,
-                      stream=None, validate: Optional[bool] = None) -> torch.Tensor:
+                      stream=None, validate: Optional[bool] = None,
+                      split_mode="auto") -> torch.Tensor:
     """Causal attention of each sequence's chunk (its last n_b tokens, already
     in the pool) over its cached tokens.  q: fp16 [sum n][Hq][D];
-    query_start: int32 [B + 1] on the device.  ``workspace`` (allocated here
-    when None) is only used for short chunks (see kvq.h)."""
+    query_start: int32 [B + 1] on the device.  ``split_mode``: "auto",
+    "walk" or "split" (see kvq.h); ``workspace`` (allocated here when None)
+    is used by the split cut only."""
     num_blocks, hkv, bs, d = _pool_geometry(k_pool, fmt)
     T, hq, dq = q.shape
     B = context_lens.numel()
@@ -423,14 +432,15 @@ def kvq_paged_prefill(q: torch.Tensor, query_start: torch.Tensor, max_query_len:
         out = torch.empty_like(q)
     if workspace is None and B > 0 and max_query_len > 0:
         workspace = alloc_workspace(kvq_prefill_workspace_size(
-            B, hq, hkv, d, bs, max_context_len, max_query_len), q.device)
+            B, hq, hkv, d, bs, max_context_len, max_query_len, split_mode), q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib().kvq_paged_prefill(_ptr(q), _ptr(query_start), max_query_len, _ptr(k_pool),
                                  _ptr(v_pool), _ptr(k_scale), _ptr(v_scale),
                                  _ptr(block_tables), block_tables.shape[1],
                                  _ptr(context_lens), max_context_len, B, hq, hkv, d, bs,
-                                 num_blocks, _fmt(fmt), group_size, softmax_scale, _ptr(out),
-                                 _ptr(workspace), ws_bytes, _stream(stream))
+                                 num_blocks, _fmt(fmt), group_size, softmax_scale,
+                                 _split_mode(split_mode), _ptr(out), _ptr(workspace), ws_bytes,
+                                 _stream(stream))
     _check(st, "kvq_paged_prefill")
     return out
 

@@ -151,6 +151,13 @@ SPECS: Dict[str, Spec] = {
         chunk=8,
         description="8 new tokens per sequence (two groups of 16 MFMA columns) "
                     "attending over 16 contexts of 32,768 tokens, GQA INT8 g64"),
+    "p4_medium_chunks": Spec(
+        "p4_medium_chunks", B=4, Hq=32, Hkv=8, D=128, BS=16, fmt="int8", G=64,
+        lens="fixed", lens_args=(32768,) * 4, seed=0, k_out=Outliers(5, 10.0),
+        chunk=32,
+        description="32-token chunks of 4 sequences (e.g. draft tokens to verify) "
+                    "attending over 32,768 cached tokens each (virtual sequences of "
+                    "8 tokens), GQA INT8 g64"),
     "c5_prefix_mixed": Spec(
         "c5_prefix_mixed", B=128, Hq=32, Hkv=8, D=128, BS=16, fmt="int8",
         G=128, lens="prefix_tails", lens_args=(64, 4096), seed=0, layers=32,

@@ -59,16 +59,20 @@ def _chunks(lens, mode, r=1):
     return np.ones_like(lens)
 
 
+@pytest.mark.parametrize("cut", ["walk", "split"])
 @pytest.mark.parametrize("mode", ["whole", "tail", "one", "short", "short2"])
 @pytest.mark.parametrize("name", CASES)
-def test_prefill_within_tolerance(name, mode, gpu):
-    print("case", name, mode, flush=True)
+def test_prefill_within_tolerance(name, mode, cut, gpu):
+    """Both cuts of the work on every chunk shape: the per-(sequence, KV head,
+    token groups) walk, and the decode partition (chunks longer than 32 / r
+    tokens cut into virtual sequences first)."""
+    print("case", name, mode, cut, flush=True)
     spec = SMALL_CASES[name]
     case = DecodeCase(spec, device=gpu, gen_device="cpu")
     case.setup_layer(0)
     n = _chunks(case.lens, mode, spec.Hq // spec.Hkv)
     q = case.chunk_queries(n)
-    got = case.prefill_attention(0, n, q).float().cpu().numpy()
+    got = case.prefill_attention(0, n, q, split_mode=cut).float().cpu().numpy()
     assert np.isfinite(got).all()
     kq, vq, toks = _quantized(case, 0, range(spec.B))
     ref = E.prefill(q.cpu().numpy(), kq, vq, toks, n)
@@ -116,7 +120,8 @@ def test_full_size_prefill_sampled_rows(gpu):
     assert ok, "max_abs %.3g max_rel %.3g excess %.3g" % (mabs, mrel, excess)
 
 
-@pytest.mark.parametrize("chunks", [(4, 3, 4, 1, 4, 2), (8, 5, 8, 1, 6, 2)])
+@pytest.mark.parametrize("chunks", [(4, 3, 4, 1, 4, 2), (8, 5, 8, 1, 6, 2),
+                                    (40, 17, 64, 1, 33, 2)])
 @pytest.mark.parametrize("name", ["c3_gqa", "c3_gqa_fp16"])
 def test_short_chunks_long_context(name, chunks, gpu):
     """A few new tokens per sequence (e.g. draft tokens to verify) over long

@@ -217,24 +217,37 @@ def test_prefill_workspace_size(lib):
         kvq.kvq_decode_workspace_size(16, 32, 8, 128, 16, 32768)
     # longer chunks walk per (sequence, KV head, group): no workspace
     assert kvq.kvq_prefill_workspace_size(16, 32, 8, 128, 16, 32768, 8) > r4
-    assert kvq.kvq_prefill_workspace_size(16, 32, 8, 128, 16, 32768, 9) == 0
-    assert kvq.kvq_prefill_workspace_size(4, 8, 8, 64, 16, 100, 33) == 0
+    # longer chunks: the walk needs nothing; split cuts them into virtual
+    # sequences of 32 / r tokens (their lengths, then the decode workspace)
+    assert kvq.kvq_prefill_workspace_size(16, 32, 8, 128, 16, 32768, 9, "walk") == 0
+    v9 = kvq.kvq_prefill_workspace_size(16, 32, 8, 128, 16, 32768, 9, "split")
+    assert v9 > kvq.kvq_prefill_workspace_size(16, 32, 8, 128, 16, 32768, 8)
+    # auto: few sequences and chunk tokens -> split; whole prompts -> walk
+    assert kvq.kvq_prefill_workspace_size(16, 32, 8, 128, 16, 32768, 9) == v9
+    assert kvq.kvq_prefill_workspace_size(16, 32, 8, 128, 16, 2048, 2048) == 0
+    assert kvq.kvq_prefill_workspace_size(16, 32, 8, 128, 16, 2048, 2048, "split") > 0
+    assert kvq.kvq_prefill_workspace_size(4, 8, 8, 64, 16, 100, 33, "walk") == 0
     assert kvq.kvq_prefill_workspace_size(4, 8, 8, 64, 16, 100, 32) > 0
+    assert kvq.kvq_prefill_workspace_size(4, 8, 8, 64, 16, 100, 32, "walk") == 0
     assert kvq.kvq_prefill_workspace_size(4, 8, 8, 64, 16, 100, 0) == 0
     with pytest.raises(ValueError):
         kvq.kvq_prefill_workspace_size(4, 8, 8, 64, 16, 10, 11)   # chunk > context bound
     with pytest.raises(ValueError):
         kvq.kvq_prefill_workspace_size(4, 6, 4, 64, 16, 100, 2)   # Hq % Hkv != 0
+    with pytest.raises(ValueError):
+        kvq.kvq_prefill_workspace_size(4, 8, 2, 64, 16, 100, 2, 7)  # no such mode
 
 
 def test_prefill_arguments_rejected_before_any_device_work(lib):
     dummy = ctypes.c_void_p(16)
 
-    def pre(mq=4, ws=None, mcl=60, Hq=8, Hkv=2, D=64):
+    def pre(mq=4, ws=None, mcl=60, Hq=8, Hkv=2, D=64, mode=0):
         return lib.kvq_paged_prefill(dummy, dummy, mq, dummy, dummy, dummy, dummy, dummy, 4,
-                                     dummy, mcl, 2, Hq, Hkv, D, 16, 8, 1, 64, 0.0, dummy,
-                                     ws, 0, None)
+                                     dummy, mcl, 2, Hq, Hkv, D, 16, 8, 1, 64, 0.0, mode,
+                                     dummy, ws, 0, None)
     assert pre(mq=4) == -3                       # short chunks need a workspace
+    assert pre(mq=20, mode=2) == -3              # so does a forced split of longer ones
+    assert pre(mq=4, mode=5) == -1               # no such split mode
     assert pre(mq=0) == 0                        # nothing to do
     assert pre(mq=61) == -1                      # chunk longer than the context bound
     assert pre(Hq=6, Hkv=4) == -1
