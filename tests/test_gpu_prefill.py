@@ -149,3 +149,28 @@ def test_short_chunks_long_context(name, chunks, gpu):
     qd = q[torch.from_numpy(last).to(q.device)].contiguous()
     dec = case.decode(0, q=qd).float().cpu().numpy()
     assert np.all(np.abs(dec - got[last]) <= 2 * (ATOL + RTOL * np.abs(ref[last])))
+
+
+@pytest.mark.parametrize("name", ["p2_short_chunks", "p3_short_chunks_8", "p4_medium_chunks"])
+def test_full_size_chunk_workloads_sampled(name, gpu):
+    """The chunk workloads at their benchmark sizes (sequences of 32,768
+    cached tokens with 4-, 8- or 32-token chunks), cut as the benchmark
+    times them (split mode auto: the short-chunk path, or virtual sequences
+    for the 32-token chunks): every chunk row of the first and the last
+    sequence against the oracle, and every output finite."""
+    spec = W.spec(name)
+    print("workload", spec.name, flush=True)
+    case = DecodeCase(spec, device=gpu, poison=True)
+    case.setup_layer(0)
+    n = np.minimum(case.lens, spec.chunk)
+    q = case.chunk_queries(n)
+    got = case.prefill_attention(0, n, q).float()
+    assert torch.isfinite(got).all()
+    got = got.cpu().numpy()
+    seqs = [0, spec.B - 1]
+    starts = np.concatenate([[0], np.cumsum(n)])
+    rows = np.concatenate([np.arange(starts[b], starts[b + 1]) for b in seqs])
+    kq, vq, toks = _quantized(case, 0, seqs)
+    ref = E.prefill(q.cpu().numpy()[rows], kq, vq, toks, n[seqs])
+    ok, mabs, mrel, excess = E.tolerance_ok(got[rows], ref, ATOL, RTOL)
+    assert ok, "max_abs %.3g max_rel %.3g excess %.3g" % (mabs, mrel, excess)
