@@ -12,24 +12,27 @@
 // through the block table (a 16-token block, or half of a 32-token block),
 // with the next tile's loads in flight while the current one is computed.
 //
-// Both contractions run on 16x16x16 fp16 MFMA with the head_dim / token axes
-// laid out so that no data moves between lanes except for softmax maxima.
+// Both contractions run on fp16 MFMA (16x16x32 on gfx950, which issues at
+// the rate of the older 16x16x16) with the head_dim / token axes laid out so
+// that no data moves between lanes except for softmax maxima.
 // Lane (col, grp) = (lane % 16, lane / 16):
 //   S^T[token][head] = K_tile (16 x D) * Q^T (D x 16)
-//       A operand: token `col`, 4 head dims per k-step; B operand: q of query
-//       head `col` (zero for col >= r), same dims.  Output: the scores of
-//       query head `col` for the tile's tokens 4*grp .. 4*grp+3.
+//       A operand: token `col`, 8 head dims per MFMA (two 4-dim k-steps);
+//       B operand: q of query head `col` (zero for col >= r), same dims.
+//       Output: the scores of query head `col` for the tile's tokens
+//       4*grp .. 4*grp+3.
 //   O^T[d][head] += V_tile^T (16 dims x 16 tokens) * P^T (16 tokens x 16 heads)
 //       B operand = P^T, exactly the softmaxed S^T output already in the
-//       lane; A operand: 4 consecutive tokens of one dim, which the V
-//       micro-tile layout stores next to each other.
+//       lane, as an fp16 pair hi + lo; A operand: 4 consecutive tokens of
+//       one dim (which the V micro-tile layout stores next to each other),
+//       taken once against hi and once against lo.
 // The head_dim order inside an MFMA k-step is a permutation chosen so that
 // each lane's K bytes are contiguous; q is loaded with the same permutation.
-// Codes are converted to exact fp16 (INT8 c + 1152, INT4 c + 1032, or E4M3
-// value * 2^-8, or E5M2 value)
-// right before the MFMA; K group scales multiply the per-group partial dot
+// Codes are converted to exact fp16 (INT8 / INT4 code c, E4M3 value * 2^-8,
+// E5M2 value) right before the MFMA; K group scales multiply the per-group partial dot
 // products (one accumulator per group); V group scales are folded into P
-// (rounded to fp16 once) so the token sum stays a single MFMA chain.
+// (kept to ~2^-22 relative by the hi + lo pair) so the token sum stays a
+// single MFMA chain.
 //
 // Online softmax in base 2 (the log2(e) factor rides on the score scale), with
 // a rescale of the running output only when some head's maximum exceeds the
@@ -411,8 +414,13 @@ constexpr int kPrefillGroups = 2;
 // kPrefill: chunked prefill instead of decode (see the end of the kernel).
 // kDecodeGroups: MFMA column groups per wavefront in the decode walk (2 for
 // short chunks of more than 16 columns: chunk tokens x query heads).
+// The INT4 decode instance runs four wavefronts per SIMD (its tiles carry
+// half the bytes, so more of them must be in flight), which needs it to fit
+// in 128 VGPRs (with 32-token blocks that would spill; it runs three).
 template <int FMT, int D, int BS, int NG, bool kPrefill = false, int kDecodeGroups = 1>
-__global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
+__global__ __launch_bounds__(64, (FMT == FMT_INT4 && BS == 16 && !kPrefill &&
+                                  kDecodeGroups == 1) ? 4 : 1)
+void paged_decode_kernel(DecodeParams p)
 {
     constexpr int KS = D / 16;   // MFMA k-steps over head_dim
     constexpr int DT = D / 16;   // 16-dim output tiles
@@ -424,12 +432,17 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
     constexpr int NA = kGroup ? NG : 1;        // score accumulators per tile
     constexpr int NQ = kPrefill ? kPrefillGroups : kDecodeGroups;  // column groups per wavefront
     constexpr int G = kGroup ? D / NG : D;     // group size
-    // INT8 and INT4 codes enter the MFMAs biased (c + kBias)
-    constexpr bool kInt8 = FMT == FMT_INT8 || FMT == FMT_INT4;
-    constexpr float kBias = FMT == FMT_INT4 ? kInt4Bias : kInt8Bias;
     constexpr bool kChannel = FMT == FMT_INT8 && !kGroup;
     static_assert(FMT != FMT_INT4 || (D == 128 && kGroup), "INT4: head_dim 128, group scales");
     constexpr float kCodeScale = FMT == FMT_FP8 ? 256.0f : 1.0f;  // E4M3 enters as value * 2^-8
+    // PV precision.  P enters the PV MFMA as fp16, rounded with relative
+    // error <= 2^-11, so a single fp16 P moves an output by up to 2^-11 times
+    // the largest |V| the softmax weighs (the weights sum to 1): inside an
+    // absolute 2e-3 only while |V| <= 4.  Outlier channels in V reach ~30.
+    // P is therefore split into hi = fp16(P) and lo = fp16(P - hi), which
+    // leaves ~2^-22 relative, and one 16x16x32 MFMA per d-tile takes the
+    // codes twice, against hi and against lo: on gfx950 it issues at the
+    // rate of the 16x16x16 MFMA a single P would need.
     static_assert(!kGroup || G >= 64, "groups must cover a 64-dim chunk");
 
     const int w = blockIdx.x;
@@ -573,31 +586,6 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
                 }
             }
         }
-        // INT8 codes enter both MFMAs as c + 1152 (no subtraction per code).
-        // The score of group j is corrected by 1152 * (sum of q over the
-        // group); the output by 1152 * (sum of the P^T operand entries of the
-        // group), accumulated in csum with the same rescales as o.
-        float qbias[NQ][NA];
-        if constexpr (kInt8) {
-#pragma unroll
-            for (int q = 0; q < NQ; ++q)
-#pragma unroll
-            for (int j = 0; j < NA; ++j) {
-                float sum = 0.0f;
-#pragma unroll
-                for (int s = j * (KS / NA); s < (j + 1) * (KS / NA); ++s) {
-                    const f16x4 &x = qop[q][s];
-                    sum += ((float)x[0] + (float)x[1]) + ((float)x[2] + (float)x[3]);
-                    if constexpr (kChannel) {
-                        const f16x4 &y = qlo[q][s];
-                        sum += ((float)y[0] + (float)y[1]) + ((float)y[2] + (float)y[3]);
-                    }
-                }
-                sum += __shfl_xor(sum, 16);
-                sum += __shfl_xor(sum, 32);
-                qbias[q][j] = kBias * sum;
-            }
-        }
         float score_scale = score_scale0;
         float out_scale = 1.0f;
         if constexpr ((FMT == FMT_FP8 || FMT == FMT_E5M2) && !kGroup) {
@@ -615,11 +603,10 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
             lane_fac = e < 4 * NG ? score_scale * kCodeScale : kCodeScale;
             lane_tok = 4 * grp + (e % (4 * NG)) / NG;
         }
-
         // o[q][tau][v]: output dim 64 (tau / 4) + 16 grp + 4 v + tau % 4 of
-        // column col of group q; m, l, csum likewise per group
+        // column col of group q; m, l likewise per group
         f32x4 o[NQ][DT];
-        float m[NQ], l[NQ], csum[NQ][NA];
+        float m[NQ], l[NQ];
 #pragma unroll
         for (int q = 0; q < NQ; ++q) {
 #pragma unroll
@@ -627,9 +614,6 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
                 o[q][i] = f32x4{0.f, 0.f, 0.f, 0.f};
             m[q] = kNoMax;
             l[q] = 0.0f;
-#pragma unroll
-            for (int j = 0; j < NA; ++j)
-                csum[q][j] = 0.0f;
         }
 
         // One tile of 16 tokens starting at logical token ts, data in `cur`.
@@ -654,35 +638,41 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
 #pragma unroll
                 for (int i = 0; i < NA; ++i)
                     sacc[q][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+            // K operand of k-step s (4 head dims per lane, see the q order)
+            auto kop = [&](int s) -> f16x4 {
+                if constexpr (FMT == FMT_INT8)
+                    return int8x4_to_f16x4(cur.k[s]);
+                else if constexpr (FMT == FMT_FP8)
+                    return fp8x4_to_f16x4_scaled(cur.k[s]);
+                else if constexpr (FMT == FMT_E5M2)
+                    return e5m2x4_to_f16x4(cur.k[s]);
+                else
+                    return f16x4_from_u2(cur.k[2 * s], cur.k[2 * s + 1]);
+            };
+            // two k-steps per 16x16x32 MFMA; both lie in one scale group
 #pragma unroll
-            for (int s = 0; s < KS; ++s) {
-                f16x4 a;
-                if constexpr (FMT == FMT_INT4) {  // a dword holds k-steps 2q, 2q + 1
+            for (int s2 = 0; s2 < KS / 2; ++s2) {
+                f16x8 a;
+                if constexpr (FMT == FMT_INT4) {  // a dword holds k-steps 2 s2, 2 s2 + 1
                     f16x4 lo, hi;
-                    int4x8_to_f16x4_biased(cur.k[s >> 1], lo, hi);
-                    a = (s & 1) ? hi : lo;
-                } else if constexpr (FMT == FMT_INT8) {
-                    a = int8x4_to_f16x4_biased(cur.k[s]);
-                } else if constexpr (FMT == FMT_FP8) {
-                    a = fp8x4_to_f16x4_scaled(cur.k[s]);
-                } else if constexpr (FMT == FMT_E5M2) {
-                    a = e5m2x4_to_f16x4(cur.k[s]);
+                    int4x8_to_f16x4(cur.k[s2], lo, hi);
+                    a = cat8(lo, hi);
                 } else {
-                    a = f16x4_from_u2(cur.k[2 * s], cur.k[2 * s + 1]);
+                    a = cat8(kop(2 * s2), kop(2 * s2 + 1));
                 }
-                const int gi = NA == 2 ? (s >> 2) : 0;
+                const int gi = NA == 2 ? (s2 >> 1) : 0;
 #pragma unroll
                 for (int q = 0; q < NQ; ++q) {
                     sacc[q][gi] =
-                        __builtin_amdgcn_mfma_f32_16x16x16f16(a, qop[q][s], sacc[q][gi], 0, 0, 0);
+                        mfma32(a, cat8(qop[q][2 * s2], qop[q][2 * s2 + 1]), sacc[q][gi]);
                     if constexpr (kChannel)
                         sacc[q][0] =
-                            __builtin_amdgcn_mfma_f32_16x16x16f16(a, qlo[q][s], sacc[q][0], 0, 0, 0);
+                            mfma32(a, cat8(qlo[q][2 * s2], qlo[q][2 * s2 + 1]), sacc[q][0]);
                 }
             }
             // ---- scores of tokens ts + 4 grp + v for query head col (base 2)
             const int tok0 = ts + 4 * grp;
-            f16x4 pop[NQ][NA];
+            f16x4 pop[NQ][NA], plo[NQ][NA];
 #pragma unroll
             for (int q = 0; q < NQ; ++q) {
                 float z[4];
@@ -690,11 +680,9 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
                 for (int v = 0; v < 4; ++v) {
                     float acc;
                     if constexpr (kGroup) {
-                        acc = (kInt8 ? sacc[q][0][v] - qbias[q][0] : sacc[q][0][v]) * sk[v][0];
+                        acc = sacc[q][0][v] * sk[v][0];
                         if constexpr (NA == 2)
-                            acc += (kInt8 ? sacc[q][1][v] - qbias[q][1] : sacc[q][1][v]) * sk[v][1];
-                    } else if constexpr (kInt8) {
-                        acc = (sacc[q][0][v] - qbias[q][0]) * score_scale;
+                            acc += sacc[q][1][v] * sk[v][1];
                     } else {
                         acc = sacc[q][0][v] * score_scale;
                     }
@@ -721,9 +709,6 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
 #pragma unroll
                     for (int i = 0; i < DT; ++i)
                         o[q][i] *= alpha;
-#pragma unroll
-                    for (int j = 0; j < NA; ++j)
-                        csum[q][j] *= alpha;
                     m[q] = mn;
                 }
                 float pr[4];
@@ -733,18 +718,15 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
                     l[q] += pr[v];
                 }
                 // ---- P^T operands (V group scales folded in; masked tokens
-                // have pr = 0 and a zeroed scale)
+                // have pr = 0 and a zeroed scale): hi = fp16(P), lo = fp16(P - hi)
 #pragma unroll
                 for (int j = 0; j < NA; ++j) {
 #pragma unroll
-                    for (int v = 0; v < 4; ++v)
-                        pop[q][j][v] = kGroup ? (f16)(pr[v] * sv[v][j]) : (f16)pr[v];
-                    if constexpr (kInt8) {
-                        const f16x2 ones = {(f16)1.0f, (f16)1.0f};
-                        csum[q][j] = __builtin_amdgcn_fdot2(f16x2{pop[q][j][0], pop[q][j][1]},
-                                                            ones, csum[q][j], false);
-                        csum[q][j] = __builtin_amdgcn_fdot2(f16x2{pop[q][j][2], pop[q][j][3]},
-                                                            ones, csum[q][j], false);
+                    for (int v = 0; v < 4; ++v) {
+                        const float P = kGroup ? pr[v] * sv[v][j] : pr[v];
+                        const f16 h16 = (f16)P;
+                        pop[q][j][v] = h16;
+                        plo[q][j][v] = (f16)(P - (float)h16);
                     }
                 }
             }
@@ -765,16 +747,17 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
                 const int nv = t_end - tok0;
                 vmask8 = nv >= 4 ? ~0u : (nv <= 0 ? 0u : (1u << (8 * nv)) - 1u);
             }
+            // one 16x16x32 MFMA per d-tile: the codes twice, against hi and lo
 #pragma unroll
             for (int tau = 0; tau < DT; ++tau) {
                 const int g4 = tau >> 2, i = tau & 3;
                 f16x4 a;
                 if constexpr (FMT == FMT_INT4) {  // a dword holds dims 4 col + i, i = 2x, 2x + 1
                     f16x4 lo, hi;
-                    int4x8_to_f16x4_biased(cur.v[2 * g4 + (i >> 1)], lo, hi);
+                    int4x8_to_f16x4(cur.v[2 * g4 + (i >> 1)], lo, hi);
                     a = (i & 1) ? hi : lo;
                 } else if constexpr (FMT == FMT_INT8) {
-                    a = int8x4_to_f16x4_biased(cur.v[4 * g4 + i]);
+                    a = int8x4_to_f16x4(cur.v[4 * g4 + i]);
                 } else if constexpr (FMT == FMT_FP8) {
                     a = fp8x4_to_f16x4_scaled(cur.v[4 * g4 + i]);
                 } else if constexpr (FMT == FMT_E5M2) {
@@ -787,8 +770,7 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
                 const int gi = NA == 2 ? (64 * g4) / G : 0;
 #pragma unroll
                 for (int q = 0; q < NQ; ++q)
-                    o[q][tau] =
-                        __builtin_amdgcn_mfma_f32_16x16x16f16(a, pop[q][gi], o[q][tau], 0, 0, 0);
+                    o[q][tau] = mfma32(cat8(a, a), cat8(pop[q][gi], plo[q][gi]), o[q][tau]);
             }
         };
 
@@ -888,19 +870,6 @@ __global__ __launch_bounds__(64) void paged_decode_kernel(DecodeParams p)
         for (int q = 0; q < NQ; ++q) {
             float lt = l[q] + __shfl_xor(l[q], 16);
             lt += __shfl_xor(lt, 32);
-            if constexpr (kInt8) {
-                // remove the code bias: o -= 1152 * (sum of P^T entries of the group)
-                float cb[NA];
-#pragma unroll
-                for (int j = 0; j < NA; ++j) {
-                    float c = csum[q][j] + __shfl_xor(csum[q][j], 16);
-                    c += __shfl_xor(c, 32);
-                    cb[j] = kBias * c;
-                }
-#pragma unroll
-                for (int tau = 0; tau < DT; ++tau)
-                    o[q][tau] -= cb[(64 * (tau >> 2)) / G];
-            }
             if (!cg[q].active)
                 continue;
             if constexpr (kChannel) {

@@ -3,10 +3,14 @@
 // Element conversions used inside the attention loops.  They turn stored
 // codes into exact fp16 values for the MFMA operands:
 //   INT8 code c (|c| <= 127), stored as the excess-128 byte u = c + 128 ->
-//     fp16 holding c + 1152 exactly, via the 1024 + byte trick (an fp16 with
-//     exponent field 25 has a unit step, so the bit pattern 0x6400 | u is the
-//     number 1024 + u).  The constant 1152 is removed after the dot products,
-//     where it costs one term per row instead of one subtraction per code.
+//     fp16 c: the 1024 + byte trick (an fp16 with exponent field 25 has a
+//     unit step, so the bit pattern 0x6400 | u is the number 1024 + u) gives
+//     c + 1152, and one packed fp16 subtraction per two codes removes 1152
+//     exactly (all integers below 2048 are fp16 values).  The codes enter
+//     the contractions unbiased: a bias removed after the dot products would
+//     leave fp32 sums ~1152 / |c| times larger than the result, whose
+//     rounding then shows in scores of large-scale keys and in outputs near
+//     zero of large-scale values.
 //   E4M3 code -> fp16 equal to value * 2^-8 exactly: moving the 4 exponent
 //     and 3 mantissa bits into the fp16 fields keeps the mantissa and
 //     re-biases the exponent from 7 to 15 (subnormals land on fp16
@@ -37,6 +41,7 @@ constexpr float fp8_max()
 typedef _Float16 f16;
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
@@ -64,15 +69,14 @@ __device__ __forceinline__ uint32_t byte_perm(uint32_t hi, uint32_t lo,
     return __builtin_amdgcn_perm(hi, lo, sel);
 }
 
-// Four excess-128 INT8 bytes (one dword) -> 4 exact fp16 holding c + 1152.
-constexpr float kInt8Bias = 1152.0f;
-constexpr float kInt4Bias = 1032.0f;  // 1024 + 8 (excess-8 nibbles)
-__device__ __forceinline__ f16x4 int8x4_to_f16x4_biased(uint32_t w)
+// Four excess-128 INT8 bytes (one dword) -> 4 exact fp16 holding c.
+__device__ __forceinline__ f16x4 int8x4_to_f16x4(uint32_t w)
 {
     const uint32_t lo = byte_perm(0x64646464u, w, 0x04010400u);  // 0x64 | byte 0, 0x64 | byte 1
     const uint32_t hi = byte_perm(0x64646464u, w, 0x04030402u);
-    const f16x2 a = bit_cast<f16x2>(lo);
-    const f16x2 b = bit_cast<f16x2>(hi);
+    const f16x2 bias = {(f16)1152.0f, (f16)1152.0f};
+    const f16x2 a = bit_cast<f16x2>(lo) - bias;
+    const f16x2 b = bit_cast<f16x2>(hi) - bias;
     return f16x4{a.x, a.y, b.x, b.y};
 }
 
@@ -89,16 +93,18 @@ __device__ __forceinline__ f16x4 fp8x4_to_f16x4_scaled(uint32_t w)
     return f16x4{a.x, a.y, b.x, b.y};
 }
 
-// Eight excess-8 INT4 nibbles (one dword) -> two f16x4 holding c + 1032:
-// `lo` from the low nibbles of bytes 0..3, `hi` from the high nibbles.
-__device__ __forceinline__ void int4x8_to_f16x4_biased(uint32_t w, f16x4 &lo, f16x4 &hi)
+// Eight excess-8 INT4 nibbles (one dword) -> two f16x4 holding c (1024 +
+// nibble, less 1032): `lo` from the low nibbles of bytes 0..3, `hi` from the
+// high nibbles.
+__device__ __forceinline__ void int4x8_to_f16x4(uint32_t w, f16x4 &lo, f16x4 &hi)
 {
     const uint32_t l = w & 0x0f0f0f0fu;
     const uint32_t h = (w >> 4) & 0x0f0f0f0fu;
-    const f16x2 a = bit_cast<f16x2>(byte_perm(0x64646464u, l, 0x04010400u));
-    const f16x2 b = bit_cast<f16x2>(byte_perm(0x64646464u, l, 0x04030402u));
-    const f16x2 c = bit_cast<f16x2>(byte_perm(0x64646464u, h, 0x04010400u));
-    const f16x2 d = bit_cast<f16x2>(byte_perm(0x64646464u, h, 0x04030402u));
+    const f16x2 bias = {(f16)1032.0f, (f16)1032.0f};
+    const f16x2 a = bit_cast<f16x2>(byte_perm(0x64646464u, l, 0x04010400u)) - bias;
+    const f16x2 b = bit_cast<f16x2>(byte_perm(0x64646464u, l, 0x04030402u)) - bias;
+    const f16x2 c = bit_cast<f16x2>(byte_perm(0x64646464u, h, 0x04010400u)) - bias;
+    const f16x2 d = bit_cast<f16x2>(byte_perm(0x64646464u, h, 0x04030402u)) - bias;
     lo = f16x4{a.x, a.y, b.x, b.y};
     hi = f16x4{c.x, c.y, d.x, d.y};
 }
@@ -119,6 +125,22 @@ __device__ __forceinline__ f16x4 f16x4_from_u2(uint32_t lo, uint32_t hi)
     const f16x2 a = bit_cast<f16x2>(lo);
     const f16x2 b = bit_cast<f16x2>(hi);
     return f16x4{a.x, a.y, b.x, b.y};
+}
+
+// The 8-element operand of a 16x16x32 MFMA from two 4-element halves.  A
+// lane's 8 elements are 8 distinct positions of the summed (k) axis; which
+// positions does not matter as long as both operands use the same order, so
+// two 16x16x16 steps fold into one 16x16x32 step by concatenation.
+__device__ __forceinline__ f16x8 cat8(f16x4 a, f16x4 b)
+{
+    return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// D += A B over k = 32 (gfx950): the same output layout as 16x16x16 (lane
+// (col, grp) holds rows 4 grp .. 4 grp + 3 of column col).
+__device__ __forceinline__ f32x4 mfma32(f16x8 a, f16x8 b, f32x4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
 // Round to the nearest E4M3 value (ties to even), saturating to +-448; the
