@@ -379,6 +379,39 @@ KVQ_API kvq_status kvq_swap_in(const int32_t *block_slot_pairs, int32_t num_pair
                        void *k_pool, void *v_pool,
                        float *k_scale, float *v_scale, void *stream);
 
+/*
+ * kvq_paged_decode_noalloc -- kvq_paged_decode for callers that cannot
+ * allocate device memory: code recorded into a HIP graph, tight serving
+ * loops, harnesses that forbid hipMalloc.  Same arguments and result as
+ * kvq_paged_decode, without the workspace: the run plan and the partial
+ * results live in a static device array of KVQ_NOALLOC_SCRATCH_BYTES bytes
+ * that the library holds on every GPU it runs on until the process ends.
+ * The call allocates nothing (no hipMalloc, no hipFree).
+ *
+ * A call whose plan would need more scratch than that returns
+ * KVQ_ERR_WORKSPACE (kvq_paged_decode with a caller workspace has no such
+ * limit).  At split_tokens = 0 on a 256-CU GPU that holds any batch of up
+ * to a million sequences whose (query heads / KV heads) x head_dim is at
+ * most 512 (e.g. GQA 4:1 at head_dim 128); short fixed spans over large
+ * batches can exceed it.  Every call on one GPU
+ * shares that GPU's array: calls that may overlap on one GPU (different
+ * streams, or threads) race and give wrong results; order them.  The
+ * array's contents on entry never matter.
+ */
+#define KVQ_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+
+KVQ_API kvq_status kvq_paged_decode_noalloc(const void *q, const void *k_pool,
+                                    const void *v_pool, const float *k_scale,
+                                    const float *v_scale, const int32_t *block_tables,
+                                    int32_t max_blocks_per_seq,
+                                    const int32_t *context_lens,
+                                    int32_t max_context_len, int32_t num_seqs,
+                                    int32_t num_q_heads, int32_t num_kv_heads,
+                                    int32_t head_dim, int32_t block_size,
+                                    int32_t num_blocks, int32_t dtype,
+                                    int32_t group_size, float softmax_scale,
+                                    int32_t split_tokens, void *out, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

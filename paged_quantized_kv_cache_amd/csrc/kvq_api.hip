@@ -102,6 +102,27 @@ kvq_status launch_status()
     return hipGetLastError() == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
 }
 
+// ---------------------------------------------------------------- scratch
+// Device scratch of kvq_paged_decode_noalloc (the decode workspace of
+// callers that cannot allocate).  In host code `scratch` names a host-side
+// stand-in, not device memory: its address on a device comes from
+// hipGetSymbolAddress with that device current, once per device, and only
+// that address is ever passed to kernels.
+static __device__ __align__(256) uint8_t scratch[KVQ_NOALLOC_SCRATCH_BYTES];
+std::atomic<void *> g_scratch[kMaxDevices];
+
+// Device address of `scratch` on device dev (the current device), or null.
+void *scratch_address(int dev)
+{
+    void *ptr = g_scratch[dev].load(std::memory_order_acquire);
+    if (ptr)
+        return ptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr)
+        return nullptr;
+    g_scratch[dev].store(ptr, std::memory_order_release);
+    return ptr;
+}
+
 // ---------------------------------------------------------------- run plan
 // split_tokens == 0: balanced runs, one per wavefront the GPU holds at once
 // (compute units x resident wavefronts per CU for the kernel instance, capped
@@ -676,6 +697,30 @@ kvq_status kvq_paged_decode_heads(const void *q, const void *k_pool, const void 
                        kv_head_ids, pool_heads, head_dim, block_size, num_blocks, dtype,
                        group_size, softmax_scale, split_tokens, out, workspace,
                        workspace_bytes, stream);
+}
+
+kvq_status kvq_paged_decode_noalloc(const void *q, const void *k_pool, const void *v_pool,
+                                    const float *k_scale, const float *v_scale,
+                                    const int32_t *block_tables, int32_t max_blocks_per_seq,
+                                    const int32_t *context_lens, int32_t max_context_len,
+                                    int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                    int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                    int32_t dtype, int32_t group_size, float softmax_scale,
+                                    int32_t split_tokens, void *out, void *stream)
+{
+    int dev = 0;
+    const kvq_status st = check_device(&dev);
+    if (st != KVQ_OK)
+        return st;
+    void *ws = scratch_address(dev);
+    if (!ws)
+        return KVQ_ERR_HIP;
+    // the plan's exact need is checked against the array's size at launch
+    return decode_impl(q, k_pool, v_pool, k_scale, v_scale, block_tables, max_blocks_per_seq,
+                       context_lens, max_context_len, num_seqs, num_q_heads, num_kv_heads,
+                       nullptr, num_kv_heads, head_dim, block_size, num_blocks, dtype,
+                       group_size, softmax_scale, split_tokens, out, ws,
+                       KVQ_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 kvq_status kvq_paged_prefill(const void *q, const int32_t *query_start, int32_t max_query_len,

@@ -50,7 +50,8 @@ STATUS = {0: "KVQ_OK", -1: "KVQ_ERR_INVALID_ARG", -2: "KVQ_ERR_UNSUPPORTED",
 EXPORTS = ("kvq_status_string", "kvq_version", "kvq_cache_write",
            "kvq_paged_decode", "kvq_decode_workspace_size", "kvq_copy_blocks",
            "kvq_swap_block_bytes", "kvq_swap_out", "kvq_swap_in", "kvq_paged_prefill",
-           "kvq_prefill_workspace_size", "kvq_cache_write_heads", "kvq_paged_decode_heads")
+           "kvq_prefill_workspace_size", "kvq_cache_write_heads", "kvq_paged_decode_heads",
+           "kvq_paged_decode_noalloc")
 
 
 class KvqError(RuntimeError):
@@ -87,6 +88,10 @@ def lib() -> ctypes.CDLL:
                                            i32, i32, i32, i32, i32, i32, i32,
                                            ctypes.c_float, i32, P, P,
                                            ctypes.c_size_t, P]
+            L.kvq_paged_decode_noalloc.restype = i32
+            L.kvq_paged_decode_noalloc.argtypes = [P, P, P, P, P, P, i32, P, i32, i32,
+                                                   i32, i32, i32, i32, i32, i32, i32,
+                                                   ctypes.c_float, i32, P, P]
             L.kvq_cache_write_heads.restype = i32
             L.kvq_cache_write_heads.argtypes = [P, P, P, i32, i32, P, i32, i32, i32, i32,
                                                 i32, i32, P, P, P, P, P]
@@ -336,6 +341,38 @@ def kvq_paged_decode(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor
                                 split_tokens, _ptr(out), _ptr(workspace), ws_bytes,
                                 _stream(stream))
     _check(st, "kvq_paged_decode")
+    return out
+
+
+def kvq_paged_decode_noalloc(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
+                             k_scale: Optional[torch.Tensor], v_scale: Optional[torch.Tensor],
+                             block_tables: torch.Tensor, context_lens: torch.Tensor,
+                             max_context_len: int, fmt: str, out: torch.Tensor,
+                             group_size: int = 0, softmax_scale: float = 0.0,
+                             split_tokens: int = 0, stream=None) -> torch.Tensor:
+    """kvq_paged_decode without a workspace: the library's static device
+    scratch holds the plan and partials (see kvq.h; calls on one GPU must
+    not overlap).  ``out`` is required, so nothing is allocated here."""
+    num_blocks, hkv, bs, d = _pool_geometry(k_pool, fmt)
+    B, hq, dq = q.shape
+    if q.dtype != torch.float16 or dq != d:
+        raise ValueError("q must be float16 [B][Hq][%d]" % d)
+    if block_tables.dtype != torch.int32 or block_tables.dim() != 2 or block_tables.shape[0] != B:
+        raise ValueError("block_tables must be int32 [B][max_blocks]")
+    if context_lens.dtype != torch.int32 or context_lens.numel() != B:
+        raise ValueError("context_lens must be int32 [B]")
+    if out.shape != q.shape or out.dtype != torch.float16:
+        raise ValueError("out must be float16 shaped like q")
+    for t in (q, k_pool, v_pool, block_tables, context_lens, out):
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+    st = lib().kvq_paged_decode_noalloc(_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(k_scale),
+                                        _ptr(v_scale), _ptr(block_tables),
+                                        block_tables.shape[1], _ptr(context_lens),
+                                        max_context_len, B, hq, hkv, d, bs, num_blocks,
+                                        _fmt(fmt), group_size, softmax_scale, split_tokens,
+                                        _ptr(out), _stream(stream))
+    _check(st, "kvq_paged_decode_noalloc")
     return out
 
 
