@@ -19,7 +19,8 @@ tail; article 312, s3 and s6: under memory pressure a low-priority request
 is preempted, its KV swapped out and brought back later): every block keeps
 the step it was last read at (``touch``), ``preempt`` picks victims by
 priority and then by least recent use, and ``swap_out`` / ``swap_in`` move a
-sequence's blocks to host swap slots and back into freshly allocated blocks.
+sequence's private blocks to host swap slots and back into freshly allocated
+blocks, while the blocks it shares stay in the pool and come back shared.
 """
 from __future__ import annotations
 
@@ -70,7 +71,9 @@ class BlockManager:
         self._clock = 0
         self._blocks: Dict[int, List[int]] = {}
         self._len: Dict[int, int] = {}
-        self._swapped: Dict[int, List[int]] = {}         # seq -> swap slots
+        # swapped-out sequences: per logical block, (kept shared block, -1)
+        # or (-1, swap slot)
+        self._swapped: Dict[int, List[Tuple[int, int]]] = {}
 
     # ------------------------------------------------------------ sequences
     def add_sequence(self, seq: int) -> None:
@@ -81,9 +84,12 @@ class BlockManager:
 
     def drop_sequence(self, seq: int, space: Optional[SwapSpace] = None) -> None:
         if seq in self._swapped:
-            slots = self._swapped.pop(seq)
+            entries = self._swapped.pop(seq)
             if space is not None:
-                space.release(slots)
+                space.release([slot for kept, slot in entries if kept < 0])
+            for kept, _ in entries:
+                if kept >= 0:
+                    self._release(kept)
         else:
             for blk in self._blocks.pop(seq):
                 self._release(blk)
@@ -146,29 +152,54 @@ class BlockManager:
 
     def swap_out(self, seq: int, space: SwapSpace) -> List[Tuple[int, int]]:
         """Move ``seq`` to host swap slots.  Returns the (block, slot) pairs
-        to copy with ``kvq_swap_out``; its blocks are released at once, so
+        to copy with ``kvq_swap_out``; those blocks are released at once, so
         the copy must be issued before anything writes into them (same
-        stream order is enough).  Blocks still shared with resident
-        sequences stay in the pool for them."""
-        blocks = self._blocks.pop(seq)
-        slots = space.alloc(len(blocks))
+        stream order is enough).
+
+        Blocks that other sequences still hold (a shared prefix, a fork's
+        blocks) are neither copied nor released: shared blocks are never
+        written in place (copy-on-write), so the swapped-out sequence keeps
+        its reference and ``swap_in`` maps the same blocks again, still
+        shared.  If the swap space cannot take the private blocks, nothing
+        changes and PoolExhausted is raised."""
+        blocks = self._blocks[seq]
+        private = [b for b in blocks if self.refcount[b] == 1]
+        slots = iter(space.alloc(len(private)))      # raises before any change
+        del self._blocks[seq]
+        entries = []                                 # (kept block or -1, slot or -1)
+        pairs = []
         for blk in blocks:
-            self._release(blk)
-        self._swapped[seq] = slots
-        return list(zip(blocks, slots))
+            if self.refcount[blk] == 1:
+                slot = next(slots)
+                pairs.append((blk, slot))
+                entries.append((-1, slot))
+                self._release(blk)
+            else:
+                entries.append((blk, -1))
+        self._swapped[seq] = entries
+        return pairs
 
     def swap_in(self, seq: int, space: SwapSpace) -> List[Tuple[int, int]]:
-        """Bring ``seq`` back into freshly allocated blocks.  Returns the
-        (block, slot) pairs to copy with ``kvq_swap_in``; the slots are free
-        again once that copy has run."""
-        slots = self._swapped[seq]
-        if len(slots) > len(self._free):
+        """Bring ``seq`` back: its private blocks into freshly allocated ones
+        (the returned (block, slot) pairs, to copy with ``kvq_swap_in``; the
+        slots are free again once that copy has run), its shared blocks as
+        they were."""
+        entries = self._swapped[seq]
+        need = sum(1 for kept, _ in entries if kept < 0)
+        if need > len(self._free):
             raise PoolExhausted("not enough free KV blocks to swap in")
         del self._swapped[seq]
-        blocks = [self._alloc() for _ in slots]
+        blocks, pairs = [], []
+        for kept, slot in entries:
+            if kept >= 0:
+                blocks.append(kept)
+            else:
+                blk = self._alloc()
+                blocks.append(blk)
+                pairs.append((blk, slot))
         self._blocks[seq] = blocks
-        space.release(slots)
-        return list(zip(blocks, slots))
+        space.release([slot for _, slot in pairs])
+        return pairs
 
     def preempt(self, need_blocks: int, priority: Dict[int, int],
                 space: SwapSpace) -> List[Tuple[int, List[Tuple[int, int]]]]:

@@ -350,13 +350,54 @@ def test_block_lru_order_and_preemption():
     out = bm.preempt(free0 + 3, {0: 9, 1: 9, 2: 5, 3: 1}, space)
     assert [s for s, _ in out] == [3, 2]
     assert bm.num_free() == free0 + 3 and not bm.resident(2) and not bm.resident(3)
-    # preempting seq 1 alone frees nothing: its blocks are shared with seq 0
+    # swapping seq 1 out copies and frees nothing: its blocks are shared
+    # with seq 0, and it keeps its reference to them
     shared = bm.blocks(1)
-    pairs = bm.swap_out(1, space)
-    assert [b for b, _ in pairs] == shared and bm.num_free() == free0 + 3
-    assert all(bm.refcount[b] == 1 for b in shared)
+    slots0 = space.num_free()
+    assert bm.swap_out(1, space) == [] and bm.num_free() == free0 + 3
+    assert all(bm.refcount[b] == 2 for b in shared) and space.num_free() == slots0
+    # a preemption that runs out of swap slots leaves its victim resident
+    # with its blocks and reference counts unchanged
+    bm.add_sequence(4)
+    for _ in range(16 * 4):
+        bm.append_slot(4)                           # 4 private blocks
+    space.alloc(space.num_free() - 2)               # only 2 slots left
+    before = (bm.blocks(4), bm.refcount.copy(), bm.num_free(), space.num_free())
     with pytest.raises(PoolExhausted):
-        bm.preempt(100, {}, space)
+        bm.preempt(100, {0: 9, 4: 0}, space)
+    assert bm.resident(4) and bm.blocks(4) == before[0]
+    assert np.array_equal(bm.refcount, before[1])
+    assert bm.num_free() == before[2] and space.num_free() == before[3]
+
+
+def test_swap_keeps_prefix_sharing():
+    from paged_quantized_kv_cache_amd.block_manager import BlockManager, SwapSpace
+    bm, space = BlockManager(32, 16, rng=np.random.default_rng(5)), SwapSpace(16)
+    bm.add_sequence(0)
+    for _ in range(64):
+        bm.append_slot(0)                           # a 4-block prefix
+    for s in (1, 2):
+        bm.fork(0, s)
+        for _ in range(20 + 10 * s):
+            bm.append_slot(s)                       # private tails
+    prefix, tail = bm.blocks(1)[:4], bm.blocks(1)[4:]
+    pairs = bm.swap_out(1, space)
+    assert [b for b, _ in pairs] == tail            # only the private blocks move
+    assert all(bm.refcount[b] == 3 for b in prefix)
+    bm.drop_sequence(0)                             # another sharer leaves
+    for _ in range(40):
+        bm.append_slot(2)                           # and the pool is reused
+    back = bm.swap_in(1, space)
+    assert bm.blocks(1)[:4] == prefix               # the same shared blocks again
+    assert [b for b, _ in back] == bm.blocks(1)[4:]
+    assert [s for _, s in back] == [s for _, s in pairs]
+    assert all(bm.refcount[b] == 2 for b in prefix) and space.num_free() == 16
+    shared = bm.tables(3, mark_shared=True)[1, :4]
+    assert all((x >> 30) & 1 for x in shared)
+    # a swapped-out sequence that is dropped gives its slots and references back
+    bm.swap_out(1, space)
+    bm.drop_sequence(1, space)
+    assert all(bm.refcount[b] == 1 for b in prefix) and space.num_free() == 16
 
 
 def test_swap_round_trip_bookkeeping():
