@@ -7,7 +7,7 @@ the oracle attending in fp64 over contiguous dequantized K/V.
 
 Small cases run the whole batch through the oracle; they span several
 16-token tiles, ragged tails and forced splits.  Full-size workloads are
-checked on sampled sequences.
+checked on every sequence (test_gpu_fullsize.py).
 """
 import numpy as np
 import pytest
@@ -338,3 +338,47 @@ def test_validation_flag_checks_device_metadata(gpu, monkeypatch):
     with pytest.raises(ValueError, match="sequence 3: table entry 2"):
         case.decode(0)
     case.block_tables = good
+
+
+def test_one_workspace_reused_by_calls_of_different_shapes(gpu):
+    """A workspace's contents on entry never matter: back-to-back decode
+    calls of different batches and head shapes (one through the plan
+    kernel, over 1024 sequences) and short-chunk and virtual-sequence
+    prefill calls share one workspace, each finding the previous call's
+    plan and partials in it; each result equals the same call on a fresh
+    workspace bit for bit and stays within tolerance of the oracle."""
+    big = small("c2_mha", B=1100, Hq=8, Hkv=2, D=64, G=64, lens="uniform", lens_args=(1, 90))
+    names = ["gqa_int8_g64_outliers", "mha_int8_g128", "c1_tiny", "fp8_bs32", "gqa_fp16"]
+    cases = [_build(SMALL_CASES[n], gpu) for n in names] + [_build(big, gpu)]
+    calls = []
+    for case in cases:
+        calls.append(("decode", case, None))
+    r4 = cases[0]                                   # Hq 8 / Hkv 2: r = 4
+    calls.append(("prefill", r4, np.minimum(r4.lens, [4, 1, 3, 0, 2])))      # short chunks
+    calls.append(("prefill", r4, np.minimum(r4.lens, [37, 9, 40, 20, 33])))  # virtual sequences
+    need = 0
+    for kind, case, n in calls:
+        s = case.spec
+        if kind == "decode":
+            need = max(need, kvq.kvq_decode_workspace_size(s.B, s.Hq, s.Hkv, s.D, s.BS,
+                                                           case.max_context_len, 0))
+        else:
+            need = max(need, kvq.kvq_prefill_workspace_size(s.B, s.Hq, s.Hkv, s.D, s.BS,
+                                                            case.max_context_len,
+                                                            int(n.max()), "split"))
+    shared = kvq.alloc_workspace(need, gpu)
+    for kind, case, n in calls:
+        print(kind, case.spec.name, case.spec.B, flush=True)
+        if kind == "decode":
+            got = case.decode(0, workspace=shared)
+            fresh = case.decode(0, workspace=case.workspace(0))
+            _, _, _, ref = _expected(case, 0)
+        else:
+            q = case.chunk_queries(n)
+            got = case.prefill_attention(0, n, q, workspace=shared, split_mode="split")
+            fresh = case.prefill_attention(0, n, q, split_mode="split")
+            kq, vq, toks, _ = _expected(case, 0)
+            ref = E.prefill(q.cpu().numpy(), kq, vq, toks, n)
+        torch.cuda.synchronize()
+        assert torch.equal(got.view(torch.int16), fresh.view(torch.int16)), kind
+        _check_out(_host(got).astype(np.float64), ref, "%s %s" % (kind, case.spec.name))
