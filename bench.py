@@ -10,7 +10,14 @@ Prints one JSON line.  `value` is seq-steps/s (sequences x steps / second).
 `roofline` prices the decode kernel (the dominant one) against MI355X HBM
 bandwidth using algorithmic bytes (every valid cached K/V code and scale
 once, plus q, out, table entries and lengths) over its event-timed duration.
-`cpu_baseline` times the CPU oracle on a bounded sample of the same workload.
+`cpu_baseline` times the CPU oracle on a bounded sample of the same workload
+(one step's work: quantize the appended tokens, fp64 attention over the
+dequantized cache).  With the default workload the line also carries
+`workloads` (the other decode configurations -- the MHA layer, the long
+FP8 contexts with 16- and 32-token blocks, the 32-layer prefix-sharing
+step -- timed the same way over fewer steps), `cache_write_us` (the
+append's event time) and `reconstruction_error` (the format's error
+against the fp16 data, from the oracle).
 """
 from __future__ import annotations
 
@@ -48,10 +55,14 @@ def load_traffic(workload: str):
     return t.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(case, layer_inputs, spec, max_seqs: int, min_seconds: float = 10.0):
-    """Time the oracle (as it stands) on the first `max_seqs` sequences of the
-    workload: quantize their appended tokens, dequantize their cached K/V and
-    attend in fp64."""
+def cpu_baseline(case, spec, max_seqs: int, layer: int = 0, passes: int = 3):
+    """Time the oracle (as it stands) doing one decode step's work for the
+    first `max_seqs` sequences of one layer, like the GPU step: quantize each
+    sequence's appended token, then fp64 attention over its cached K/V.  The
+    cache itself is state, as the GPU's pool is: every cached token is
+    quantized, dequantized and laid out contiguously per sequence (the form
+    the oracle reads) once, before timing.  Median of `passes` passes, on all
+    the oracle's threads and, for the first 16 sequences, on one."""
     import numpy as np
     import torch
 
@@ -59,75 +70,108 @@ def cpu_baseline(case, layer_inputs, spec, max_seqs: int, min_seconds: float = 1
     from oracle import expected as E
     from paged_quantized_kv_cache_amd import kvq
 
-    layers = [0] if spec.layers == 1 else list(range(spec.layers))
     nseq = min(max_seqs, spec.B)
-    seqs = list(range(nseq))
-    total = 0.0
-    ntok = 0
-    passes = 0
-    for layer in layers:
-        d = case.data[layer] if case.data[layer] is not None else case.gen(layer)
-        ids = np.unique(np.concatenate([case.layout.seq_tokens[b] for b in seqs]))
-        remap = np.full(case.layout.n_unique, -1, np.int64)
-        remap[ids] = np.arange(ids.size)
-        k16 = d.k[torch.from_numpy(ids).to(d.k.device)].cpu().numpy()
-        v16 = d.v[torch.from_numpy(ids).to(d.v.device)].cpu().numpy()
-        q = d.q[:nseq].cpu().numpy()
-        fmt = spec.fmt_of_layer(layer)
-        sk = sv = None
-        if kvq.scale_mode(fmt, spec.G) in ("head", "channel"):   # static scales
-            sk = case.pools[layer].k_scale.cpu().numpy()
-            sv = case.pools[layer].v_scale.cpu().numpy()
-        toks = [remap[case.layout.seq_tokens[b]] for b in seqs]
+    d = case.data[layer] if case.data[layer] is not None else case.gen(layer)
+    fmt = spec.fmt_of_layer(layer)
+    sk = sv = None
+    if kvq.scale_mode(fmt, spec.G) in ("head", "channel"):   # static scales
+        sk = case.pools[layer].k_scale.cpu().numpy()
+        sv = case.pools[layer].v_scale.cpu().numpy()
+    toks = [np.asarray(case.layout.seq_tokens[b], np.int64) for b in range(nseq)]
+    lens = np.array([t.size for t in toks], np.int64)
+    idx = np.concatenate(toks)
+    ids = np.unique(idx)
+    remap = np.full(case.layout.n_unique, -1, np.int64)
+    remap[ids] = np.arange(ids.size)
+    tdev = torch.from_numpy(ids).to(d.k.device)
+    k16 = d.k.index_select(0, tdev).cpu().numpy()
+    v16 = d.v.index_select(0, tdev).cpu().numpy()
+    q = d.q[:nseq].cpu().numpy()
+    # state: the dequantized cache, contiguous per sequence
+    K = E.quantize(k16, fmt, spec.G, sk).deq[remap[idx]]
+    V = E.quantize(v16, fmt, spec.G, sv).deq[remap[idx]]
+    last = np.cumsum(lens) - 1                       # each sequence's appended token
+    ka, va = k16[remap[idx[last]]], v16[remap[idx[last]]]
+
+    def step(n):
+        kq = E.quantize(ka[:n], fmt, spec.G, sk)     # the appended tokens
+        vq = E.quantize(va[:n], fmt, spec.G, sv)
+        K[last[:n]] = kq.deq
+        V[last[:n]] = vq.deq
+        oracle.decode_attention(q[:n], K[:last[n - 1] + 1], V[:last[n - 1] + 1], lens[:n])
+
+    times = []
+    for _ in range(passes):
         t0 = time.perf_counter()
-        kq = E.quantize(k16, fmt, spec.G, sk)
-        vq = E.quantize(v16, fmt, spec.G, sv)
-        E.attention(q, kq, vq, toks)
-        total += time.perf_counter() - t0
-        ntok += int(sum(len(t) for t in toks))
-        if spec.layers > 1:
-            case.data[layer] = None
-    passes = 1
-    if spec.layers == 1:
-        # repeat the same sample until about min_seconds of CPU work
-        while total < min_seconds and passes < 20:
-            t0 = time.perf_counter()
-            kq = E.quantize(k16, fmt, spec.G, sk)
-            vq = E.quantize(v16, fmt, spec.G, sv)
-            E.attention(q, kq, vq, toks)
-            total += time.perf_counter() - t0
-            passes += 1
+        step(nseq)
+        times.append(time.perf_counter() - t0)
     cores = oracle.num_threads()
-    single = None
-    if spec.layers == 1:
-        # the same work on one thread, on the first sequences of the sample
-        n1 = min(16, nseq)
-        sub = np.unique(np.concatenate(toks[:n1]))
-        remap1 = np.full(int(sub.max()) + 1, -1, np.int64)
-        remap1[sub] = np.arange(sub.size)
-        k1, v1 = k16[sub], v16[sub]
-        toks1 = [remap1[t] for t in toks[:n1]]
-        oracle.set_num_threads(1)
-        try:
+    n1 = min(16, nseq)
+    oracle.set_num_threads(1)
+    try:
+        t1 = []
+        for _ in range(passes):
             t0 = time.perf_counter()
-            kq = E.quantize(k1, fmt, spec.G, sk)
-            vq = E.quantize(v1, fmt, spec.G, sv)
-            E.attention(q[:n1], kq, vq, toks1)
-            single = n1 / (time.perf_counter() - t0)
-        finally:
-            oracle.set_num_threads(cores)
+            step(n1)
+            t1.append(time.perf_counter() - t0)
+    finally:
+        oracle.set_num_threads(cores)
+    med = float(np.median(times))
     return {
-        "value": nseq * passes / total,
+        "value": nseq / med,
         "unit": "seq-steps/s",
         "cores": cores,
         "kind": "oracle",
-        "sample": "first %d of %d sequences (%d cached tokens per layer-pass, %d layer(s)): "
-                  "quantize every cached and appended token, dequantize, fp64 attention; "
-                  "%d pass(es), %.1f s" % (nseq, spec.B, ntok // len(layers), len(layers),
-                                           passes, total),
-        "single_thread_value": single,
+        "sample": "first %d of %d sequences of layer %d (%d cached tokens): quantize the "
+                  "appended tokens, fp64 attention over the dequantized cache (built once, "
+                  "untimed); median of %d passes, %.2f s each"
+                  % (nseq, spec.B, layer, int(lens.sum()), passes, med),
+        "single_thread_value": n1 / float(np.median(t1)),
         "cpu_model": cpu_model(),
     }
+
+
+def recon_error_summary(case, spec, layer: int = 0, ntok: int = 4096, nseq: int = 4) -> dict:
+    """Reconstruction error of the layer's format on its own data, from the
+    oracle (reported beside the parity check, not gated): K / V max-abs and
+    RMSE of x - x_hat over the first `ntok` tokens, and the decode output of
+    the first `nseq` sequences over the original fp16 K/V against the output
+    over the dequantized K/V (both fp64)."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from oracle import expected as E
+    from paged_quantized_kv_cache_amd import kvq
+
+    d = case.data[layer] if case.data[layer] is not None else case.gen(layer)
+    fmt = spec.fmt_of_layer(layer)
+    st = {}
+    if kvq.scale_mode(fmt, spec.G) in ("head", "channel"):
+        st = {"k": case.pools[layer].k_scale.cpu().numpy(),
+              "v": case.pools[layer].v_scale.cpu().numpy()}
+    out = {"format": fmt, "group_size": spec.G, "tokens": ntok}
+    for which, x in (("k", d.k), ("v", d.v)):
+        x16 = x[:ntok].cpu().numpy()
+        err = E.quantize(x16, fmt, spec.G, st.get(which)).deq - oracle.f16_to_f64(x16)
+        out[which + "_max_abs"] = float(np.abs(err).max())
+        out[which + "_rmse"] = float(np.sqrt(np.mean(err ** 2)))
+    toks = [np.asarray(case.layout.seq_tokens[b], np.int64) for b in range(nseq)]
+    ids = np.unique(np.concatenate(toks))
+    remap = np.full(case.layout.n_unique, -1, np.int64)
+    remap[ids] = np.arange(ids.size)
+    tdev = torch.from_numpy(ids).to(d.k.device)
+    k16 = d.k.index_select(0, tdev).cpu().numpy()
+    v16 = d.v.index_select(0, tdev).cpu().numpy()
+    q = d.q[:nseq].cpu().numpy()
+    lt = [remap[t] for t in toks]
+    ref = E.attention(q, E.quantize(k16, "fp16"), E.quantize(v16, "fp16"), lt)
+    got = E.attention(q, E.quantize(k16, fmt, spec.G, st.get("k")),
+                      E.quantize(v16, fmt, spec.G, st.get("v")), lt)
+    out["attn_seqs"] = nseq
+    out["attn_max_abs"] = float(np.abs(got - ref).max())
+    out["attn_rel"] = float(np.abs(got - ref).max() / np.abs(ref).max())
+    return out
 
 
 def cpu_model() -> str:
@@ -139,22 +183,6 @@ def cpu_model() -> str:
     except OSError:
         pass
     return "unknown"
-
-
-def copy_bandwidth(nbytes: int = 2 << 30, reps: int = 5) -> float:
-    """Measured streaming copy (torch) bandwidth, read + write bytes / time."""
-    import torch
-    a = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
-    b = torch.empty_like(a)
-    b.copy_(a)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(reps):
-        b.copy_(a)
-    torch.cuda.synchronize()
-    dt = (time.perf_counter() - t0) / reps
-    del a, b
-    return 2 * nbytes / dt / 1e9
 
 
 def swap_bandwidth(case, spec, reps: int = 3) -> dict:
@@ -494,6 +522,160 @@ def run_prefill(args, spec) -> int:
     return 0
 
 
+EXTRA_WORKLOADS = ("c2_mha", "c4_long_bs16", "c4_long_bs32", "c5_prefix_mixed")
+
+
+def decode_bench(spec, steps: int, warmup: int, kv_copies: int = 4, flush_bytes: int = 0,
+                 flush_mode: str = "read") -> dict:
+    """Build a decode workload in HBM and time `steps` steps after `warmup`
+    untimed ones.  A step, for every layer: the one-token append
+    (kvq_cache_write) and the decode call (kvq_paged_decode), each between
+    HIP events on the stream they run on."""
+    import dataclasses
+
+    import numpy as np
+    import torch
+
+    from paged_quantized_kv_cache_amd import workloads as W
+    from paged_quantized_kv_cache_amd.harness import DecodeCase
+
+    dev = torch.device("cuda:0")
+    t_setup = time.perf_counter()
+    # A single-layer workload keeps `copies` independent caches of its layer
+    # (the per-layer draws of the same recipe) and step i runs on copy
+    # i % copies: consecutive steps touch different K/V, as consecutive layers
+    # of a model do, so no step reads what the previous one left in the
+    # 256 MB last-level cache.  (Back to back on one cache, C3 ran ~3.5 %
+    # faster than with a 2 GiB read between steps.)
+    copies = max(1, kv_copies) if spec.layers == 1 else 1
+    case_spec = dataclasses.replace(spec, layers=copies) if copies > 1 else spec
+    case = DecodeCase(case_spec, device=dev, poison=False)
+    inputs = []
+    for layer in range(case_spec.layers):
+        # prefill every cached token of the layer (untimed), keep only what a
+        # decode step needs: the appended tokens' K/V and the queries
+        case.gen(layer)
+        case.alloc(layer)
+        case.prefill(layer)
+        case.cow(layer)
+        k, v = case.append_inputs(layer)
+        q = case.data[layer].q.contiguous()
+        case.append(layer, (k, v))
+        if layer != (1 if spec.layers > 1 else 0):   # keep one layer's data (CPU leg)
+            case.data[layer] = None
+        inputs.append((k, v, q, torch.empty_like(q)))
+    ws = case.workspace(0)
+    torch.cuda.synchronize()
+    setup_s = time.perf_counter() - t_setup
+    print("setup %.1fs: %s, %d seqs, %d cached tokens, pool %d blocks" %
+          (setup_s, spec.name, spec.B, int(case.lens.sum()), case.layout.num_blocks),
+          file=sys.stderr, flush=True)
+
+    stream = torch.cuda.current_stream()
+    nl = spec.layers
+    # optional: stream flush_bytes through a scratch copy before every step
+    # (outside the decode events) so that no K/V can be served from the
+    # last-level cache left by the previous step; a check of that effect,
+    # not the default (the wall-clock step time then includes the copies)
+    flush = None
+    if flush_bytes:
+        flush = (torch.empty(flush_bytes, dtype=torch.uint8, device=dev),
+                 torch.empty(flush_bytes, dtype=torch.uint8, device=dev))
+        flush[0].fill_(1)
+
+    def step(i, events=None):
+        if flush is not None:
+            if flush_mode == "copy":
+                flush[1].copy_(flush[0])
+            else:  # read only: no dirty lines left behind
+                torch.amax(flush[0])
+        for li in range(nl):
+            layer = i % copies if copies > 1 else li
+            k, v, q, out = inputs[layer]
+            if events is not None:
+                events[li][0].record(stream)
+            case.append(layer, (k, v))
+            if events is not None:
+                events[li][1].record(stream)
+            case.decode(layer, q=q, out=out, workspace=ws)
+            if events is not None:
+                events[li][2].record(stream)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    # timed region: exactly `steps` steps, synchronized on both sides
+    ev = [[tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(nl)]
+          for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(warmup + i, ev[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    dec_ms = np.array([[ev[i][l][1].elapsed_time(ev[i][l][2]) for l in range(nl)]
+                       for i in range(steps)])
+    wr_ms = np.array([[ev[i][l][0].elapsed_time(ev[i][l][1]) for l in range(nl)]
+                      for i in range(steps)])
+    per_layer_ms = dec_ms.mean(0)
+    fmts = [spec.fmt_of_layer(l) for l in range(nl)]
+    uniq = case.layout.n_unique if spec.shared_prefix else None  # shared blocks once
+    layer_bytes = [W.algorithmic_bytes(spec, case.lens, f, unique_tokens=uniq) for f in fmts]
+    logical_bytes = [W.algorithmic_bytes(spec, case.lens, f) for f in fmts]
+    # dominant kernel: the INT8 decode (all layers of that format)
+    dom = [l for l in range(nl) if fmts[l] == "int8"] or list(range(nl))
+    dom_ms = float(np.mean(per_layer_ms[dom]))
+    dom_bytes = float(np.mean([layer_bytes[l] for l in dom]))
+    all_layers = None
+    if nl > 1 or spec.shared_prefix:
+        # whole step, every layer's decode call: unique bytes (shared blocks
+        # once) and logical bytes (every sequence's own reads)
+        tot = float(per_layer_ms.sum())
+        all_layers = {
+            "ms": round(tot, 5),
+            "unique_bytes": int(sum(layer_bytes)),
+            "unique_GBps": round(sum(layer_bytes) / (tot * 1e-3) / 1e9, 1),
+            "logical_bytes": int(sum(logical_bytes)),
+            "logical_GBps": round(sum(logical_bytes) / (tot * 1e-3) / 1e9, 1),
+            "full_model_seq_steps_per_s": round(spec.B / (tot * 1e-3), 1),
+        }
+    return {
+        "case": case, "copies": copies, "fmts": fmts, "setup_s": round(setup_s, 1),
+        "ms_per_step": wall * 1e3 / steps, "per_layer_ms": per_layer_ms,
+        "dom_ms": dom_ms, "dom_bytes": dom_bytes,
+        "achieved": dom_bytes / (dom_ms * 1e-3) / 1e9,
+        "p10_p50_p90": [round(float(x), 5) for x in
+                        np.percentile(dec_ms[:, dom].ravel(), [10, 50, 90])],
+        "write_us": round(float(wr_ms.mean()) * 1e3, 2),
+        "all_layers": all_layers,
+    }
+
+
+def summarize(spec, r: dict) -> dict:
+    """The figures of one extra workload for the bench line."""
+    import numpy as np
+    fmt = "int8" if "int8" in r["fmts"] else r["fmts"][0]
+    out = {
+        "format": fmt if spec.layers == 1 else "mixed (%s dominant)" % fmt,
+        "decode_call_ms": round(r["dom_ms"], 5),
+        "algorithmic_bytes_per_call": int(r["dom_bytes"]),
+        "achieved_GBps": round(r["achieved"], 1),
+        "frac_of_peak": round(r["achieved"] / HBM_PEAK_GBPS, 4),
+        "decode_ms_p10_p50_p90": r["p10_p50_p90"],
+        "cache_write_us": r["write_us"],
+        "ms_per_step": round(r["ms_per_step"], 5),
+        "seq_steps_per_s": round(spec.B / (r["ms_per_step"] * 1e-3), 1),
+    }
+    if r["all_layers"] is not None:
+        out["decode_all_layers"] = r["all_layers"]
+        out["fp16_layer_call_ms"] = (round(float(np.mean([r["per_layer_ms"][l]
+                                                          for l, f in enumerate(r["fmts"])
+                                                          if f == "fp16"])), 5)
+                                     if "fp16" in r["fmts"] else None)
+    return out
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -515,6 +697,12 @@ def main(argv=None) -> int:
                     help="read the flush buffer, or copy it (which also leaves dirty lines)")
     ap.add_argument("--copy-calib-bytes", type=int, default=0,
                     help="also run one plain copy of this many bytes (counter calibration)")
+    ap.add_argument("--no-extras", dest="extras", action="store_false",
+                    help="default workload only: skip the other decode workloads (C2, C4 "
+                         "bs16 / bs32, the 32-layer prefix-sharing step), timed after it "
+                         "over fewer steps")
+    ap.add_argument("--no-recon", dest="recon", action="store_false",
+                    help="skip the reconstruction-error summary (oracle, CPU)")
     ap.add_argument("--swap", action="store_true",
                     help="also time swapping layer 0's blocks out to pinned host "
                          "memory and back (kvq_swap_out / kvq_swap_in), outside the "
@@ -542,116 +730,27 @@ def main(argv=None) -> int:
         return run_prefill(args, spec)
     if spec.fp16_heads:
         return run_mixed_heads(args, spec)
-    t_setup = time.perf_counter()
-    # A single-layer workload keeps `copies` independent caches of its layer
-    # (the per-layer draws of the same recipe) and step i runs on copy
-    # i % copies: consecutive steps touch different K/V, as consecutive layers
-    # of a model do, so no step reads what the previous one left in the
-    # 256 MB last-level cache.  (Back to back on one cache, C3 ran ~3.5 %
-    # faster than with a 2 GiB read between steps.)
-    copies = max(1, args.kv_copies) if spec.layers == 1 else 1
-    import dataclasses
-    case_spec = dataclasses.replace(spec, layers=copies) if copies > 1 else spec
-    case = DecodeCase(case_spec, device=dev, poison=False)
-    inputs = []
-    for layer in range(case_spec.layers):
-        # prefill every cached token of the layer (untimed), keep only what a
-        # decode step needs: the appended tokens' K/V and the queries
-        case.gen(layer)
-        case.alloc(layer)
-        case.prefill(layer)
-        case.cow(layer)
-        k, v = case.append_inputs(layer)
-        q = case.data[layer].q.contiguous()
-        case.append(layer, (k, v))
-        if layer > 0 or spec.layers > 1:   # (copy 0's data feeds the CPU baseline)
-            case.data[layer] = None
-        inputs.append((k, v, q, torch.empty_like(q)))
-    ws = case.workspace(0)
-    torch.cuda.synchronize()
-    setup_s = time.perf_counter() - t_setup
-    print("setup %.1fs: %s, %d seqs, %d cached tokens, pool %d blocks" %
-          (setup_s, spec.name, spec.B, int(case.lens.sum()), case.layout.num_blocks),
-          file=sys.stderr, flush=True)
-
-    stream = torch.cuda.current_stream()
+    res = decode_bench(spec, args.steps, args.warmup, args.kv_copies, args.flush_bytes,
+                       args.flush_mode)
+    case = res["case"]
     nl = spec.layers
-
-    # optional: stream flush_bytes through a scratch copy before every step
-    # (outside the decode events) so that no K/V can be served from the
-    # last-level cache left by the previous step; a check of that effect,
-    # not the default (the wall-clock step time then includes the copies)
-    flush = None
-    if args.flush_bytes:
-        flush = (torch.empty(args.flush_bytes, dtype=torch.uint8, device=dev),
-                 torch.empty(args.flush_bytes, dtype=torch.uint8, device=dev))
-        flush[0].fill_(1)
-
-    def step(i, events=None):
-        if flush is not None:
-            if args.flush_mode == "copy":
-                flush[1].copy_(flush[0])
-            else:  # read only: no dirty lines left behind
-                torch.amax(flush[0])
-        for li in range(nl):
-            layer = i % copies if copies > 1 else li
-            k, v, q, out = inputs[layer]
-            case.append(layer, (k, v))
-            if events is not None:
-                events[li][0].record(stream)
-            case.decode(layer, q=q, out=out, workspace=ws)
-            if events is not None:
-                events[li][1].record(stream)
-
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-
-    # timed region: exactly `steps` steps, synchronized on both sides
-    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(nl)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(args.warmup + i, ev[i])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_per_step = wall * 1e3 / args.steps
-
-    # decode kernel durations (one launch per layer per step)
-    dec_ms = np.array([[ev[i][l][0].elapsed_time(ev[i][l][1]) for l in range(nl)]
-                       for i in range(args.steps)])
-    per_layer_ms = dec_ms.mean(0)
-    fmts = [spec.fmt_of_layer(l) for l in range(nl)]
-    uniq = None
-    if spec.shared_prefix:
-        uniq = case.layout.n_unique  # shared blocks counted once
-    layer_bytes = [W.algorithmic_bytes(spec, case.lens, f, unique_tokens=uniq) for f in fmts]
-    logical_bytes = [W.algorithmic_bytes(spec, case.lens, f) for f in fmts]
-    # dominant kernel: the INT8 decode (all layers of that format)
-    dom = [l for l in range(nl) if fmts[l] == "int8"] or list(range(nl))
-    dom_ms = float(np.mean(per_layer_ms[dom]))
-    dom_bytes = float(np.mean([layer_bytes[l] for l in dom]))
-    achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
+    fmts = res["fmts"]
     traffic = load_traffic(spec.name)
-
     swap = swap_bandwidth(case, spec) if args.swap else None
-    copy_gbps = copy_bandwidth()
     if args.copy_calib_bytes:
         a = torch.zeros(args.copy_calib_bytes, dtype=torch.uint8, device=dev)
         b = torch.empty_like(a)
         b.copy_(a)
         torch.cuda.synchronize()
         del a, b
-
     result = {
         "metric": METRIC,
-        "value": spec.B / (ms_per_step * 1e-3),
+        "value": spec.B / (res["ms_per_step"] * 1e-3),
         "unit": "seq-steps/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms_per_step,
+        "ms_per_step": res["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -668,47 +767,56 @@ def main(argv=None) -> int:
             "mean_context": float(case.lens.mean()),
             "max_context": int(case.lens.max()),
             "partition": "balanced runs over the GPU's resident wavefronts",
-            "kv_copies": copies,
+            "kv_copies": res["copies"],
         },
         "roofline": {
             "bound": "hbm",
-            "achieved": round(achieved, 1),
+            "achieved": round(res["achieved"], 1),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "frac": round(res["achieved"] / HBM_PEAK_GBPS, 4),
             "traffic": traffic,
             "kernel": "kvq_paged_decode call: paged_decode_kernel + merge_runs_kernel (%s)"
                       % ("int8" if "int8" in fmts else fmts[0]),
-            "algorithmic_bytes_per_launch": int(dom_bytes),
-            "avg_launch_ms": round(dom_ms, 5),
+            "algorithmic_bytes_per_launch": int(res["dom_bytes"]),
+            "avg_launch_ms": round(res["dom_ms"], 5),
         },
-        "decode_ms_per_layer": [round(float(x), 5) for x in per_layer_ms] if nl > 1 else None,
-        # whole step, every layer's decode call: unique bytes (shared blocks
-        # once) and logical bytes (every sequence's own reads)
-        "decode_all_layers": {
-            "ms": round(float(per_layer_ms.sum()), 5),
-            "unique_bytes": int(sum(layer_bytes)),
-            "unique_GBps": round(sum(layer_bytes) / (per_layer_ms.sum() * 1e-3) / 1e9, 1),
-            "logical_bytes": int(sum(logical_bytes)),
-            "logical_GBps": round(sum(logical_bytes) / (per_layer_ms.sum() * 1e-3) / 1e9, 1),
-        } if nl > 1 or spec.shared_prefix else None,
+        "decode_ms_per_layer": ([round(float(x), 5) for x in res["per_layer_ms"]]
+                                if nl > 1 else None),
+        "decode_all_layers": res["all_layers"],
         # spread of the timed calls of the dominant format (event times)
-        "decode_ms_p10_p50_p90": [round(float(x), 5) for x in
-                                  np.percentile(dec_ms[:, dom].ravel(), [10, 50, 90])],
-        "measured_copy_gbps": round(copy_gbps, 1),
+        "decode_ms_p10_p50_p90": res["p10_p50_p90"],
+        "cache_write_us": res["write_us"],
         "flush_bytes_between_steps": args.flush_bytes,
         "flush_mode": args.flush_mode if args.flush_bytes else None,
         "swap": swap,
-        "setup_s": round(setup_s, 1),
+        "setup_s": res["setup_s"],
     }
     if args.cpu_seqs > 0:
-        result["cpu_baseline"] = cpu_baseline(case, inputs, spec, args.cpu_seqs,
-                                              args.cpu_min_seconds)
+        result["cpu_baseline"] = cpu_baseline(case, spec, args.cpu_seqs,
+                                              layer=1 if nl > 1 else 0)
     else:
         result["cpu_baseline"] = None
+    if args.recon:
+        result["reconstruction_error"] = recon_error_summary(case, spec,
+                                                             layer=1 if nl > 1 else 0)
+    del case, res
+    import gc
+    gc.collect()
+    torch.cuda.empty_cache()
+    # the other decode workloads, timed the same way over fewer steps
+    if args.extras and spec.name == DEFAULT_WORKLOAD:
+        extra = {}
+        for name in EXTRA_WORKLOADS:
+            r = decode_bench(W.spec(name), max(1, min(args.steps, 10)),
+                             max(1, min(args.warmup, 3)), args.kv_copies)
+            extra[name] = summarize(W.spec(name), r)
+            del r
+            gc.collect()
+            torch.cuda.empty_cache()
+        result["workloads"] = extra
     print(json.dumps(result), flush=True)
     return 0
-
 
 if __name__ == "__main__":
     sys.exit(main())
