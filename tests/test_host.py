@@ -485,3 +485,24 @@ def test_bench_refuses_more_than_one_gpu(capsys):
     import bench
     assert bench.main(["--gpus", "2"]) == 2
     assert "one GPU" in capsys.readouterr().err
+
+
+def test_generated_inputs_match_their_fingerprints():
+    """The seeded inputs of every workload (lengths, block tables, the first
+    4,096 tokens' K / V and the queries of layer 0, drawn on the CPU) hash
+    to the values stored in tests/golden/input_fingerprints.txt: a change of
+    the recipe or of the random streams it uses fails here."""
+    import importlib.util
+    path = os.path.join(ROOT, "tests", "golden", "make_input_fingerprints.py")
+    spec = importlib.util.spec_from_file_location("make_input_fingerprints", path)
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    stored = {}
+    with open(os.path.join(ROOT, "tests", "golden", "input_fingerprints.txt")) as f:
+        for line in f:
+            if line.strip() and not line.startswith("#"):
+                p = line.split()
+                stored[p[0]] = dict(zip(("lens", "tables", "k", "v", "q"), p[1:]))
+    assert set(stored) == set(W.SPECS)
+    for name in sorted(W.SPECS):
+        assert mod.fingerprints(name) == stored[name], name
