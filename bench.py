@@ -513,7 +513,7 @@ def run_prefill(args, spec) -> int:
         "roofline": {"bound": "mfma", "achieved": round(achieved, 1),
                      "peak": MFMA_FP16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / MFMA_FP16_PEAK_TFLOPS, 4), "traffic": None,
-                     "kernel": "kvq_paged_prefill: paged_decode_kernel<prefill> (%s)" % spec.fmt,
+                     "kernel": "kvq_paged_prefill: prefill_kernel (%s)" % spec.fmt,
                      "flops_per_launch": flops, "avg_launch_ms": round(att_ms, 5)},
         "cpu_baseline": (prefill_cpu_baseline(case, spec, q, chunk, args.cpu_min_seconds)
                          if args.cpu_seqs > 0 else None),

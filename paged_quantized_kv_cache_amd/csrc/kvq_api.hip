@@ -14,6 +14,7 @@
 #include "kvq.h"
 #include "kvq_decode.hpp"
 #include "kvq_device.hpp"
+#include "kvq_prefill.hpp"
 #include "kvq_write.hpp"
 
 namespace {
@@ -236,7 +237,7 @@ int waves_per_cu()
     if (v == 0) {
         int n = 0;
         const void *kernel =
-            reinterpret_cast<const void *>(&paged_decode_kernel<FMT, D, BS, NG, false, QG>);
+            reinterpret_cast<const void *>(&paged_decode_kernel<FMT, D, BS, NG, QG>);
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, 64, 0) != hipSuccess ||
             n <= 0)
             n = 4;
@@ -287,7 +288,7 @@ kvq_status launch_decode(DecodeParams p, const LaunchPlan &lp, hipStream_t s)
     pp.span_tiles = lp.split_tokens / 16;
     if (!p.inline_plan)
         hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, pp);
-    hipLaunchKernelGGL((paged_decode_kernel<FMT, D, BS, NG, false, QG>), dim3((unsigned)runs),
+    hipLaunchKernelGGL((paged_decode_kernel<FMT, D, BS, NG, QG>), dim3((unsigned)runs),
                        dim3(64), 0, s, p);
     if (runs > 1)
         hipLaunchKernelGGL((merge_runs_kernel<D>),
@@ -297,21 +298,21 @@ kvq_status launch_decode(DecodeParams p, const LaunchPlan &lp, hipStream_t s)
     return launch_status();
 }
 
-// Chunked prefill: one wavefront per (kPrefillGroups chunk-token groups,
-// sequence, KV head).
+// Chunked prefill (the walk): one workgroup of kPfWaves wavefronts per
+// (sequence, KV head, block of 128 / r chunk tokens); p.groups query blocks
+// per pair.
 template <int FMT, int D, int BS, int NG>
 kvq_status launch_prefill(const DecodeParams &p, hipStream_t s)
 {
-    // wavefronts per (sequence, KV head) pair, times the pairs rounded up to
-    // the 8 XCDs (see the kernel)
-    const int64_t grid = (int64_t)((p.groups + kPrefillGroups - 1) / kPrefillGroups) *
-                         (((int64_t)p.B * p.Hkv + 7) / 8 * 8);
+    // query blocks per (sequence, KV head) pair, times the pairs rounded up
+    // to the 8 XCDs (see the kernel)
+    const int64_t grid = (int64_t)p.groups * (((int64_t)p.B * p.Hkv + 7) / 8 * 8);
     if (grid > (int64_t)INT32_MAX)
         return KVQ_ERR_UNSUPPORTED;
     if (grid == 0)
         return KVQ_OK;
-    hipLaunchKernelGGL((paged_decode_kernel<FMT, D, BS, NG, true>), dim3((unsigned)grid),
-                       dim3(64), 0, s, p);
+    hipLaunchKernelGGL((prefill_kernel<FMT, D, BS, NG>), dim3((unsigned)grid),
+                       dim3(64 * kPfWaves), 0, s, p);
     return launch_status();
 }
 
@@ -517,9 +518,9 @@ static PrefillCut prefill_cut(int32_t num_seqs, int32_t num_q_heads, int32_t num
         return c;
     const bool fits = (int64_t)max_query_len * r <= 32;
     if (mode == KVQ_PREFILL_AUTO && !fits) {
-        const int64_t tokens_per_wave = 2 * (16 / r);
-        const int64_t walk_waves = (int64_t)num_seqs * num_kv_heads *
-                                   ((max_query_len + tokens_per_wave - 1) / tokens_per_wave);
+        const int64_t tokens_per_group = prefill_tokens_per_group(r);
+        const int64_t walk_waves = (int64_t)num_seqs * num_kv_heads * kPfWaves *
+                                   ((max_query_len + tokens_per_group - 1) / tokens_per_group);
         if (walk_waves >= (int64_t)device_cus() * run_waves_per_cu(FMT_INT8))
             return c;
     }
@@ -794,8 +795,7 @@ kvq_status kvq_paged_prefill(const void *q, const int32_t *query_start, int32_t 
     const float sm = softmax_scale > 0.0f ? softmax_scale : 1.0f / std::sqrt((float)head_dim);
     p.score_scale = sm * 1.4426950408889634f;
     p.q_start = query_start;
-    p.qpc = 16 / r;
-    p.groups = (max_query_len + p.qpc - 1) / p.qpc;
+    p.groups = (max_query_len + prefill_tokens_per_group(r) - 1) / prefill_tokens_per_group(r);
     if (cut.path != kPathWalk) {  // the decode partition, columns = (chunk token, query head)
         hipStream_t s = static_cast<hipStream_t>(stream);
         uint8_t *ws = static_cast<uint8_t *>(workspace);

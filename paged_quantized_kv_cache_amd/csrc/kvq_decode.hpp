@@ -120,8 +120,7 @@ struct DecodeParams {
     // [B] table row of each (virtual) sequence when the chunks of longer
     // prompts are cut into virtual sequences; null: row b is sequence b
     const int32_t *seq_row;
-    int32_t qpc;             // chunk tokens per wavefront (16 / r)
-    int32_t groups;          // ceil(max chunk length / qpc)
+    int32_t groups;          // chunked prefill: query blocks per (sequence, KV head)
 };
 
 struct PlanParams {
@@ -150,24 +149,6 @@ __device__ __forceinline__ void set_run_priority(int left, int len)
     else if (4 * left > len)
         __builtin_amdgcn_s_setprio(2);
     else if (8 * left > len)
-        __builtin_amdgcn_s_setprio(1);
-    else
-        __builtin_amdgcn_s_setprio(0);
-}
-
-// Chunked prefill: wavefronts walk different numbers of tiles (causal
-// groups), and more of them are launched than the GPU holds.  The priority
-// follows the tiles a wavefront still has to walk (3 above 64, 2 above 32,
-// 1 above 16), so the longest remaining walks issue first and the launch
-// does not end on a few long wavefronts (measured: attention 10 % faster on
-// 2048-token prompts).
-__device__ __forceinline__ void set_prefill_priority(int left)
-{
-    if (left > 64)
-        __builtin_amdgcn_s_setprio(3);
-    else if (left > 32)
-        __builtin_amdgcn_s_setprio(2);
-    else if (left > 16)
         __builtin_amdgcn_s_setprio(1);
     else
         __builtin_amdgcn_s_setprio(0);
@@ -407,19 +388,13 @@ struct Cols {
     bool active;
 };
 
-// Chunked prefill: column groups per wavefront.  Each tile is loaded and its
-// codes converted once for all of them.
-constexpr int kPrefillGroups = 2;
-
-// kPrefill: chunked prefill instead of decode (see the end of the kernel).
 // kDecodeGroups: MFMA column groups per wavefront in the decode walk (2 for
 // short chunks of more than 16 columns: chunk tokens x query heads).
 // The INT4 decode instance runs four wavefronts per SIMD (its tiles carry
 // half the bytes, so more of them must be in flight), which needs it to fit
 // in 128 VGPRs (with 32-token blocks that would spill; it runs three).
-template <int FMT, int D, int BS, int NG, bool kPrefill = false, int kDecodeGroups = 1>
-__global__ __launch_bounds__(64, (FMT == FMT_INT4 && BS == 16 && !kPrefill &&
-                                  kDecodeGroups == 1) ? 4 : 1)
+template <int FMT, int D, int BS, int NG, int kDecodeGroups = 1>
+__global__ __launch_bounds__(64, (FMT == FMT_INT4 && BS == 16 && kDecodeGroups == 1) ? 4 : 1)
 void paged_decode_kernel(DecodeParams p)
 {
     constexpr int KS = D / 16;   // MFMA k-steps over head_dim
@@ -430,7 +405,7 @@ void paged_decode_kernel(DecodeParams p)
     // one per (KV head, channel) (INT8), none (fp16).
     constexpr bool kGroup = NG > 0;
     constexpr int NA = kGroup ? NG : 1;        // score accumulators per tile
-    constexpr int NQ = kPrefill ? kPrefillGroups : kDecodeGroups;  // column groups per wavefront
+    constexpr int NQ = kDecodeGroups;          // column groups per wavefront
     constexpr int G = kGroup ? D / NG : D;     // group size
     constexpr bool kChannel = FMT == FMT_INT8 && !kGroup;
     static_assert(FMT != FMT_INT4 || (D == 128 && kGroup), "INT4: head_dim 128, group scales");
@@ -450,59 +425,59 @@ void paged_decode_kernel(DecodeParams p)
     const int col = lane & 15;
     const int grp = lane >> 4;
     PlanRecord rec{};
-    if constexpr (!kPrefill) {  // this wavefront's run of tiles
-        if (p.inline_plan) {
-            // every wavefront scans the lengths: lane i holds sequences
-            // per*i .. per*i + per - 1
-            const int per = (p.B + 63) >> 6;
-            int tl[kInlineSeqs];
-            int sum = 0;
-    #pragma unroll
-            for (int j = 0; j < kInlineSeqs; ++j) {
-                const int bb = lane * per + j;
-                tl[j] = (j < per && bb < p.B) ? ctx_tiles(p.context_lens, bb, p.max_ctx) : 0;
-                sum += tl[j];
-            }
-            int incl = sum;
-    #pragma unroll
-            for (int o = 1; o < 64; o <<= 1) {
-                const int y = __shfl_up(incl, o);
-                if (lane >= o)
-                    incl += y;
-            }
-            // (readfirstlane: the values are wave-uniform; keep them scalar)
-            const int T = p.Hkv * __builtin_amdgcn_readfirstlane(__shfl(incl, 63));
-            const int W = min(p.W, T);
-            if (w == 0 && lane == 0)
-                p.plan_meta[0] = W;  // runs in use, for the merge launch
-            if (w >= W)
-                return;
-            const int g0 = (int)((int64_t)w * T / W);
-            const int g1 = (int)((int64_t)(w + 1) * T / W);
-            int s0 = incl - sum, found = -1, fbase = 0, fn = 1;
-    #pragma unroll
-            for (int j = 0; j < kInlineSeqs; ++j) {
-                if (p.Hkv * s0 <= g0 && g0 < p.Hkv * (s0 + tl[j])) {
-                    found = lane * per + j;
-                    fbase = p.Hkv * s0;
-                    fn = tl[j];
-                }
-                s0 += tl[j];
-            }
-            const int src = __builtin_ctzll(__builtin_amdgcn_ballot_w64(found >= 0));
-            const int base = __builtin_amdgcn_readlane(fbase, src);
-            const int n0 = __builtin_amdgcn_readlane(fn, src);
-            const int us = base + (g0 - base) / n0 * n0;
-            rec = PlanRecord{__builtin_amdgcn_readlane(found, src), g0, g1, base, us, us + n0,
-                             {0, 0}};
-            if (lane == 0)
-                p.plan_rec[w] = rec;  // for the merge launch
-        } else {
-            if (w >= p.plan_meta[0])
-                return;
-            rec = p.plan_rec[w];
+    // this wavefront's run of tiles
+    if (p.inline_plan) {
+        // every wavefront scans the lengths: lane i holds sequences
+        // per*i .. per*i + per - 1
+        const int per = (p.B + 63) >> 6;
+        int tl[kInlineSeqs];
+        int sum = 0;
+#pragma unroll
+        for (int j = 0; j < kInlineSeqs; ++j) {
+            const int bb = lane * per + j;
+            tl[j] = (j < per && bb < p.B) ? ctx_tiles(p.context_lens, bb, p.max_ctx) : 0;
+            sum += tl[j];
         }
+        int incl = sum;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int y = __shfl_up(incl, o);
+            if (lane >= o)
+                incl += y;
+        }
+        // (readfirstlane: the values are wave-uniform; keep them scalar)
+        const int T = p.Hkv * __builtin_amdgcn_readfirstlane(__shfl(incl, 63));
+        const int W = min(p.W, T);
+        if (w == 0 && lane == 0)
+            p.plan_meta[0] = W;  // runs in use, for the merge launch
+        if (w >= W)
+            return;
+        const int g0 = (int)((int64_t)w * T / W);
+        const int g1 = (int)((int64_t)(w + 1) * T / W);
+        int s0 = incl - sum, found = -1, fbase = 0, fn = 1;
+#pragma unroll
+        for (int j = 0; j < kInlineSeqs; ++j) {
+            if (p.Hkv * s0 <= g0 && g0 < p.Hkv * (s0 + tl[j])) {
+                found = lane * per + j;
+                fbase = p.Hkv * s0;
+                fn = tl[j];
+            }
+            s0 += tl[j];
+        }
+        const int src = __builtin_ctzll(__builtin_amdgcn_ballot_w64(found >= 0));
+        const int base = __builtin_amdgcn_readlane(fbase, src);
+        const int n0 = __builtin_amdgcn_readlane(fn, src);
+        const int us = base + (g0 - base) / n0 * n0;
+        rec = PlanRecord{__builtin_amdgcn_readlane(found, src), g0, g1, base, us, us + n0,
+                         {0, 0}};
+        if (lane == 0)
+            p.plan_rec[w] = rec;  // for the merge launch
+    } else {
+        if (w >= p.plan_meta[0])
+            return;
+        rec = p.plan_rec[w];
     }
+
     float score_scale0 = p.score_scale;
 
     // decode: tiles of the run, and those after the piece being walked
@@ -515,18 +490,9 @@ void paged_decode_kernel(DecodeParams p)
                       const int t1, const Cols (&cg)[NQ]) {
         const int t_end = min(ctx, 16 * t1);  // token bound of this run (data)
         int t_col[NQ];                        // score bound of this lane's columns
-        int t_full = t_end;                   // below it every column takes every token
 #pragma unroll
-        for (int q = 0; q < NQ; ++q) {
+        for (int q = 0; q < NQ; ++q)
             t_col[q] = min(t_end, cg[q].tcol);
-            t_full = min(t_full, t_col[q]);
-        }
-        if constexpr (kPrefill) {
-#pragma unroll
-            for (int o = 1; o < 64; o <<= 1)
-                t_full = min(t_full, __shfl_xor(t_full, o));
-            t_full = __builtin_amdgcn_readfirstlane(t_full);
-        }
 
         // ---- query operand, in the k-step dim order of the K loads:
         //   1-byte codes: k-step s, lane group grp, element v -> dim
@@ -617,14 +583,11 @@ void paged_decode_kernel(DecodeParams p)
         }
 
         // One tile of 16 tokens starting at logical token ts, data in `cur`.
-        // kFull (chunked prefill): every token of the tile is below every
-        // column's bound, so no score or scale needs a mask.
-        auto process = [&](const TileData<FMT, D> &cur, const int ts, auto full_tag) {
-            constexpr bool kFull = decltype(full_tag)::value;
+        auto process = [&](const TileData<FMT, D> &cur, const int ts) {
             // ---- this lane's scales: sk[v][j], sv[v][j] of tokens 4 grp + v
             float sk[4][NA], sv[4][NA];
             if constexpr (kGroup) {
-                const float sc = (kFull || ts + lane_tok < t_end) ? cur.sc * lane_fac : 0.0f;
+                const float sc = ts + lane_tok < t_end ? cur.sc * lane_fac : 0.0f;
                 static_for<0, 4 * NG>([&](auto I) {
                     constexpr int i = decltype(I)::value;
                     sk[i / NG][i % NG] = row_bcast<i>(sc);
@@ -686,7 +649,7 @@ void paged_decode_kernel(DecodeParams p)
                     } else {
                         acc = sacc[q][0][v] * score_scale;
                     }
-                    z[v] = (kFull || tok0 + v < t_col[q]) ? acc : -INFINITY;
+                    z[v] = tok0 + v < t_col[q] ? acc : -INFINITY;
                 }
                 // ---- online softmax, with a lazy rescale: the reference m
                 // moves only when a score exceeds it by more than kSlack (base
@@ -694,8 +657,6 @@ void paged_decode_kernel(DecodeParams p)
                 // scale) stay finite in fp16 for any fp16 input: a group scale
                 // is at most 65504 / 127 (INT8) or / 7 (INT4); FP8 group
                 // scales carry the 2^8 of the E4M3 operands, so there P <= 1.
-                // (With 16 active columns some maximum grows in most early
-                // tiles; measured: prefill 5 % faster.)
                 constexpr float kSlack = !kGroup ? 8.0f
                                        : FMT == FMT_INT8 ? 6.0f
                                        : FMT == FMT_INT4 ? 2.0f : 0.0f;
@@ -738,8 +699,7 @@ void paged_decode_kernel(DecodeParams p)
             // codes survive it; a V dword holds tokens 0..3 of the quad, one
             // byte each.
             uint32_t vmask01 = ~0u, vmask23 = ~0u, vmask8 = ~0u;
-            if constexpr (kFull) {
-            } else if constexpr (FMT == FMT_FP16) {
+            if constexpr (FMT == FMT_FP16) {
                 const int nv = t_end - tok0;  // valid tokens of this lane's quad (if < 4)
                 vmask01 = nv >= 2 ? ~0u : (nv == 1 ? 0xffffu : 0u);
                 vmask23 = nv >= 4 ? ~0u : (nv == 3 ? 0xffffu : 0u);
@@ -816,17 +776,14 @@ void paged_decode_kernel(DecodeParams p)
         };
         // walk tiles [tb, te) with one cache policy; tile tb lies in window
         // wi or wi + 1
-        auto walk = [&](const int tb, const int te, auto nt_tag, auto full_tag) {
+        auto walk = [&](const int tb, const int te, auto nt_tag) {
             auto ldw = [&](TileData<FMT, D> &buf, int i) { ld(buf, min(i, te - 1), nt_tag); };
-            auto proc = [&](const TileData<FMT, D> &buf, int i) { process(buf, 16 * i, full_tag); };
+            auto proc = [&](const TileData<FMT, D> &buf, int i) { process(buf, 16 * i); };
             TileData<FMT, D> buf0, buf1;
             ldw(buf0, tb);
             // loop invariant: tile i lies in window wi and its data is in buf0
             for (int i = tb; i < te; i += 2) {
-                if constexpr (kPrefill)
-                    set_prefill_priority(t1 - i);
-                else
-                    set_run_priority(t1 - i + run_after, run_len);
+                set_run_priority(t1 - i + run_after, run_len);
                 if (i / (64 * TPB) != wi) {  // entering the next window
                     ++wi;
                     win_a = win_b;
@@ -843,28 +800,18 @@ void paged_decode_kernel(DecodeParams p)
         auto has_shared = [&](int win) {
             return __builtin_amdgcn_ballot_w64((win & kSharedBlock) != 0) != 0;
         };
-        if constexpr (kPrefill) {
-            // every group of the pair reads these tiles: ordinary loads keep
-            // them in L2; the tiles below t_full need no masks
-            const int tf = min(max(t_full >> 4, t0), t1);
-            if (tf > t0)
-                walk(t0, tf, std::false_type{}, std::true_type{});
-            if (tf < t1)
-                walk(tf, t1, std::false_type{}, std::false_type{});
-        } else {
-            int ts = t0;  // end of the leading windows that hold shared blocks
-            if (has_shared(win_a)) {
-                ts = (wi + 1) * 64 * TPB;
-                if (has_shared(win_b))
-                    ts = has_shared(win_c) ? t1 : (wi + 2) * 64 * TPB;
-            }
-            ts = min(ts, t1);
-            if (ts > t0)
-                walk(t0, ts, std::false_type{}, std::false_type{});
-            if (ts < t1)
-                walk(ts, t1, std::true_type{}, std::false_type{});
+        int ts = t0;  // end of the leading windows that hold shared blocks
+        if (has_shared(win_a)) {
+            ts = (wi + 1) * 64 * TPB;
+            if (has_shared(win_b))
+                ts = has_shared(win_c) ? t1 : (wi + 2) * 64 * TPB;
         }
-
+        ts = min(ts, t1);
+        if (ts > t0)
+            walk(t0, ts, std::false_type{});
+        if (ts < t1)
+            walk(ts, t1, std::true_type{});
+    
         // ---- epilogue: lane holds dims 64 g4 + 16 grp + (0..15) of head col
 #pragma unroll
         for (int q = 0; q < NQ; ++q) {
@@ -923,59 +870,6 @@ void paged_decode_kernel(DecodeParams p)
                 *reinterpret_cast<float2 *>(p.ws_ml + 2 * idx) = make_float2(m[q], lt);
         }
     };
-
-    if constexpr (kPrefill) {
-        // ---- chunked prefill ("KV Cache优化实战" s1.1: every prompt token
-        // attends to the tokens before it; xpshop.cn article 312 s6: long
-        // prompts go in chunks).  Sequence b's chunk is the last nq of its
-        // ctx tokens (their K/V already written); chunk token i sits at
-        // position ctx - nq + i.  Chunk tokens form groups of qpc = 16 / r;
-        // in group gi, MFMA column col is chunk token gi * qpc + col / r with
-        // query head h * r + col % r, so one MFMA column group serves qpc
-        // tokens x r heads.  A wavefront takes (b, KV head h) and NQ
-        // consecutive groups; the later (longer) ones start first.
-        // Order for L2 reuse: every group of a (sequence, KV head) pair
-        // reads the same K/V, so the pairs are spread over the XCDs and each
-        // XCD walks its pairs one after another.  Workgroups are dispatched
-        // round-robin, w to XCD w % 8: XCD x takes pairs x, x + 8, x + 16,
-        // ..., all wavefronts of one pair (longest first) before the next,
-        // so the K/V it reads at a time (one or two pairs) stays in its L2.
-        // Interleaving the pairs instead gave a 50 % L2 hit rate and fetched
-        // ~135x the unique K/V bytes from beyond L2.  A wavefront takes NQ
-        // consecutive groups, which share every tile it loads.
-        const int BH = p.B * p.Hkv;
-        const int nw = (p.groups + NQ - 1) / NQ;  // wavefronts per pair
-        const int sl = w >> 3;                    // slot in XCD (w % 8)'s sequence
-        const int pair = (w & 7) + 8 * (sl / nw);
-        const int gw = nw - 1 - sl % nw;
-        if (pair >= BH)
-            return;
-        const int b = pair / p.Hkv;
-        const int h = pair % p.Hkv;
-        const int ctx = min(max(p.context_lens[b], 0), p.max_ctx);
-        const int qs = p.q_start[b];
-        const int nq = min(p.q_start[b + 1] - qs, ctx);
-        const int i0 = gw * NQ * p.qpc;           // first chunk token of the wavefront
-        if (i0 >= nq)
-            return;
-        const int c0 = ctx - nq;                  // cached before the chunk
-        const int tl = c0 + min(i0 + NQ * p.qpc, nq);  // tokens this wavefront reads
-        const int n = (tl + 15) >> 4;
-        const int gh = model_head(p, h);
-        const int jc = col % p.r;
-        Cols cg[NQ];
-#pragma unroll
-        for (int q = 0; q < NQ; ++q) {
-            const int ib = i0 + q * p.qpc;        // group q's first chunk token
-            const int ic = ib + col / p.r;
-            const bool active = col < p.qpc * p.r && ic < min(ib + p.qpc, nq);
-            const int64_t row = (int64_t)(qs + (active ? ic : i0)) * p.Hq + gh * p.r +
-                                (active ? jc : 0);
-            cg[q] = Cols{p.q + row * D, p.out + row * D, active ? c0 + ic + 1 : tl, active};
-        }
-        attend(b, h, tl, n, 0, n, cg);
-        return;
-    }
 
     // ---- decode: walk the run [g0, g1) unit by unit (values wave-uniform).
     // Unit column c = 16 q + col (column group q) is query head c of the

@@ -127,6 +127,18 @@ __device__ __forceinline__ f16x4 f16x4_from_u2(uint32_t lo, uint32_t hi)
     return f16x4{a.x, a.y, b.x, b.y};
 }
 
+// Two fp32 values as fp16 pairs hi + lo with hi + lo within about 2^-21 of
+// each value (relative, for values in fp16's normal range): hi keeps the top
+// 11 significant bits (so converting it is exact), lo the remainder, which
+// fp32 holds exactly, converted toward zero.
+__device__ __forceinline__ void split_f16x2(float a, float b, f16x2 &hi, f16x2 &lo)
+{
+    const float ah = __uint_as_float(__float_as_uint(a) & 0xffffe000u);
+    const float bh = __uint_as_float(__float_as_uint(b) & 0xffffe000u);
+    hi = bit_cast<f16x2>(__builtin_amdgcn_cvt_pkrtz(ah, bh));
+    lo = bit_cast<f16x2>(__builtin_amdgcn_cvt_pkrtz(a - ah, b - bh));
+}
+
 // The 8-element operand of a 16x16x32 MFMA from two 4-element halves.  A
 // lane's 8 elements are 8 distinct positions of the summed (k) axis; which
 // positions does not matter as long as both operands use the same order, so
