@@ -36,10 +36,15 @@ HBM_PEAK_GBPS = 8000.0
 DEFAULT_WORKLOAD = "c3_gqa"
 
 
+# the kernels of a decode call (plan, tile walk, merge): traffic counters
+# taken on them stay valid while other kernels change
+DECODE_KERNELS = ("plan_kernel", "paged_decode_kernel", "merge_runs_kernel")
+
+
 def kernel_hash() -> str:
-    """Identity of the device code the counters were taken on."""
+    """Identity of the decode call's device code the counters were taken on."""
     from paged_quantized_kv_cache_amd import build as B
-    return B.device_code_hash()
+    return B.device_code_hash(kernels=DECODE_KERNELS)
 
 
 def load_traffic(workload: str):

@@ -44,7 +44,8 @@ def build(verbose: bool = False, extra=()) -> str:
 
 
 def _elf_sections(b: bytes, base: int = 0) -> dict:
-    """name -> (offset, size) of the sections of the 64-bit ELF at b[base:]."""
+    """name -> (offset, size, address) of the sections of the 64-bit ELF at
+    b[base:]."""
     shoff, = struct.unpack_from("<Q", b, base + 0x28)
     shentsize, shnum, shstrndx = struct.unpack_from("<HHH", b, base + 0x3A)
     hdrs = [struct.unpack_from("<IIQQQQIIQQ", b, base + shoff + i * shentsize)
@@ -53,17 +54,37 @@ def _elf_sections(b: bytes, base: int = 0) -> dict:
     out = {}
     for h in hdrs:
         end = b.index(b"\0", names + h[0])
-        out[b[names + h[0]:end].decode()] = (base + h[4], h[5])
+        out[b[names + h[0]:end].decode()] = (base + h[4], h[5], h[3])
     return out
 
 
-def device_code_hash(path: str = LIB) -> str:
-    """Hash of the gfx950 machine code (.text of the device code object in
-    the library's offload bundle).  Comments or host-side edits leave it
-    unchanged; any change to a kernel's instructions changes it."""
+def _functions(b: bytes, base: int) -> dict:
+    """name -> machine code of every function symbol in the ELF at b[base:]."""
+    secs = _elf_sections(b, base)
+    to, _ts, taddr = secs[".text"]
+    so, ss, _ = secs[".symtab"]
+    stro = secs[".strtab"][0]
+    out = {}
+    for i in range(ss // 24):
+        st_name, st_info, _oth, _shn, st_value, st_size = struct.unpack_from("<IBBHQQ", b, so + 24 * i)
+        if st_info & 0xF != 2 or st_size == 0:  # STT_FUNC
+            continue
+        end = b.index(b"\0", stro + st_name)
+        name = b[stro + st_name:end].decode()
+        out[name] = b[to + st_value - taddr:to + st_value - taddr + st_size]
+    return out
+
+
+def device_code_hash(path: str = LIB, kernels=None) -> str:
+    """Hash of the gfx950 machine code in the library's offload bundle: the
+    whole .text, or (kernels: substrings of mangled names) only the
+    functions whose names contain one of them, so a measurement taken on
+    some kernels stays matched while other kernels change.  Comments or
+    host-side edits leave it unchanged; any change to a hashed kernel's
+    instructions changes it."""
     with open(path, "rb") as f:
         b = f.read()
-    off, size = _elf_sections(b)[".hip_fatbin"]
+    off, size, _ = _elf_sections(b)[".hip_fatbin"]
     fb = b[off:off + size]
     if not fb.startswith(b"__CLANG_OFFLOAD_BUNDLE__"):
         raise ValueError("no offload bundle in %s" % path)
@@ -73,9 +94,15 @@ def device_code_hash(path: str = LIB) -> str:
         eo, _es, tl = struct.unpack_from("<QQQ", fb, pos)
         triple = fb[pos + 24:pos + 24 + tl].decode()
         pos += 24 + tl
-        if "gfx950" in triple:
-            to, ts = _elf_sections(fb, eo)[".text"]
+        if "gfx950" not in triple:
+            continue
+        if kernels is None:
+            to, ts, _ = _elf_sections(fb, eo)[".text"]
             h.update(fb[to:to + ts])
+        else:
+            for name, code in sorted(_functions(fb, eo).items()):
+                if any(k in name for k in kernels):
+                    h.update(name.encode() + b"\0" + code)
     return h.hexdigest()[:16]
 
 
