@@ -310,7 +310,10 @@ struct TileData {
 };
 
 // Broadcast entry `idx` of each 16-lane row to the whole row (ds_swizzle in
-// bit mode: source lane = (lane & 0x10) | idx within each 32-lane half).
+// bit mode: source lane = (lane & 0x10) | idx within each 32-lane half).  It
+// runs on the LDS pipe; a DPP row_newbcast move, one VALU instruction, was
+// measured 4-6 % slower on INT4 (whose tiles leave the VALU the busier unit)
+// and no faster elsewhere.
 template <int idx>
 __device__ __forceinline__ float row_bcast(float x)
 {
@@ -679,16 +682,16 @@ void paged_decode_kernel(DecodeParams p)
                     l[q] += pr[v];
                 }
                 // ---- P^T operands (V group scales folded in; masked tokens
-                // have pr = 0 and a zeroed scale): hi = fp16(P), lo = fp16(P - hi)
+                // have pr = 0 and a zeroed scale): P split into fp16 hi + lo
 #pragma unroll
                 for (int j = 0; j < NA; ++j) {
+                    f16x2 h[2], lo[2];
 #pragma unroll
-                    for (int v = 0; v < 4; ++v) {
-                        const float P = kGroup ? pr[v] * sv[v][j] : pr[v];
-                        const f16 h16 = (f16)P;
-                        pop[q][j][v] = h16;
-                        plo[q][j][v] = (f16)(P - (float)h16);
-                    }
+                    for (int v = 0; v < 4; v += 2)
+                        split_f16x2(kGroup ? pr[v] * sv[v][j] : pr[v],
+                                    kGroup ? pr[v + 1] * sv[v + 1][j] : pr[v + 1], h[v / 2], lo[v / 2]);
+                    pop[q][j] = f16x4{h[0].x, h[0].y, h[1].x, h[1].y};
+                    plo[q][j] = f16x4{lo[0].x, lo[0].y, lo[1].x, lo[1].y};
                 }
             }
             // ---- O^T += V^T P^T; d-tile tau covers dims 64 (tau/4) + 4 m + tau%4
@@ -779,10 +782,7 @@ void paged_decode_kernel(DecodeParams p)
         auto walk = [&](const int tb, const int te, auto nt_tag) {
             auto ldw = [&](TileData<FMT, D> &buf, int i) { ld(buf, min(i, te - 1), nt_tag); };
             auto proc = [&](const TileData<FMT, D> &buf, int i) { process(buf, 16 * i); };
-            TileData<FMT, D> buf0, buf1;
-            ldw(buf0, tb);
-            // loop invariant: tile i lies in window wi and its data is in buf0
-            for (int i = tb; i < te; i += 2) {
+            auto next_window = [&](int i) {
                 set_run_priority(t1 - i + run_after, run_len);
                 if (i / (64 * TPB) != wi) {  // entering the next window
                     ++wi;
@@ -790,11 +790,39 @@ void paged_decode_kernel(DecodeParams p)
                     win_b = win_c;
                     win_c = load_win(wi + 2);
                 }
-                ldw(buf1, i + 1);
-                proc(buf0, i);
-                ldw(buf0, i + 2);
-                if (i + 1 < te)
-                    proc(buf1, i + 1);
+            };
+            if constexpr (NQ == 2 && FMT != FMT_FP16) {
+                // two column groups: twice the compute per tile at 2 waves /
+                // SIMD, so three tile buffers keep two tiles' loads in flight
+                // (fp16 tiles are twice the size: they stay at two)
+                TileData<FMT, D> buf0, buf1, buf2;
+                ldw(buf0, tb);
+                ldw(buf1, tb + 1);
+                // loop invariant: tile i lies in window wi, its data is in
+                // buf0 and tile i + 1's in buf1
+                for (int i = tb; i < te; i += 3) {
+                    next_window(i);
+                    ldw(buf2, i + 2);
+                    proc(buf0, i);
+                    ldw(buf0, i + 3);
+                    if (i + 1 < te)
+                        proc(buf1, i + 1);
+                    ldw(buf1, i + 4);
+                    if (i + 2 < te)
+                        proc(buf2, i + 2);
+                }
+            } else {
+                TileData<FMT, D> buf0, buf1;
+                ldw(buf0, tb);
+                // loop invariant: tile i lies in window wi and its data is in buf0
+                for (int i = tb; i < te; i += 2) {
+                    next_window(i);
+                    ldw(buf1, i + 1);
+                    proc(buf0, i);
+                    ldw(buf0, i + 2);
+                    if (i + 1 < te)
+                        proc(buf1, i + 1);
+                }
             }
         };
         auto has_shared = [&](int win) {

@@ -139,6 +139,17 @@ __device__ __forceinline__ void split_f16x2(float a, float b, f16x2 &hi, f16x2 &
     lo = bit_cast<f16x2>(__builtin_amdgcn_cvt_pkrtz(a - ah, b - bh));
 }
 
+// The maximum of x over the four 16-lane rows (lanes l, l ^ 16, l ^ 32,
+// l ^ 48), in every lane: gfx950's lane-swap moves (v_permlane32_swap,
+// v_permlane16_swap) keep it off the LDS path.
+__device__ __forceinline__ float max_over_groups(float x)
+{
+    const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(r32[0]), __uint_as_float(r32[1]));
+    const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r16[0]), __uint_as_float(r16[1]));
+}
+
 // The 8-element operand of a 16x16x32 MFMA from two 4-element halves.  A
 // lane's 8 elements are 8 distinct positions of the summed (k) axis; which
 // positions does not matter as long as both operands use the same order, so

@@ -357,15 +357,6 @@ __global__ __launch_bounds__(64 * kPfWaves, 2) void prefill_kernel(DecodeParams 
             store(step, buf, std::true_type{});
     };
 
-    // the maximum over a row's four lane groups (lanes col, col + 16, col +
-    // 32, col + 48): gfx950's lane-swap moves keep it off the LDS path
-    auto row_max = [](float x) {
-        const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-        x = fmaxf(__uint_as_float(r32[0]), __uint_as_float(r32[1]));
-        const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-        return fmaxf(__uint_as_float(r16[0]), __uint_as_float(r16[1]));
-    };
-
     // ---- accumulators
     f32x4 o[2][DT];
     float m[2], l[2];
@@ -453,7 +444,7 @@ __global__ __launch_bounds__(64 * kPfWaves, 2) void prefill_kernel(DecodeParams 
         for (int rt = 0; rt < 2; ++rt) {
             float mt = fmaxf(fmaxf(fmaxf(z[rt][0][0], z[rt][0][1]), fmaxf(z[rt][0][2], z[rt][0][3])),
                              fmaxf(fmaxf(z[rt][1][0], z[rt][1][1]), fmaxf(z[rt][1][2], z[rt][1][3])));
-            mt = row_max(mt);
+            mt = max_over_groups(mt);
             constexpr float kSlack = !kGroup ? 8.0f
                                    : FMT == FMT_INT8 ? 6.0f
                                    : FMT == FMT_INT4 ? 2.0f : 0.0f;
