@@ -172,10 +172,14 @@ __global__ __launch_bounds__(64 * kPfWaves, 2) void prefill_kernel(DecodeParams 
         out_scale = kCodeScale * p.v_scale[h];
     }
 
-    // ---- the step loader.  fetch(step) reads, from the block table, the
-    // blocks of the tokens whose pieces this thread loads for the step;
-    // load(step) gathers those K / V codes (16-byte pieces) and scales into
-    // registers; store() converts them and writes LDS.  The walk issues
+    // ---- the step loader.  A step's 32 keys span two 16-token halves, each
+    // inside one block; fetch(step) reads the two block-table entries (the
+    // same address in every lane, so each wavefront reads them once);
+    // load(step) gathers the step's K / V codes (16-byte pieces) and scales
+    // into registers; store() converts them and writes LDS.  Every
+    // wavefront's K and V pieces lie in one half, so a piece's address is a
+    // wave-uniform tile base (scalar registers) plus an offset fixed per
+    // thread: the loads cost no vector address arithmetic.  The walk issues
     // fetch two steps ahead and load one step ahead, so neither the table
     // read nor the code read it depends on waits behind compute.  Tokens at
     // or past ctx read a valid block and are written as zeros (stale slots
@@ -183,71 +187,73 @@ __global__ __launch_bounds__(64 * kPfWaves, 2) void prefill_kernel(DecodeParams 
     const int32_t *bt = p.block_tables + (int64_t)b * p.max_blocks;
     constexpr int PPT = TB / 16;                // K pieces per token
     constexpr int UPH = VPIECES / 2;            // V units per 16-token half
+    static_assert(64 / PPT <= 16 && UPH % 64 == 0, "a wavefront's pieces lie in one half");
     // whether a thread's x-th piece exists (always, when the pieces fill
     // every thread: no branch then, so no wait lands inside one)
     auto has_k = [&](int x) { return KPIECES % NT == 0 || tid + NT * x < KPIECES; };
     auto has_v = [&](int x) { return VPIECES % NT == 0 || tid + NT * x < VPIECES; };
-    u32x4 kraw[KPT], vraw[VPT];
-    float sraw = 0.0f;
-    int kid[KPT], vid[VPT], sid = 0;            // block-table entries of the next load
-    auto entry = [&](int tok) { return bt[min(tok, kend - 1) / BS]; };
-    auto block = [&](int e) -> int64_t {        // (block, head) tile of an entry
-        return (int64_t)min(max(e & kBlockIdMask, 0), p.num_blocks - 1) * p.Hkv + h;
-    };
+    const int wvu = __builtin_amdgcn_readfirstlane(wv);
+    // per thread: byte offsets of its pieces inside their (block, head) tile
+    // (a step starts on a block boundary or a block's second half, so these
+    // do not change from step to step), and the half each piece lies in
+    int k_off[KPT], v_off[VPT];
+#pragma unroll
+    for (int x = 0; x < KPT; ++x) {
+        const int c = tid + NT * x;
+        const int kk = c / PPT, pc = c % PPT;
+        if constexpr (FMT == FMT_INT4)
+            k_off[x] = (kk % BS) * 64 + 16 * pc;
+        else
+            k_off[x] = k_offset<D, EB>(BS, kk % BS, pc * 16 / EB);
+    }
+#pragma unroll
+    for (int x = 0; x < VPT; ++x) {
+        const int c = tid + NT * x;
+        const int hf = c / UPH, u = c % UPH;
+        const int hb = (16 * hf % BS) / 16;     // half of its block
+        if constexpr (FMT == FMT_INT4) {
+            v_off[x] = hb * 1024 + u * 16;      // (dim quad, token quad) unit
+        } else {
+            // unit u = (part e, dim quad dq, token quad tq)
+            const int e = u / D, dq = (u % D) / 4, tq = u % 4;
+            v_off[x] = (((hb * EB + e) * (D / 4) + dq) * 4 + tq) * 16;
+        }
+    }
+    auto k_half = [&](int x) { return ((64 * wvu + NT * x) / PPT) / 16; };   // wave-uniform
+    auto v_half = [&](int x) { return (64 * wvu + NT * x) / UPH; };          // wave-uniform
     // scale loads: every thread loads one (the first 2 x 32 x NG are kept)
     const int s_kind = (tid / (kPfKeys * NA)) & 1, s_idx = tid % (kPfKeys * NA);
+    const int s_half = (s_idx / NA) / 16;
+    const int s_off = ((s_idx / NA) % BS) * NA + s_idx % NA;
+    u32x4 kraw[KPT], vraw[VPT];
+    float sraw = 0.0f;
+    int ent_f[2] = {0, 0}, ent_l[2] = {0, 0};   // table entries: fetched / for the next load
     auto fetch = [&](int step) {
         const int kb = step * kPfKeys;
-#pragma unroll
-        for (int x = 0; x < KPT; ++x)
-            if (has_k(x))
-                kid[x] = entry(kb + (tid + NT * x) / PPT);
-#pragma unroll
-        for (int x = 0; x < VPT; ++x)
-            if (has_v(x))
-                vid[x] = entry(kb + 16 * ((tid + NT * x) / UPH));
-        if constexpr (kGroup)
-            sid = entry(kb + s_idx / NG);
+        ent_f[0] = bt[min(kb, kend - 1) / BS];
+        ent_f[1] = bt[min(kb + 16, kend - 1) / BS];
+    };
+    auto tile_of = [&](int half) -> int64_t {   // (block, head) tile of a half, wave-uniform
+        const int e = __builtin_amdgcn_readfirstlane(ent_l[half]);
+        return (int64_t)min(max(e & kBlockIdMask, 0), p.num_blocks - 1) * p.Hkv + h;
     };
     auto load = [&](int step) {
-        const int kb = step * kPfKeys;
+        const int64_t t0 = tile_of(0), t1 = tile_of(1);
 #pragma unroll
-        for (int x = 0; x < KPT; ++x) {
+        for (int x = 0; x < KPT; ++x)
             if (has_k(x)) {
-                const int c = tid + NT * x;
-                const int kk = c / PPT, pc = c % PPT;
-                const int off = (kb + kk) % BS;
-                const uint8_t *tile = p.k_pool + block(kid[x]) * (BS * TB);
-                int boff;
-                if constexpr (FMT == FMT_INT4)
-                    boff = off * 64 + 16 * pc;
-                else
-                    boff = k_offset<D, EB>(BS, off, pc * 16 / EB);
-                kraw[x] = *reinterpret_cast<const u32x4 *>(tile + boff);
+                const uint8_t *tile = p.k_pool + (k_half(x) ? t1 : t0) * (BS * TB);
+                kraw[x] = *reinterpret_cast<const u32x4 *>(tile + k_off[x]);
             }
-        }
 #pragma unroll
-        for (int x = 0; x < VPT; ++x) {
+        for (int x = 0; x < VPT; ++x)
             if (has_v(x)) {
-                const int c = tid + NT * x;
-                const int hf = c / UPH, u = c % UPH;
-                const int hb = ((kb + 16 * hf) % BS) / 16;   // half of its block
-                const uint8_t *tile = p.v_pool + block(vid[x]) * (BS * TB);
-                int boff;
-                if constexpr (FMT == FMT_INT4) {
-                    boff = hb * 1024 + u * 16;      // (dim quad, token quad) unit
-                } else {
-                    // unit u = (part e, dim quad dq, token quad tq)
-                    const int e = u / D, dq = (u % D) / 4, tq = u % 4;
-                    boff = (((hb * EB + e) * (D / 4) + dq) * 4 + tq) * 16;
-                }
-                vraw[x] = *reinterpret_cast<const u32x4 *>(tile + boff);
+                const uint8_t *tile = p.v_pool + (v_half(x) ? t1 : t0) * (BS * TB);
+                vraw[x] = *reinterpret_cast<const u32x4 *>(tile + v_off[x]);
             }
-        }
         if constexpr (kGroup) {
-            const int tok = kb + s_idx / NG, g = s_idx % NG;
             const float *arr = s_kind == 0 ? p.k_scale : p.v_scale;
-            sraw = arr[(block(sid) * BS + tok % BS) * NG + g];
+            sraw = arr[(s_half ? t1 : t0) * (BS * NG) + s_off];
         }
     };
     auto cvt4 = [&](uint32_t wd) -> f16x4 {
@@ -538,12 +544,16 @@ __global__ __launch_bounds__(64 * kPfWaves, 2) void prefill_kernel(DecodeParams 
     // position (masked), then none of its keys (loads and barriers only);
     // one loop per run keeps each loop's accumulators in place.
     fetch(0);
+    ent_l[0] = ent_f[0];
+    ent_l[1] = ent_f[1];
     load(0);
     if (nsteps > 1)
         fetch(1);
     store_step(0, 0);
     __syncthreads();
     auto advance = [&](int step) {   // before a step's compute
+        ent_l[0] = ent_f[0];
+        ent_l[1] = ent_f[1];
         if (step + 1 < nsteps)
             load(step + 1);
         if (step + 2 < nsteps)
