@@ -13,10 +13,10 @@
 // and each wavefront owns 32 of them (two 16-row MFMA tiles).  The workgroup
 // walks the keys its rows need in steps of 32 tokens.  For every step the
 // 256 threads gather the step's K / V codes and scales through the block
-// table once, convert the codes to exact fp16 and store them in LDS (two
-// buffers: the next step's loads are in flight while the current one is
-// computed); every wavefront then contracts its rows against the step from
-// LDS.  A tile is therefore converted once for 128 rows instead of once per
+// table once, convert the codes to exact fp16 and store them in LDS (three
+// buffers: while step s is contracted, step s + 1's K forms the next scores
+// and step s + 2's loads are in flight); every wavefront then contracts its
+// rows against the step from LDS.  A tile is therefore converted once for 128 rows instead of once per
 // 32-row wavefront.  What bounds the walk is the vector ALU: per step a
 // wavefront issues ~280 VALU instructions (score scaling, softmax, the P
 // split) against 48 MFMAs, so the VALU port, not the matrix core, is the
@@ -71,9 +71,11 @@ __global__ __launch_bounds__(64 * kPfWaves, 2) void prefill_kernel(DecodeParams 
     static_assert(FMT != FMT_INT4 || (D == 128 && kGroup), "INT4: head_dim 128, group scales");
     static_assert(!kGroup || G >= 64, "groups cover a 64-dim chunk");
 
-    __shared__ __align__(16) f16 k_lds[2][kPfKeys * KSTR];
-    __shared__ __align__(16) f16 v_lds[2][D * VSTR];
-    __shared__ __align__(16) float sc_lds[2][2][kPfKeys * NA];  // [buf][K, V][key * NA + g]
+    // three buffers: step s is contracted from one while step s + 1's K
+    // feeds the next scores and step s + 2 is being stored
+    __shared__ __align__(16) f16 k_lds[3][kPfKeys * KSTR];
+    __shared__ __align__(16) f16 v_lds[3][D * VSTR];
+    __shared__ __align__(16) float sc_lds[3][2][kPfKeys * NA];  // [buf][K, V][key * NA + g]
 
     const int tid = threadIdx.x;
     const int wv = tid >> 6, lane = tid & 63;
@@ -375,15 +377,10 @@ __global__ __launch_bounds__(64 * kPfWaves, 2) void prefill_kernel(DecodeParams 
         l[rt] = 0.0f;
     }
 
-    // One step: keys kb .. kb + 31 from LDS buffer buf.  kMask: some key may
-    // lie past some row's position.
-    // kFirst: the wavefront's first step (m is not yet a running maximum).
-    auto compute = [&](int step, int buf, auto mask_tag, auto first_tag) {
-        constexpr bool kMask = decltype(mask_tag)::value;
-        constexpr bool kFirst = decltype(first_tag)::value;
-        const int kb = step * kPfKeys;
-        // S^T = K Q^T per half (16 keys), one accumulator per scale group
-        f32x4 sacc[2][2][NA];
+    // S^T = K Q^T of the step in LDS buffer buf, per half (16 keys), one
+    // accumulator per scale group
+    using SAcc = f32x4[2][2][NA];
+    auto qk = [&](int buf, SAcc &sacc) {
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
 #pragma unroll
@@ -404,14 +401,17 @@ __global__ __launch_bounds__(64 * kPfWaves, 2) void prefill_kernel(DecodeParams 
                 }
             }
         }
-        // the V^T operands (dims 16 t + col; this lane's 8 keys), read now so
-        // the softmax covers their latency
-        f16x8 va[DT];
-#pragma unroll
-        for (int t = 0; t < DT; ++t) {
-            const f16 *vr = &v_lds[buf][(16 * t + col) * VSTR + 4 * grp];
-            va[t] = cat8(*reinterpret_cast<const f16x4 *>(vr), *reinterpret_cast<const f16x4 *>(vr + 16));
-        }
+    };
+
+    // One step: keys kb .. kb + 31, scores in sacc, codes in LDS buffer buf.
+    // While its softmax runs, the next step's scores (K from buffer nbuf) go
+    // into sacc, the MFMAs interleaved with the VALU work.  kMask: some key
+    // may lie past some row's position.  kFirst: the wavefront's first step
+    // (m is not yet a running maximum).
+    auto compute = [&](int step, int buf, int nbuf, SAcc &sacc, auto mask_tag, auto first_tag) {
+        constexpr bool kMask = decltype(mask_tag)::value;
+        constexpr bool kFirst = decltype(first_tag)::value;
+        const int kb = step * kPfKeys;
         // scores of this lane's keys kb + 16 hf + 4 grp + v (base 2, scaled),
         // less the running maximum m (0 before the first step)
         float z[2][2][4];   // [rt][hf][v]
@@ -443,17 +443,16 @@ __global__ __launch_bounds__(64 * kPfWaves, 2) void prefill_kernel(DecodeParams 
                     z[rt][hf][v] = (!kMask || t <= pos[rt]) ? acc : -INFINITY;
                 }
         }
-        // online softmax; z becomes the unnormalised probabilities.  The
-        // maximum moves only when a score passes it by more than kSlack (in
-        // log2 units), and always on the first step.
+        // online softmax: the maximum moves only when a score passes it by
+        // more than kSlack (in log2 units), and always on the first step
+        constexpr float kSlack = !kGroup ? 8.0f
+                               : FMT == FMT_INT8 ? 6.0f
+                               : FMT == FMT_INT4 ? 2.0f : 0.0f;
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt) {
             float mt = fmaxf(fmaxf(fmaxf(z[rt][0][0], z[rt][0][1]), fmaxf(z[rt][0][2], z[rt][0][3])),
                              fmaxf(fmaxf(z[rt][1][0], z[rt][1][1]), fmaxf(z[rt][1][2], z[rt][1][3])));
             mt = max_over_groups(mt);
-            constexpr float kSlack = !kGroup ? 8.0f
-                                   : FMT == FMT_INT8 ? 6.0f
-                                   : FMT == FMT_INT4 ? 2.0f : 0.0f;
             if (kFirst || __builtin_amdgcn_ballot_w64(mt > kSlack)) {
                 // a row with every key masked (mt = -inf) keeps its maximum
                 const float shift = kFirst ? (mt > -INFINITY ? mt : 0.0f) : fmaxf(mt, 0.0f);
@@ -471,13 +470,6 @@ __global__ __launch_bounds__(64 * kPfWaves, 2) void prefill_kernel(DecodeParams 
                     for (int v = 0; v < 4; ++v)
                         z[rt][hf][v] -= shift;
             }
-#pragma unroll
-            for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    z[rt][hf][v] = __builtin_amdgcn_exp2f(z[rt][hf][v]);
-                    l[rt] += z[rt][hf][v];
-                }
         }
         // O^T += V^T P^T per scale group, P (with the group's V scales)
         // split into fp16 hi + lo: a lane's 8 k-slots are its 8 keys (4 grp
@@ -512,37 +504,48 @@ __global__ __launch_bounds__(64 * kPfWaves, 2) void prefill_kernel(DecodeParams 
         };
         auto pv = [&](int g) {
 #pragma unroll
-            for (int t = g * DT / NA; t < (g + 1) * DT / NA; ++t)
+            for (int t = g * DT / NA; t < (g + 1) * DT / NA; ++t) {
+                const f16 *vr = &v_lds[buf][(16 * t + col) * VSTR + 4 * grp];
+                const f16x8 a = cat8(*reinterpret_cast<const f16x4 *>(vr),
+                                     *reinterpret_cast<const f16x4 *>(vr + 16));
 #pragma unroll
                 for (int rt = 0; rt < 2; ++rt) {
-                    o[rt][t] = mfma32(va[t], phi[g][rt], o[rt][t]);
-                    o[rt][t] = mfma32(va[t], plo[g][rt], o[rt][t]);
+                    o[rt][t] = mfma32(a, phi[g][rt], o[rt][t]);
+                    o[rt][t] = mfma32(a, plo[g][rt], o[rt][t]);
                 }
+            }
         };
+        // exp2, the sums and the first group's P (VALU), with the next
+        // step's S^T MFMAs between them
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    z[rt][hf][v] = __builtin_amdgcn_exp2f(z[rt][hf][v]);
+                    l[rt] += z[rt][hf][v];
+                }
         make_p(0);
+        qk(nbuf, sacc);
+
         if constexpr (NA == 2) {
-            // the second group's split (VALU) rides between the first
-            // group's MFMAs
-            __builtin_amdgcn_sched_barrier(0);
+            // the second group's P rides between the first group's MFMAs
             make_p(1);
             pv(0);
-#pragma unroll
-            for (int i = 0; i < 4 * DT / NA; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
-            }
-            __builtin_amdgcn_sched_barrier(0);
+
             pv(1);
         } else {
             pv(0);
         }
     };
 
-    // ---- the walk: the codes of step s + 1 and the blocks of step s + 2 in
-    // flight while step s is computed.  The wavefront's steps fall in three
-    // runs: below every row's position (no mask), then up to its last
-    // position (masked), then none of its keys (loads and barriers only);
-    // one loop per run keeps each loop's accumulators in place.
+    // ---- the walk: the codes of step s + 2 and the blocks of step s + 3 in
+    // flight while step s is computed (and step s + 1's scores formed).  The
+    // wavefront's steps fall in three runs: below every row's position (no
+    // mask), then up to its last position (masked), then none of its keys
+    // (loads and barriers only); one loop per run keeps each loop's
+    // accumulators in place.
     fetch(0);
     ent_l[0] = ent_f[0];
     ent_l[1] = ent_f[1];
@@ -550,45 +553,68 @@ __global__ __launch_bounds__(64 * kPfWaves, 2) void prefill_kernel(DecodeParams 
     if (nsteps > 1)
         fetch(1);
     store_step(0, 0);
+    if (nsteps > 1) {
+        ent_l[0] = ent_f[0];
+        ent_l[1] = ent_f[1];
+        load(1);
+        if (nsteps > 2)
+            fetch(2);
+        store_step(1, 1);
+    }
     __syncthreads();
     auto advance = [&](int step) {   // before a step's compute
         ent_l[0] = ent_f[0];
         ent_l[1] = ent_f[1];
-        if (step + 1 < nsteps)
-            load(step + 1);
         if (step + 2 < nsteps)
-            fetch(step + 2);
+            load(step + 2);
+        if (step + 3 < nsteps)
+            fetch(step + 3);
     };
-    auto finish = [&](int step) {    // after it
-        if (step + 1 < nsteps)
-            store_step(step + 1, (step & 1) ^ 1);
+    auto finish = [&](int step, int b2) {    // after it; b2: buffer of step + 2
+        if (step + 2 < nsteps)
+            store_step(step + 2, b2);
         __syncthreads();
     };
     const int n_free = wpos < 0 ? 0 : min((wpos + 1) / kPfKeys, nsteps);
     const int n_any = wmax < 0 ? 0 : min(wmax / kPfKeys + 1, nsteps);
-    int step = 0;
+    SAcc sacc;
+    int step = 0, b0 = 0, b1 = 1, b2 = 2;   // buffers of steps s, s + 1, s + 2
+    auto rotate = [&]() {
+        const int t = b0;
+        b0 = b1;
+        b1 = b2;
+        b2 = t;
+    };
+    // the next step's buffer; the last step re-forms its own scores instead
+    // (a spare contraction, but no branch around the MFMAs)
+    auto nb = [&](int s) { return s + 1 < nsteps ? b1 : b0; };
     if (n_any > 0) {   // step 0, every row's first
+        qk(0, sacc);
         advance(0);
         if (n_free > 0)
-            compute(0, 0, std::false_type{}, std::true_type{});
+            compute(0, b0, nb(0), sacc, std::false_type{}, std::true_type{});
         else
-            compute(0, 0, std::true_type{}, std::true_type{});
-        finish(0);
+            compute(0, b0, nb(0), sacc, std::true_type{}, std::true_type{});
+        finish(0, b2);
+        rotate();
         step = 1;
     }
     for (; step < n_free; ++step) {
         advance(step);
-        compute(step, step & 1, std::false_type{}, std::false_type{});
-        finish(step);
+        compute(step, b0, nb(step), sacc, std::false_type{}, std::false_type{});
+        finish(step, b2);
+        rotate();
     }
     for (; step < n_any; ++step) {
         advance(step);
-        compute(step, step & 1, std::true_type{}, std::false_type{});
-        finish(step);
+        compute(step, b0, nb(step), sacc, std::true_type{}, std::false_type{});
+        finish(step, b2);
+        rotate();
     }
     for (; step < nsteps; ++step) {
         advance(step);
-        finish(step);
+        finish(step, b2);
+        rotate();
     }
 
     // ---- epilogue: lane holds dims 16 t + 4 grp .. + 3 of its rows
