@@ -16,14 +16,14 @@
 // table once, convert the codes to exact fp16 and store them in LDS (three
 // buffers: while step s is contracted, step s + 1's K forms the next scores
 // and step s + 2's loads are in flight); every wavefront then contracts its
-// rows against the step from LDS.  A tile is therefore converted once for 128 rows instead of once per
-// 32-row wavefront.  What bounds the walk is the vector ALU: per step a
-// wavefront issues ~280 VALU instructions (score scaling, softmax, the P
-// split) against 48 MFMAs, so the VALU port, not the matrix core, is the
-// busy unit.
+// rows against the step from LDS.  A tile is therefore converted once for
+// 128 rows instead of once per 32-row wavefront.  What bounds the walk is
+// the vector ALU: per step a wavefront issues ~290 VALU instructions (score
+// scaling, softmax, the P split) against 48 MFMAs, so the VALU port, not
+// the matrix core, is the busy unit.
 //
 // Contractions (16x16x32 fp16 MFMA, laid out as in the decode kernel so the
-// softmax needs only two cross-lane shuffles per row):
+// softmax needs only two cross-lane exchanges per row):
 //   S^T[key][row] = K (16 keys x 32 dims, from LDS) * Q^T (32 dims x 16 rows,
 //       in registers); one accumulator per scale group, K group scales (with
 //       the softmax scale) applied to the partial dots in fp32.
@@ -177,12 +177,12 @@ __global__ __launch_bounds__(64 * kPfWaves, 2) void prefill_kernel(DecodeParams 
     // ---- the step loader.  A step's 32 keys span two 16-token halves, each
     // inside one block; fetch(step) reads the two block-table entries (the
     // same address in every lane, so each wavefront reads them once);
-    // load(step) gathers the step's K / V codes (16-byte pieces) and scales
+    // load() gathers that step's K / V codes (16-byte pieces) and scales
     // into registers; store() converts them and writes LDS.  Every
     // wavefront's K and V pieces lie in one half, so a piece's address is a
     // wave-uniform tile base (scalar registers) plus an offset fixed per
     // thread: the loads cost no vector address arithmetic.  The walk issues
-    // fetch two steps ahead and load one step ahead, so neither the table
+    // fetch three steps ahead and load two steps ahead, so neither the table
     // read nor the code read it depends on waits behind compute.  Tokens at
     // or past ctx read a valid block and are written as zeros (stale slots
     // may hold non-finite fp16 / E5M2 codes).
@@ -239,7 +239,7 @@ __global__ __launch_bounds__(64 * kPfWaves, 2) void prefill_kernel(DecodeParams 
         const int e = __builtin_amdgcn_readfirstlane(ent_l[half]);
         return (int64_t)min(max(e & kBlockIdMask, 0), p.num_blocks - 1) * p.Hkv + h;
     };
-    auto load = [&](int step) {
+    auto load = [&]() {   // the step whose entries are in ent_l
         const int64_t t0 = tile_of(0), t1 = tile_of(1);
 #pragma unroll
         for (int x = 0; x < KPT; ++x)
@@ -549,14 +549,14 @@ __global__ __launch_bounds__(64 * kPfWaves, 2) void prefill_kernel(DecodeParams 
     fetch(0);
     ent_l[0] = ent_f[0];
     ent_l[1] = ent_f[1];
-    load(0);
+    load();
     if (nsteps > 1)
         fetch(1);
     store_step(0, 0);
     if (nsteps > 1) {
         ent_l[0] = ent_f[0];
         ent_l[1] = ent_f[1];
-        load(1);
+        load();
         if (nsteps > 2)
             fetch(2);
         store_step(1, 1);
@@ -566,7 +566,7 @@ __global__ __launch_bounds__(64 * kPfWaves, 2) void prefill_kernel(DecodeParams 
         ent_l[0] = ent_f[0];
         ent_l[1] = ent_f[1];
         if (step + 2 < nsteps)
-            load(step + 2);
+            load();
         if (step + 3 < nsteps)
             fetch(step + 3);
     };
