@@ -423,7 +423,12 @@ void paged_decode_kernel(DecodeParams p)
     // rate of the 16x16x16 MFMA a single P would need.
     static_assert(!kGroup || G >= 64, "groups must cover a 64-dim chunk");
 
-    const int w = blockIdx.x;
+    // run index: workgroups go round-robin to the 8 XCDs (w to XCD w % 8);
+    // XCD x takes the runs x G / 8 .. (x + 1) G / 8 - 1, so the heads of a
+    // sequence (consecutive runs) share an XCD and start together
+    const int G8 = gridDim.x;
+    const int w = (G8 & 7) == 0 ? (int)(blockIdx.x & 7) * (G8 >> 3) + (int)(blockIdx.x >> 3)
+                                : (int)blockIdx.x;
     const int lane = threadIdx.x;
     const int col = lane & 15;
     const int grp = lane >> 4;
