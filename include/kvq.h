@@ -230,8 +230,10 @@ KVQ_API kvq_status kvq_paged_decode(const void *q, const void *k_pool,
  *                 n_b <= context_lens[b]; max_query_len >= every n_b is the
  *                 host-side bound that sizes the launch.
  *   split_mode    how the work is cut (KVQ_PREFILL_*):
- *     WALK: one wavefront per (sequence, KV head, two groups of
- *       16 / (Hq / Hkv) chunk tokens) walks the tokens it needs;
+ *     WALK: one workgroup per (sequence, KV head, block of
+ *       128 / (Hq / Hkv) chunk tokens) walks the tokens it needs, each
+ *       32-token step of K/V converted once into LDS for its 128
+ *       (token, query head) rows;
  *     SPLIT: the decode partition -- the batch's 16-token tiles dealt in
  *       equal runs over every wavefront the GPU holds, an MFMA column per
  *       (chunk token, query head) of a KV head with its own causal bound

@@ -484,8 +484,10 @@ size_t kvq_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t 
 }
 
 // How kvq_paged_prefill cuts the work.
-//   walk:    one wavefront per (sequence, KV head, two groups of 16 / r chunk
-//            tokens) walks the tokens it needs (the prefill kernel);
+//   walk:    one workgroup of four wavefronts per (sequence, KV head, block
+//            of 128 / r chunk tokens) walks the tokens it needs, staging
+//            each 32-key step in LDS once for its 128 rows (the prefill
+//            kernel);
 //   short:   chunks of at most 32 / r tokens (up to 32 MFMA columns of chunk
 //            tokens x query heads, one or two column groups per wavefront)
 //            go through the decode partition: balanced runs over every
