@@ -25,7 +25,7 @@
 //       B operand = P^T, exactly the softmaxed S^T output already in the
 //       lane, as an fp16 pair hi + lo; A operand: 4 consecutive tokens of
 //       one dim (which the V micro-tile layout stores next to each other),
-//       taken once against hi and once against lo.
+//       taken once against hi and once against lo (16x16x16 MFMAs).
 // The head_dim order inside an MFMA k-step is a permutation chosen so that
 // each lane's K bytes are contiguous; q is loaded with the same permutation.
 // Codes are converted to exact fp16 (INT8 / INT4 code c, E4M3 value * 2^-8,
@@ -418,9 +418,9 @@ void paged_decode_kernel(DecodeParams p)
     // the largest |V| the softmax weighs (the weights sum to 1): inside an
     // absolute 2e-3 only while |V| <= 4.  Outlier channels in V reach ~30.
     // P is therefore split into hi = fp16(P) and lo = fp16(P - hi), which
-    // leaves ~2^-22 relative, and one 16x16x32 MFMA per d-tile takes the
-    // codes twice, against hi and against lo: on gfx950 it issues at the
-    // rate of the 16x16x16 MFMA a single P would need.
+    // leaves ~2^-22 relative; the codes meet hi and lo in two 16x16x16
+    // MFMAs per d-tile (one column group) or in one 16x16x32 MFMA that holds
+    // them twice (two column groups).
     static_assert(!kGroup || G >= 64, "groups must cover a 64-dim chunk");
 
     // run index: workgroups go round-robin to the 8 XCDs (w to XCD w % 8);
@@ -715,7 +715,13 @@ void paged_decode_kernel(DecodeParams p)
                 const int nv = t_end - tok0;
                 vmask8 = nv >= 4 ? ~0u : (nv <= 0 ? 0u : (1u << (8 * nv)) - 1u);
             }
-            // one 16x16x32 MFMA per d-tile: the codes twice, against hi and lo
+            // per d-tile, one column group: two 16x16x16 MFMAs, the codes
+            // against hi, then against lo (a 16x16x32 one would need the
+            // codes copied into both halves of its operand: 16 register moves
+            // per tile, which cost more VALU time than the second MFMA costs
+            // matrix time); two column groups: one 16x16x32 MFMA per group,
+            // the codes twice, against hi and lo (there the matrix core is
+            // the busier unit)
 #pragma unroll
             for (int tau = 0; tau < DT; ++tau) {
                 const int g4 = tau >> 2, i = tau & 3;
@@ -736,9 +742,14 @@ void paged_decode_kernel(DecodeParams p)
                     a = f16x4_from_u2(cur.v[4 * x + wd] & vmask01, cur.v[4 * x + wd + 1] & vmask23);
                 }
                 const int gi = NA == 2 ? (64 * g4) / G : 0;
+                if constexpr (NQ == 1) {
+                    o[0][tau] = mfma16(a, pop[0][gi], o[0][tau]);
+                    o[0][tau] = mfma16(a, plo[0][gi], o[0][tau]);
+                } else {
 #pragma unroll
-                for (int q = 0; q < NQ; ++q)
-                    o[q][tau] = mfma32(cat8(a, a), cat8(pop[q][gi], plo[q][gi]), o[q][tau]);
+                    for (int q = 0; q < NQ; ++q)
+                        o[q][tau] = mfma32(cat8(a, a), cat8(pop[q][gi], plo[q][gi]), o[q][tau]);
+                }
             }
         };
 

@@ -139,15 +139,22 @@ __device__ __forceinline__ void split_f16x2(float a, float b, f16x2 &hi, f16x2 &
     lo = bit_cast<f16x2>(__builtin_amdgcn_cvt_pkrtz(a - ah, b - bh));
 }
 
-// The maximum of x over the four 16-lane rows (lanes l, l ^ 16, l ^ 32,
-// l ^ 48), in every lane: gfx950's lane-swap moves (v_permlane32_swap,
-// v_permlane16_swap) keep it off the LDS path.
-__device__ __forceinline__ float max_over_groups(float x)
+// The maxima of a and of b over the four 16-lane rows (lanes l, l ^ 16,
+// l ^ 32, l ^ 48), each in every lane.  gfx950's lane-swap moves
+// (v_permlane32_swap, v_permlane16_swap) keep it off the LDS path, and the
+// first swap packs a's and b's half-reduced values into the two halves of
+// one register, so the pair costs three swaps.
+__device__ __forceinline__ void max_over_groups2(float &a, float &b)
 {
-    const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    x = fmaxf(__uint_as_float(r32[0]), __uint_as_float(r32[1]));
-    const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return fmaxf(__uint_as_float(r16[0]), __uint_as_float(r16[1]));
+    // lanes 0-31: max(a[l], a[l + 32]); lanes 32-63: max(b[l - 32], b[l])
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    float x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    // rows 0, 1: a's maximum; rows 2, 3: b's
+    const auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
+    const auto t = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    a = __uint_as_float(t[0]);
+    b = __uint_as_float(t[1]);
 }
 
 // The 8-element operand of a 16x16x32 MFMA from two 4-element halves.  A
@@ -157,6 +164,13 @@ __device__ __forceinline__ float max_over_groups(float x)
 __device__ __forceinline__ f16x8 cat8(f16x4 a, f16x4 b)
 {
     return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// D += A B over k = 16: lane (col, grp) holds k positions 4 grp .. 4 grp + 3
+// of both operands and rows 4 grp .. 4 grp + 3 of column col of D.
+__device__ __forceinline__ f32x4 mfma16(f16x4 a, f16x4 b, f32x4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
 }
 
 // D += A B over k = 32 (gfx950): the same output layout as 16x16x16 (lane

@@ -351,11 +351,11 @@ __global__ __launch_bounds__(64 * kPfWaves, 2) void prefill_kernel(DecodeParams 
             }
         }
         if constexpr (kGroup) {
-            if (tid < 2 * kPfKeys * NG) {
-                const bool ok = !kTail || kb + s_idx / NG < ctx;
-                sc_lds[buf][s_kind][s_idx] =
-                    ok ? sraw * (s_kind == 0 ? score_scale : kCodeScale) : 0.0f;
-            }
+            // threads past the first 2 x 32 x NG write the same value to
+            // the same slot as a thread below (same load): no branch
+            const bool ok = !kTail || kb + s_idx / NG < ctx;
+            sc_lds[buf][s_kind][s_idx] =
+                ok ? sraw * (s_kind == 0 ? score_scale : kCodeScale) : 0.0f;
         }
     };
     auto store_step = [&](int step, int buf) {
@@ -404,13 +404,16 @@ __global__ __launch_bounds__(64 * kPfWaves, 2) void prefill_kernel(DecodeParams 
     };
 
     // One step: keys kb .. kb + 31, scores in sacc, codes in LDS buffer buf.
-    // While its softmax runs, the next step's scores (K from buffer nbuf) go
-    // into sacc, the MFMAs interleaved with the VALU work.  kMask: some key
-    // may lie past some row's position.  kFirst: the wavefront's first step
-    // (m is not yet a running maximum).
-    auto compute = [&](int step, int buf, int nbuf, SAcc &sacc, auto mask_tag, auto first_tag) {
+    // Once its scores are formed, the next step's (K from buffer nbuf) go
+    // into sacc, the MFMAs interleaved with the softmax VALU work.  kMask:
+    // some key may lie past some row's position.  kFirst: the wavefront's
+    // first step (m is not yet a running maximum).  kFuse: the step also
+    // converts and stores step + 2 (whole, in range) into LDS buffer sbuf.
+    auto compute = [&](int step, int buf, int nbuf, SAcc &sacc, auto mask_tag, auto first_tag,
+                       auto fuse_tag, int sbuf) {
         constexpr bool kMask = decltype(mask_tag)::value;
         constexpr bool kFirst = decltype(first_tag)::value;
+        constexpr bool kFuse = decltype(fuse_tag)::value;
         const int kb = step * kPfKeys;
         // scores of this lane's keys kb + 16 hf + 4 grp + v (base 2, scaled),
         // less the running maximum m (0 before the first step)
@@ -448,14 +451,25 @@ __global__ __launch_bounds__(64 * kPfWaves, 2) void prefill_kernel(DecodeParams 
         constexpr float kSlack = !kGroup ? 8.0f
                                : FMT == FMT_INT8 ? 6.0f
                                : FMT == FMT_INT4 ? 2.0f : 0.0f;
+        // the next step's S^T MFMAs (sacc is free now that z holds this
+        // step's scores) run beside the softmax VALU work below
+        qk(nbuf, sacc);
+        float mt[2];
 #pragma unroll
-        for (int rt = 0; rt < 2; ++rt) {
-            float mt = fmaxf(fmaxf(fmaxf(z[rt][0][0], z[rt][0][1]), fmaxf(z[rt][0][2], z[rt][0][3])),
-                             fmaxf(fmaxf(z[rt][1][0], z[rt][1][1]), fmaxf(z[rt][1][2], z[rt][1][3])));
-            mt = max_over_groups(mt);
-            if (kFirst || __builtin_amdgcn_ballot_w64(mt > kSlack)) {
+        for (int rt = 0; rt < 2; ++rt) {   // a chain, so it folds into 3-input maxima
+            mt[rt] = z[rt][0][0];
+#pragma unroll
+            for (int x = 1; x < 8; ++x)
+                mt[rt] = fmaxf(mt[rt], z[rt][x / 4][x % 4]);
+        }
+        max_over_groups2(mt[0], mt[1]);
+        // one branch for both row tiles: a row whose scores stay at or below
+        // its maximum shifts by 0 (alpha 1) when the other tile moves
+        if (kFirst || __builtin_amdgcn_ballot_w64(fmaxf(mt[0], mt[1]) > kSlack)) {
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt) {
                 // a row with every key masked (mt = -inf) keeps its maximum
-                const float shift = kFirst ? (mt > -INFINITY ? mt : 0.0f) : fmaxf(mt, 0.0f);
+                const float shift = kFirst ? (mt[rt] > -INFINITY ? mt[rt] : 0.0f) : fmaxf(mt[rt], 0.0f);
                 if constexpr (!kFirst) {
                     const float alpha = __builtin_amdgcn_exp2f(-shift);
                     l[rt] *= alpha;
@@ -515,8 +529,7 @@ __global__ __launch_bounds__(64 * kPfWaves, 2) void prefill_kernel(DecodeParams 
                 }
             }
         };
-        // exp2, the sums and the first group's P (VALU), with the next
-        // step's S^T MFMAs between them
+        // exp2, the sums and the first group's P (VALU)
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
@@ -527,7 +540,6 @@ __global__ __launch_bounds__(64 * kPfWaves, 2) void prefill_kernel(DecodeParams 
                     l[rt] += z[rt][hf][v];
                 }
         make_p(0);
-        qk(nbuf, sacc);
 
         if constexpr (NA == 2) {
             // the second group's P rides between the first group's MFMAs
@@ -537,6 +549,11 @@ __global__ __launch_bounds__(64 * kPfWaves, 2) void prefill_kernel(DecodeParams 
             pv(1);
         } else {
             pv(0);
+        }
+        if constexpr (kFuse) {
+            // step s + 2's conversion and LDS stores fill the VALU slots
+            // beside this step's last MFMAs
+            store(step + 2, sbuf, std::false_type{});
         }
     };
 
@@ -592,22 +609,34 @@ __global__ __launch_bounds__(64 * kPfWaves, 2) void prefill_kernel(DecodeParams 
         qk(0, sacc);
         advance(0);
         if (n_free > 0)
-            compute(0, b0, nb(0), sacc, std::false_type{}, std::true_type{});
+            compute(0, b0, nb(0), sacc, std::false_type{}, std::true_type{}, std::false_type{}, 0);
         else
-            compute(0, b0, nb(0), sacc, std::true_type{}, std::true_type{});
+            compute(0, b0, nb(0), sacc, std::true_type{}, std::true_type{}, std::false_type{}, 0);
         finish(0, b2);
         rotate();
         step = 1;
     }
+    // steps whose loads, table reads and store are all in range and whole:
+    // the store of step s + 2 goes inside the compute, between its MFMAs
+    const int n_fast = min(n_free, min(nsteps - 3, ctx / kPfKeys - 2));
+    for (; step < n_fast; ++step) {
+        ent_l[0] = ent_f[0];
+        ent_l[1] = ent_f[1];
+        load();
+        fetch(step + 3);
+        compute(step, b0, b1, sacc, std::false_type{}, std::false_type{}, std::true_type{}, b2);
+        __syncthreads();
+        rotate();
+    }
     for (; step < n_free; ++step) {
         advance(step);
-        compute(step, b0, nb(step), sacc, std::false_type{}, std::false_type{});
+        compute(step, b0, nb(step), sacc, std::false_type{}, std::false_type{}, std::false_type{}, 0);
         finish(step, b2);
         rotate();
     }
     for (; step < n_any; ++step) {
         advance(step);
-        compute(step, b0, nb(step), sacc, std::true_type{}, std::false_type{});
+        compute(step, b0, nb(step), sacc, std::true_type{}, std::false_type{}, std::false_type{}, 0);
         finish(step, b2);
         rotate();
     }
