@@ -28,7 +28,7 @@
 //       taken once against hi and once against lo (16x16x16 MFMAs).
 // The head_dim order inside an MFMA k-step is a permutation chosen so that
 // each lane's K bytes are contiguous; q is loaded with the same permutation.
-// Codes are converted to exact fp16 (INT8 / INT4 code c, E4M3 value * 2^-8,
+// Codes are converted to exact fp16 (INT8 / INT4 code c, E4M3 and
 // E5M2 value) right before the MFMA; K group scales multiply the per-group partial dot
 // products (one accumulator per group); V group scales are folded into P
 // (kept to ~2^-22 relative by the hi + lo pair) so the token sum stays a
@@ -412,7 +412,6 @@ void paged_decode_kernel(DecodeParams p)
     constexpr int G = kGroup ? D / NG : D;     // group size
     constexpr bool kChannel = FMT == FMT_INT8 && !kGroup;
     static_assert(FMT != FMT_INT4 || (D == 128 && kGroup), "INT4: head_dim 128, group scales");
-    constexpr float kCodeScale = FMT == FMT_FP8 ? 256.0f : 1.0f;  // E4M3 enters as value * 2^-8
     // PV precision.  P enters the PV MFMA as fp16, rounded with relative
     // error <= 2^-11, so a single fp16 P moves an output by up to 2^-11 times
     // the largest |V| the softmax weighs (the weights sum to 1): inside an
@@ -563,8 +562,8 @@ void paged_decode_kernel(DecodeParams p)
         float score_scale = score_scale0;
         float out_scale = 1.0f;
         if constexpr ((FMT == FMT_FP8 || FMT == FMT_E5M2) && !kGroup) {
-            score_scale *= kCodeScale * p.k_scale[h];
-            out_scale = kCodeScale * p.v_scale[h];
+            score_scale *= p.k_scale[h];
+            out_scale = p.v_scale[h];
         }
         // Per-group scales: this lane's scale entry (see TileData) is token
         // lane_tok of the tile; K entries carry the score scale, so the
@@ -574,7 +573,7 @@ void paged_decode_kernel(DecodeParams p)
         int lane_tok = 0;
         if constexpr (kGroup) {
             const int e = col % (8 * NG);
-            lane_fac = e < 4 * NG ? score_scale * kCodeScale : kCodeScale;
+            lane_fac = e < 4 * NG ? score_scale : 1.0f;
             lane_tok = 4 * grp + (e % (4 * NG)) / NG;
         }
         // o[q][tau][v]: output dim 64 (tau / 4) + 16 grp + 4 v + tau % 4 of
@@ -614,7 +613,7 @@ void paged_decode_kernel(DecodeParams p)
                 if constexpr (FMT == FMT_INT8)
                     return int8x4_to_f16x4(cur.k[s]);
                 else if constexpr (FMT == FMT_FP8)
-                    return fp8x4_to_f16x4_scaled(cur.k[s]);
+                    return fp8x4_to_f16x4(cur.k[s]);
                 else if constexpr (FMT == FMT_E5M2)
                     return e5m2x4_to_f16x4(cur.k[s]);
                 else
@@ -663,10 +662,9 @@ void paged_decode_kernel(DecodeParams p)
                 // moves only when a score exceeds it by more than kSlack (base
                 // 2), so P < 2^kSlack.  The P^T operands (P times a V group
                 // scale) stay finite in fp16 for any fp16 input: a group scale
-                // is at most 65504 / 127 (INT8) or / 7 (INT4); FP8 group
-                // scales carry the 2^8 of the E4M3 operands, so there P <= 1.
+                // is at most 65504 / 127 (INT8), / 448 (E4M3) or / 7 (INT4).
                 constexpr float kSlack = !kGroup ? 8.0f
-                                       : FMT == FMT_INT8 ? 6.0f
+                                       : FMT == FMT_INT8 || FMT == FMT_FP8 ? 6.0f
                                        : FMT == FMT_INT4 ? 2.0f : 0.0f;
                 float mt = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
                 mt = fmaxf(mt, __shfl_xor(mt, 16));
@@ -703,15 +701,15 @@ void paged_decode_kernel(DecodeParams p)
             // fp16: stale slots past t_end may hold non-finite values, which
             // a zero P entry does not cancel; the lane's V dwords hold tokens
             // (0, 1) or (2, 3) of its quad and are masked per token.
-            // E5M2 likewise: its conversion is exact, so stale NaN / inf
-            // codes survive it; a V dword holds tokens 0..3 of the quad, one
-            // byte each.
+            // E5M2 and E4M3 likewise: their conversions are exact, so stale
+            // NaN / inf codes survive them; a V dword holds tokens 0..3 of
+            // the quad, one byte each.
             uint32_t vmask01 = ~0u, vmask23 = ~0u, vmask8 = ~0u;
             if constexpr (FMT == FMT_FP16) {
                 const int nv = t_end - tok0;  // valid tokens of this lane's quad (if < 4)
                 vmask01 = nv >= 2 ? ~0u : (nv == 1 ? 0xffffu : 0u);
                 vmask23 = nv >= 4 ? ~0u : (nv == 3 ? 0xffffu : 0u);
-            } else if constexpr (FMT == FMT_E5M2) {
+            } else if constexpr (FMT == FMT_E5M2 || FMT == FMT_FP8) {
                 const int nv = t_end - tok0;
                 vmask8 = nv >= 4 ? ~0u : (nv <= 0 ? 0u : (1u << (8 * nv)) - 1u);
             }
@@ -733,7 +731,7 @@ void paged_decode_kernel(DecodeParams p)
                 } else if constexpr (FMT == FMT_INT8) {
                     a = int8x4_to_f16x4(cur.v[4 * g4 + i]);
                 } else if constexpr (FMT == FMT_FP8) {
-                    a = fp8x4_to_f16x4_scaled(cur.v[4 * g4 + i]);
+                    a = fp8x4_to_f16x4(cur.v[4 * g4 + i] & vmask8);
                 } else if constexpr (FMT == FMT_E5M2) {
                     a = e5m2x4_to_f16x4(cur.v[4 * g4 + i] & vmask8);
                 } else {

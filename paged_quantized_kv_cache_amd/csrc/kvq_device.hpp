@@ -11,10 +11,10 @@
 //     leave fp32 sums ~1152 / |c| times larger than the result, whose
 //     rounding then shows in scores of large-scale keys and in outputs near
 //     zero of large-scale values.
-//   E4M3 code -> fp16 equal to value * 2^-8 exactly: moving the 4 exponent
-//     and 3 mantissa bits into the fp16 fields keeps the mantissa and
-//     re-biases the exponent from 7 to 15 (subnormals land on fp16
-//     subnormals with the same factor); the 2^8 goes into the scale.
+//   E4M3 code -> fp16 of the same value: gfx950's packed conversion
+//     (v_cvt_scalef32_pk_f16_fp8, scale 1) turns two codes into two fp16 in
+//     one instruction, exactly (every E4M3 value, subnormals included, is an
+//     fp16 normal number); the NaN codes become NaN.
 //   E5M2 code -> fp16 of the same value: E5M2 has fp16's sign and exponent
 //     fields and its two top fraction bits, so the code is the fp16's high
 //     byte.
@@ -80,16 +80,12 @@ __device__ __forceinline__ f16x4 int8x4_to_f16x4(uint32_t w)
     return f16x4{a.x, a.y, b.x, b.y};
 }
 
-// Four E4M3 bytes -> 4 fp16 holding value * 2^-8 exactly.
-__device__ __forceinline__ f16x4 fp8x4_to_f16x4_scaled(uint32_t w)
+// Four E4M3 bytes -> 4 fp16 of the same values (bytes 0, 1 from the low
+// word, 2, 3 from the high word).
+__device__ __forceinline__ f16x4 fp8x4_to_f16x4(uint32_t w)
 {
-    const uint32_t t0 = byte_perm(0u, w, 0x0c010c00u);  // b0 in half 0, b1 in half 1
-    const uint32_t t1 = byte_perm(0u, w, 0x0c030c02u);
-    // (b + (b & 0x80)) << 7 puts the sign at bit 15, exponent/mantissa at 7..13
-    const uint32_t h0 = (t0 + (t0 & 0x00800080u)) << 7;
-    const uint32_t h1 = (t1 + (t1 & 0x00800080u)) << 7;
-    const f16x2 a = bit_cast<f16x2>(h0);
-    const f16x2 b = bit_cast<f16x2>(h1);
+    const f16x2 a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false);
+    const f16x2 b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true);
     return f16x4{a.x, a.y, b.x, b.y};
 }
 

@@ -56,7 +56,6 @@ __global__ __launch_bounds__(64 * kPfWaves, 2) void prefill_kernel(DecodeParams 
     constexpr int NA = kGroup ? NG : 1;         // score accumulators (scale groups)
     constexpr int G = kGroup ? D / NG : D;
     constexpr bool kChannel = FMT == FMT_INT8 && !kGroup;
-    constexpr float kCodeScale = FMT == FMT_FP8 ? 256.0f : 1.0f;  // E4M3 enters as value * 2^-8
     constexpr int KS = D / 32;                  // 16x16x32 k-steps over head_dim
     constexpr int DT = D / 16;                  // 16-dim output tiles
     constexpr int KSTR = D + 8;                 // K row stride in LDS (halves; 16 B pad)
@@ -167,11 +166,11 @@ __global__ __launch_bounds__(64 * kPfWaves, 2) void prefill_kernel(DecodeParams 
                 }
         }
     }
-    float score_scale = p.score_scale * kCodeScale;
+    float score_scale = p.score_scale;
     float out_scale = 1.0f;
     if constexpr ((FMT == FMT_FP8 || FMT == FMT_E5M2) && !kGroup) {
         score_scale *= p.k_scale[h];
-        out_scale = kCodeScale * p.v_scale[h];
+        out_scale = p.v_scale[h];
     }
 
     // ---- the step loader.  A step's 32 keys span two 16-token halves, each
@@ -262,7 +261,7 @@ __global__ __launch_bounds__(64 * kPfWaves, 2) void prefill_kernel(DecodeParams 
         if constexpr (FMT == FMT_INT8)
             return int8x4_to_f16x4(wd);
         else if constexpr (FMT == FMT_FP8)
-            return fp8x4_to_f16x4_scaled(wd);
+            return fp8x4_to_f16x4(wd);
         else
             return e5m2x4_to_f16x4(wd);
     };
@@ -355,7 +354,7 @@ __global__ __launch_bounds__(64 * kPfWaves, 2) void prefill_kernel(DecodeParams 
             // the same slot as a thread below (same load): no branch
             const bool ok = !kTail || kb + s_idx / NG < ctx;
             sc_lds[buf][s_kind][s_idx] =
-                ok ? sraw * (s_kind == 0 ? score_scale : kCodeScale) : 0.0f;
+                ok ? (s_kind == 0 ? sraw * score_scale : sraw) : 0.0f;
         }
     };
     auto store_step = [&](int step, int buf) {
@@ -449,7 +448,7 @@ __global__ __launch_bounds__(64 * kPfWaves, 2) void prefill_kernel(DecodeParams 
         // online softmax: the maximum moves only when a score passes it by
         // more than kSlack (in log2 units), and always on the first step
         constexpr float kSlack = !kGroup ? 8.0f
-                               : FMT == FMT_INT8 ? 6.0f
+                               : FMT == FMT_INT8 || FMT == FMT_FP8 ? 6.0f
                                : FMT == FMT_INT4 ? 2.0f : 0.0f;
         // the next step's S^T MFMAs (sacc is free now that z holds this
         // step's scores) run beside the softmax VALU work below
