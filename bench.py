@@ -36,9 +36,12 @@ HBM_PEAK_GBPS = 8000.0
 DEFAULT_WORKLOAD = "c3_gqa"
 
 
-# the kernels of a decode call (plan, tile walk, merge): traffic counters
-# taken on them stay valid while other kernels change
-DECODE_KERNELS = ("plan_kernel", "paged_decode_kernel", "merge_runs_kernel")
+# the kernels of the default workload's decode call (plan, the INT8 g64
+# head_dim-128 16-token-block tile walk with one column group, the
+# 128-dim merge; substrings of their mangled names): traffic counters taken
+# on them stay valid while other kernels and instances change
+DECODE_KERNELS = ("plan_kernel", "merge_runs_kernelILi128E",
+                  "paged_decode_kernelILi1ELi128ELi16ELi2ELi1E")
 
 
 def kernel_hash() -> str:
