@@ -422,6 +422,18 @@ void paged_decode_kernel(DecodeParams p)
     // them twice (two column groups).
     static_assert(!kGroup || G >= 64, "groups must cover a 64-dim chunk");
 
+    // Vector memory operations complete in issue order, so a store issued
+    // between a run's tile loads holds up every later wait for those loads
+    // until the store is done (microseconds with HBM busy).  With one column
+    // group the results of a piece therefore wait in registers while the
+    // run continues, up to two pieces' (a third piece stores the oldest),
+    // and are stored once the run's last piece is done; a run of up to three
+    // pieces then stores nothing before its last load, and the inline
+    // plan's record for the merge launch is stored after the walk too.
+    // (Two column groups, or INT4's four wavefronts per SIMD, have no
+    // registers to spare; they store as they go.)
+    constexpr bool kDefer = NQ == 1 && FMT != FMT_INT4;
+
     // run index: workgroups go round-robin to the 8 XCDs (w to XCD w % 8);
     // XCD x takes the runs x G / 8 .. (x + 1) G / 8 - 1, so the heads of a
     // sequence (consecutive runs) share an XCD and start together
@@ -477,8 +489,10 @@ void paged_decode_kernel(DecodeParams p)
         const int us = base + (g0 - base) / n0 * n0;
         rec = PlanRecord{__builtin_amdgcn_readlane(found, src), g0, g1, base, us, us + n0,
                          {0, 0}};
-        if (lane == 0)
-            p.plan_rec[w] = rec;  // for the merge launch
+        if constexpr (!kDefer) {
+            if (lane == 0)
+                p.plan_rec[w] = rec;  // for the merge launch
+        }
     } else {
         if (w >= p.plan_meta[0])
             return;
@@ -493,8 +507,60 @@ void paged_decode_kernel(DecodeParams p)
     // Attend over tiles [t0, t1) of unit (b, h); ctx clamped to the host
     // bound.  cg[q]: the columns of group q (see Cols); every loaded tile
     // serves all NQ groups.
+    // A piece's results: the final fp16 output of a whole unit (kind 1) or
+    // the fp32 partial (out_scale-scaled acc, then (m, l)) of a cut one
+    // (kind 2) in its workspace slot.
+    auto emit = [&](const f32x4 (&oq)[DT], const float mq, const float lq, const float osc,
+                    const int kind, f16 *orow, const int64_t idx) {
+        if (kind == 1) {
+            const float inv = osc / lq;
+            orow += 16 * grp;
+#pragma unroll
+            for (int g4 = 0; g4 < D / 64; ++g4) {
+                f16x4 hv[4];
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const f32x4 *t = &oq[4 * g4];
+                    hv[v] = f16x4{(f16)(t[0][v] * inv), (f16)(t[1][v] * inv),
+                                  (f16)(t[2][v] * inv), (f16)(t[3][v] * inv)};
+                }
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    *reinterpret_cast<f16x4 *>(orow + 64 * g4 + 4 * v) = hv[v];
+            }
+        } else if (kind == 2) {
+            float *wacc = p.ws_acc + idx * D + 16 * grp;
+#pragma unroll
+            for (int g4 = 0; g4 < D / 64; ++g4)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const f32x4 *t = &oq[4 * g4];
+                    const f32x4 wv = {t[0][v] * osc, t[1][v] * osc, t[2][v] * osc, t[3][v] * osc};
+                    *reinterpret_cast<f32x4 *>(wacc + 64 * g4 + 4 * v) = wv;
+                }
+            if (grp == 0)
+                *reinterpret_cast<float2 *>(p.ws_ml + 2 * idx) = make_float2(mq, lq);
+        }
+    };
+    constexpr int kHeld = kDefer ? 2 : 1;   // pieces whose results can wait
+    struct Held {
+        f32x4 o[DT];
+        float m, l, s;
+        int kind;       // 0: nothing held
+        f16 *orow;
+        int64_t idx;
+    };
+    Held held[kHeld];
+#pragma unroll
+    for (int i = 0; i < kHeld; ++i)
+        held[i].kind = 0;
+    auto emit_held = [&](const Held &x) {
+        if (x.kind != 0)
+            emit(x.o, x.m, x.l, x.s, x.kind, x.orow, x.idx);
+    };
+
     auto attend = [&](const int b, const int h, const int ctx, const int n, const int t0,
-                      const int t1, const Cols (&cg)[NQ]) {
+                      const int t1, const Cols (&cg)[NQ], const bool last) {
         const int t_end = min(ctx, 16 * t1);  // token bound of this run (data)
         int t_col[NQ];                        // score bound of this lane's columns
 #pragma unroll
@@ -876,40 +942,39 @@ void paged_decode_kernel(DecodeParams p)
                         o[q][4 * g4 + 3][v] *= sc4.w;
                     }
             }
-            if (t0 == 0 && t1 == n) {  // the whole unit: final output
-                const float inv = out_scale / lt;
-                f16 *orow = cg[q].orow + 16 * grp;
-#pragma unroll
-                for (int g4 = 0; g4 < D / 64; ++g4) {
-                    f16x4 hv[4];
-#pragma unroll
-                    for (int v = 0; v < 4; ++v) {
-                        const f32x4 *t = &o[q][4 * g4];
-                        hv[v] = f16x4{(f16)(t[0][v] * inv), (f16)(t[1][v] * inv),
-                                      (f16)(t[2][v] * inv), (f16)(t[3][v] * inv)};
-                    }
-#pragma unroll
-                    for (int v = 0; v < 4; ++v)
-                        *reinterpret_cast<f16x4 *>(orow + 64 * g4 + 4 * v) = hv[v];
-                }
-                continue;
-            }
-            // a piece of a unit: slot 0 if it continues a unit, slot 1 if it
-            // starts one (decode walk only); unit column 16 q + col
+            // the whole unit: final output; else a piece of a unit: slot 0
+            // if it continues a unit, slot 1 if it starts one (decode walk
+            // only); unit column 16 q + col
+            const int kind = (t0 == 0 && t1 == n) ? 1 : 2;
             const int slot = t0 > 0 ? 0 : 1;
             const int64_t idx = ((int64_t)w * 2 + slot) * p.cols + 16 * q + col;
-            float *wacc = p.ws_acc + idx * D + 16 * grp;
+            if constexpr (kDefer) {
+                if (last) {   // the run's loads are done: store everything
 #pragma unroll
-            for (int g4 = 0; g4 < D / 64; ++g4)
+                    for (int i = 0; i < kHeld; ++i) {
+                        emit_held(held[i]);
+                        held[i].kind = 0;
+                    }
+                    emit(o[q], m[q], lt, out_scale, kind, cg[q].orow, idx);
+                } else {      // hold it; when every slot is full, store the oldest
+                    emit_held(held[0]);
 #pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    const f32x4 *t = &o[q][4 * g4];
-                    const f32x4 wv = {t[0][v] * out_scale, t[1][v] * out_scale,
-                                      t[2][v] * out_scale, t[3][v] * out_scale};
-                    *reinterpret_cast<f32x4 *>(wacc + 64 * g4 + 4 * v) = wv;
+                    for (int i = 0; i + 1 < kHeld; ++i)
+                        held[i] = held[i + 1];
+                    Held &x = held[kHeld - 1];
+#pragma unroll
+                    for (int i = 0; i < DT; ++i)
+                        x.o[i] = o[q][i];
+                    x.m = m[q];
+                    x.l = lt;
+                    x.s = out_scale;
+                    x.kind = kind;
+                    x.orow = cg[q].orow;
+                    x.idx = idx;
                 }
-            if (grp == 0)
-                *reinterpret_cast<float2 *>(p.ws_ml + 2 * idx) = make_float2(m[q], lt);
+            } else {
+                emit(o[q], m[q], lt, out_scale, kind, cg[q].orow, idx);
+            }
         }
     };
 
@@ -954,9 +1019,18 @@ void paged_decode_kernel(DecodeParams p)
                     (int64_t)(qs + (act ? ci : 0)) * p.Hq + gh * p.r + (act ? cj : 0);
                 cg[q] = Cols{p.q + row * D, p.out + row * D, p.q_start ? tcol + ci : tcol, act};
             }
-            attend(b, h, ctx, n, t0, t1, cg);
+            attend(b, h, ctx, n, t0, t1, cg, g + (t1 - t0) >= rec.g1);
         }
         g += t1 - t0;
+    }
+    if constexpr (kDefer) {   // pieces before an empty last chunk, or inactive lanes'
+#pragma unroll
+        for (int i = 0; i < kHeld; ++i)
+            emit_held(held[i]);
+    }
+    if constexpr (kDefer) {   // the record for the merge launch, after the loads
+        if (p.inline_plan && lane == 0)
+            p.plan_rec[w] = rec;
     }
 }
 
