@@ -63,14 +63,15 @@ def load_traffic(workload: str):
     return t.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(case, spec, max_seqs: int, layer: int = 0, passes: int = 3):
+def cpu_baseline(case, spec, max_seqs: int, layer: int = 0, min_seconds: float = 10.0):
     """Time the oracle (as it stands) doing one decode step's work for the
     first `max_seqs` sequences of one layer, like the GPU step: quantize each
     sequence's appended token, then fp64 attention over its cached K/V.  The
     cache itself is state, as the GPU's pool is: every cached token is
     quantized, dequantized and laid out contiguously per sequence (the form
-    the oracle reads) once, before timing.  Median of `passes` passes, on all
-    the oracle's threads and, for the first 16 sequences, on one."""
+    the oracle reads) once, before timing.  Median over at least three
+    passes and about `min_seconds` of work, on all the oracle's threads and,
+    for the first 16 sequences, on one (three passes)."""
     import numpy as np
     import torch
 
@@ -109,16 +110,17 @@ def cpu_baseline(case, spec, max_seqs: int, layer: int = 0, passes: int = 3):
         oracle.decode_attention(q[:n], K[:last[n - 1] + 1], V[:last[n - 1] + 1], lens[:n])
 
     times = []
-    for _ in range(passes):
+    while len(times) < 3 or (sum(times) < min_seconds and len(times) < 60):
         t0 = time.perf_counter()
         step(nseq)
         times.append(time.perf_counter() - t0)
+    passes = len(times)
     cores = oracle.num_threads()
     n1 = min(16, nseq)
     oracle.set_num_threads(1)
     try:
         t1 = []
-        for _ in range(passes):
+        for _ in range(3):
             t0 = time.perf_counter()
             step(n1)
             t1.append(time.perf_counter() - t0)
@@ -802,7 +804,8 @@ def main(argv=None) -> int:
     }
     if args.cpu_seqs > 0:
         result["cpu_baseline"] = cpu_baseline(case, spec, args.cpu_seqs,
-                                              layer=1 if nl > 1 else 0)
+                                              layer=1 if nl > 1 else 0,
+                                              min_seconds=args.cpu_min_seconds)
     else:
         result["cpu_baseline"] = None
     if args.recon:
