@@ -12,9 +12,9 @@
 // through the block table (a 16-token block, or half of a 32-token block),
 // with the next tile's loads in flight while the current one is computed.
 //
-// Both contractions run on fp16 MFMA (16x16x32 on gfx950, which issues at
-// the rate of the older 16x16x16) with the head_dim / token axes laid out so
-// that no data moves between lanes except for softmax maxima.
+// Both contractions run on fp16 MFMA (S^T on 16x16x32, which gfx950 issues
+// at the rate of the older 16x16x16) with the head_dim / token axes laid
+// out so that no data moves between lanes except for softmax maxima.
 // Lane (col, grp) = (lane % 16, lane / 16):
 //   S^T[token][head] = K_tile (16 x D) * Q^T (D x 16)
 //       A operand: token `col`, 8 head dims per MFMA (two 4-dim k-steps);
@@ -39,7 +39,9 @@
 // reference by more than a few units (P stays below 2^slack).
 // Pieces of a unit cut by run boundaries write (m, l, acc) partials that a
 // second, small launch merges with a log-sum-exp; a unit that lies inside one
-// run is finished by the decode kernel itself.
+// run is finished by the decode kernel itself.  A run's results are stored
+// only once its loads are done (see kDefer): a store among the loads would
+// hold up every later wait for them.
 #pragma once
 
 #include "kvq_device.hpp"
