@@ -54,30 +54,38 @@ __global__ __launch_bounds__(64 * kWriteWaves) void cache_write_kernel(WritePara
         return;
     const int t = (int)(pair / p.Hkv);
     const int h = (int)(pair % p.Hkv);
-    const int64_t slot = p.slots[t];
-    if (slot < 0 || slot >= p.num_slots)
-        return;
-    const int BS = p.block_size;
-    const int64_t blk = slot / BS;
-    const int off = (int)(slot % BS);
     const bool is_v = lane >= 32;
     const int e0 = (lane & 31) * EPL;
 
+    // The slot and the token's values are read together (the values' address
+    // does not depend on the slot); the empty asm uses both before the slot
+    // check, which keeps the compiler from moving the value load below it.
     const int gh = p.head_ids ? p.head_ids[h] : h;
     const f16 *src = (is_v ? p.v : p.k) + ((int64_t)t * p.Hkv_src + gh) * D + e0;
-    float x[EPL];
+    int64_t slot = p.slots[t];
+    uint32_t raw[EPL / 2];
     if constexpr (EPL == 4) {
-        const uint2 raw = *reinterpret_cast<const uint2 *>(src);
-        const f16x4 hv = f16x4_from_u2(raw.x, raw.y);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            x[i] = (float)hv[i];
+        const uint2 r2 = *reinterpret_cast<const uint2 *>(src);
+        raw[0] = r2.x;
+        raw[1] = r2.y;
     } else {
-        const uint32_t raw = *reinterpret_cast<const uint32_t *>(src);
-        const f16x2 hv = bit_cast<f16x2>(raw);
-        x[0] = (float)hv.x;
-        x[1] = (float)hv.y;
+        raw[0] = *reinterpret_cast<const uint32_t *>(src);
     }
+#pragma unroll
+    for (int i = 0; i < EPL / 2; ++i)
+        __asm__ __volatile__("" : "+v"(raw[i]), "+v"(slot));
+    if (slot < 0 || slot >= p.num_slots)
+        return;
+    float x[EPL];
+#pragma unroll
+    for (int i = 0; i < EPL / 2; ++i) {
+        const f16x2 hv = bit_cast<f16x2>(raw[i]);
+        x[2 * i] = (float)hv.x;
+        x[2 * i + 1] = (float)hv.y;
+    }
+    const int BS = p.block_size;
+    const int64_t blk = slot / BS;
+    const int off = (int)(slot % BS);
 
     const int64_t head_base = blk * p.Hkv + h;  // (block, head) tile index
     uint32_t code[EPL];
@@ -169,9 +177,9 @@ __global__ __launch_bounds__(64 * kWriteWaves) void cache_write_kernel(WritePara
         uint8_t *dst = tile + k_offset<D, EB>(BS, off, e0);
         if constexpr (FMT == FMT_FP16) {
             if constexpr (EPL == 4)
-                *reinterpret_cast<uint2 *>(dst) = *reinterpret_cast<const uint2 *>(src);
+                *reinterpret_cast<uint2 *>(dst) = make_uint2(raw[0], raw[1]);
             else
-                *reinterpret_cast<uint32_t *>(dst) = *reinterpret_cast<const uint32_t *>(src);
+                *reinterpret_cast<uint32_t *>(dst) = raw[0];
         } else if constexpr (EPL == 4) {
             *reinterpret_cast<uint32_t *>(dst) =
                 code[0] | (code[1] << 8) | (code[2] << 16) | (code[3] << 24);
@@ -183,7 +191,7 @@ __global__ __launch_bounds__(64 * kWriteWaves) void cache_write_kernel(WritePara
         for (int i = 0; i < EPL; ++i) {
             uint8_t *dst = tile + v_offset<D, EB>(BS, off, e0 + i);
             if constexpr (FMT == FMT_FP16)
-                *reinterpret_cast<f16 *>(dst) = src[i];
+                *reinterpret_cast<f16 *>(dst) = bit_cast<f16x2>(raw[i / 2])[i % 2];
             else
                 *dst = (uint8_t)code[i];
         }
