@@ -721,7 +721,7 @@ def main(argv=None) -> int:
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the decode path has no cross-GPU "
-              "stage in this build (--gpus %d requested)" % args.gpus, file=sys.stderr)
+              "stage (--gpus %d requested)" % args.gpus, file=sys.stderr)
         return 2
 
     import numpy as np

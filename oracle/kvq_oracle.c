@@ -25,7 +25,7 @@
  *  [P1] xpshop.cn article 402, s3 / [P2] xpshop.cn article 312, s2-s3: INT8 /
  *       FP8 KV cache in paged 16/32-token blocks.
  *
- * Readings where the pages are silent (each also listed in the design doc):
+ * Readings where the pages are silent:
  *  - INT8 scale s = fl32(absmax / 127), code = clamp(rne(fl32(x / s)), -127,
  *    127); an all-zero group stores s = 0 and codes 0.
  *  - FP8 is OCP E4M3FN (bias 7, max 448, no infinities); encode rounds to

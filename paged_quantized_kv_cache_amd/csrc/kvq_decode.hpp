@@ -1045,8 +1045,8 @@ void paged_decode_kernel(DecodeParams p)
 // made the 16-column merge of short chunks 2.6x slower).  The pieces are run
 // k-1's slot 1 (the unit's start) and slot 0 of runs k, k+1, ... up to the
 // unit's end.  It runs as its own launch, so the partials written by
-// wavefronts on any XCD are visible without device-wide fences.  Loads go in
-// two rounds: the run records (each carries its unit's bounds), then every
+// wavefronts on any XCD are visible without device-wide fences.  Loads come in
+// two batches: the run records (each carries its unit's bounds), then every
 // piece's (m, l) together with the first pieces' partial outputs.
 constexpr int kMergeCols = 4;
 
@@ -1060,7 +1060,7 @@ __global__ __launch_bounds__(64 * kMergeCols) void merge_runs_kernel(DecodeParam
     const int lane = threadIdx.x & 63;
     if (col >= p.cols)
         return;
-    // round 1: the runs in use, and the records of runs k - 1 .. k + 62
+    // first loads: the runs in use, and the records of runs k - 1 .. k + 62
     // (lane j: run k - 1 + j; p.W records are allocated)
     const int nrec = p.plan_meta[0];
     const int rj = k - 1 + lane;
@@ -1104,7 +1104,7 @@ __global__ __launch_bounds__(64 * kMergeCols) void merge_runs_kernel(DecodeParam
             return;
         row = (int64_t)(qs + col / p.r) * p.Hq + model_head(p, h) * p.r + col % p.r;
     }
-    // round 2: (m, l) of every piece, the partials of the first kAhead
+    // second loads: (m, l) of every piece, the partials of the first kAhead
     float ahead[kAhead][PER];
 #pragma unroll
     for (int j = 0; j < kAhead; ++j) {

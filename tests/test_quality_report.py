@@ -1,5 +1,5 @@
 """Reconstruction error of the cache formats on the workloads' synthetic
-data (reported; the pages judge formats by task quality -- "KV Cache优化实战"
+data (reported; the pages rate formats by task quality -- "KV Cache优化实战"
 s3.3 and s4.2, xpshop.cn article 402 s4 -- which needs trained weights; this
 is the measurable stand-in).  CPU only.
 
